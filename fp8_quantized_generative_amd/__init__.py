@@ -1,0 +1,164 @@
+"""MI355X (gfx950) W8A8 FP8 linear for OneRec-V2 post-training-quantized serving.
+
+Python face of the C ABI in ``include/rq_fp8.h`` (``librq_fp8.so``).  Every step of the
+computation runs in the library's HIP kernels; this module only marshals arguments.
+PyTorch provides device memory and the current stream.
+
+* ``quant_weights(w)``                         offline per-output-channel E4M3 quantization
+* ``linear(x, w_q, w_scale, act=...)``         per-token quantization + FP8 GEMM + FP16 epilogue
+* ``moe_grouped_linear(x, ids, w_q, w_scale, ...)``  routing plan + grouped GEMM (+ combine)
+* ``linear_workspace_size`` / ``moe_workspace_size``  scratch sizes for caller-held workspaces
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (RQ_ACT_NONE, RQ_ACT_SILU_MUL, RQ_MOE_IN_PERMUTED, RQ_MOE_IN_TOKENS,  # noqa: F401
+                   RQ_MOE_OUT_COMBINED, RQ_MOE_OUT_PERMUTED, DebugOut, RqError)
+
+ACTS = {"none": RQ_ACT_NONE, "silu_mul": RQ_ACT_SILU_MUL}
+IN_LAYOUTS = {"tokens": RQ_MOE_IN_TOKENS, "permuted": RQ_MOE_IN_PERMUTED}
+OUT_LAYOUTS = {"permuted": RQ_MOE_OUT_PERMUTED, "combined": RQ_MOE_OUT_COMBINED}
+
+
+def _code(table, v, what):
+    if isinstance(v, str):
+        if v not in table:
+            raise ValueError("unknown %s %r" % (what, v))
+        return table[v]
+    return int(v)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dev(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError("%s must be a device tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise TypeError("%s must be contiguous" % name)
+    return t
+
+
+def _stream(t, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is not None:
+        return workspace
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def quant_weights(w, w_q=None, w_scale=None, stream=None):
+    """FP16 [N, K] or [B, N, K] -> (E4M3 bytes of the same shape, FP32 scales [N] / [B, N])."""
+    _dev(w, torch.float16, "w")
+    if w.dim() not in (2, 3):
+        raise ValueError("w must be [N, K] or [B, N, K]")
+    b, n, k = (1,) + tuple(w.shape) if w.dim() == 2 else tuple(w.shape)
+    if w_q is None:
+        w_q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    if w_scale is None:
+        w_scale = torch.empty(w.shape[:-1], dtype=torch.float32, device=w.device)
+    _dev(w_q, torch.uint8, "w_q")
+    _dev(w_scale, torch.float32, "w_scale")
+    st = _lib.load().rq_fp8_quant_weights(_ptr(w), b, n, k, _ptr(w_q), _ptr(w_scale), _stream(w, stream))
+    _lib.check("rq_fp8_quant_weights", st)
+    return w_q, w_scale
+
+
+def linear_workspace_size(m, k, act="none"):
+    return int(_lib.load().rq_fp8_linear_workspace_size(m, k, _code(ACTS, act, "act")))
+
+
+def moe_workspace_size(t, top_k, e, n, k, in_layout="tokens", act="none", out_layout="permuted"):
+    return int(_lib.load().rq_fp8_moe_workspace_size(
+        t, top_k, e, n, k, _code(IN_LAYOUTS, in_layout, "in_layout"), _code(ACTS, act, "act"),
+        _code(OUT_LAYOUTS, out_layout, "out_layout")))
+
+
+def _debug(debug, rows, k, act, device):
+    if not debug:
+        return None, None
+    d = {"a_q": torch.empty((rows, k), dtype=torch.uint8, device=device),
+         "a_scale": torch.empty((rows,), dtype=torch.float32, device=device),
+         "h": torch.empty((rows, k), dtype=torch.float16, device=device) if act == RQ_ACT_SILU_MUL else None}
+    s = DebugOut(d["a_q"].data_ptr(), d["a_scale"].data_ptr(), d["h"].data_ptr() if d["h"] is not None else 0)
+    return d, s
+
+
+def linear(x, w_q, w_scale, act="none", out=None, workspace=None, debug=False, stream=None):
+    """W8A8 FP8 linear: FP16 x [M, K] (or [M, 2K] for ``act='silu_mul'``) -> FP16 y [M, N].
+
+    With ``debug=True`` returns ``(y, {"a_q", "a_scale", "h"})``: the quantized GEMM input
+    (and the SiLU*up rows).
+    """
+    a = _code(ACTS, act, "act")
+    _dev(x, torch.float16, "x")
+    _dev(w_q, torch.uint8, "w_q")
+    _dev(w_scale, torch.float32, "w_scale")
+    if x.dim() != 2 or w_q.dim() != 2:
+        raise ValueError("x and w_q must be 2-D")
+    m = x.shape[0]
+    n, k = w_q.shape
+    if x.shape[1] != (2 * k if a == RQ_ACT_SILU_MUL else k):
+        raise ValueError("x width %d does not match K=%d for act=%r" % (x.shape[1], k, act))
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float16, device=x.device)
+    _dev(out, torch.float16, "out")
+    lib = _lib.load()
+    ws_bytes = lib.rq_fp8_linear_workspace_size(m, k, a)
+    ws = _workspace(ws_bytes, x.device, workspace)
+    dbg, dbg_s = _debug(debug, m, k, a, x.device)
+    st = lib.rq_fp8_linear(_ptr(x), m, k, a, _ptr(w_q), _ptr(w_scale), n, _ptr(out), _ptr(ws),
+                           ws.numel(), ctypes.byref(dbg_s) if dbg_s is not None else None,
+                           _stream(x, stream))
+    _lib.check("rq_fp8_linear", st)
+    return (out, dbg) if debug else out
+
+
+def moe_grouped_linear(x, topk_ids, w_q, w_scale, in_layout="tokens", act="none",
+                       out_layout="permuted", topk_w=None, out=None, workspace=None,
+                       debug=False, stream=None):
+    """Expert grouped W8A8 linear.
+
+    ``x``: FP16 [T, K*] (tokens) or [T*top_k, K*] (permuted), K* = 2K for ``silu_mul``;
+    ``topk_ids``: int32 [T, top_k]; ``w_q``: uint8 [E, N, K]; ``w_scale``: FP32 [E, N];
+    ``topk_w``: FP16 [T, top_k] for ``out_layout='combined'``.
+    Returns FP16 [T*top_k, N] (permuted) or [T, N] (combined), plus the debug dict when
+    ``debug=True``.
+    """
+    il = _code(IN_LAYOUTS, in_layout, "in_layout")
+    a = _code(ACTS, act, "act")
+    ol = _code(OUT_LAYOUTS, out_layout, "out_layout")
+    _dev(x, torch.float16, "x")
+    _dev(topk_ids, torch.int32, "topk_ids")
+    _dev(w_q, torch.uint8, "w_q")
+    _dev(w_scale, torch.float32, "w_scale")
+    if topk_w is not None:
+        _dev(topk_w, torch.float16, "topk_w")
+    t, top_k = topk_ids.shape
+    e, n, k = w_q.shape
+    r = t * top_k
+    rows = t if il == RQ_MOE_IN_TOKENS else r
+    if tuple(x.shape) != (rows, 2 * k if a == RQ_ACT_SILU_MUL else k):
+        raise ValueError("x shape %r does not match the layout" % (tuple(x.shape),))
+    if out is None:
+        out = torch.empty((t if ol == RQ_MOE_OUT_COMBINED else r, n), dtype=torch.float16, device=x.device)
+    _dev(out, torch.float16, "out")
+    lib = _lib.load()
+    ws_bytes = lib.rq_fp8_moe_workspace_size(t, top_k, e, n, k, il, a, ol)
+    ws = _workspace(ws_bytes, x.device, workspace)
+    dbg, dbg_s = _debug(debug, rows, k, a, x.device)
+    st = lib.rq_fp8_moe_grouped_linear(
+        _ptr(x), il, a, _ptr(topk_ids), _ptr(topk_w), t, top_k, _ptr(w_q), _ptr(w_scale), e, n, k,
+        _ptr(out), ol, _ptr(ws), ws.numel(), ctypes.byref(dbg_s) if dbg_s is not None else None,
+        _stream(x, stream))
+    _lib.check("rq_fp8_moe_grouped_linear", st)
+    return (out, dbg) if debug else out

@@ -1,0 +1,237 @@
+// C ABI of the gfx950 W8A8 FP8 library: argument validation, workspace layout and the
+// launch sequence of each entry point.  The operations are specified in rq_fp8.h.
+
+#include <atomic>
+#include <cstring>
+
+#include "rq_fp8.h"
+#include "common.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxExperts = 1024;
+constexpr int kMaxDevices = 64;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Per-device arch cache: 0 unknown, 1 gfx950, 2 other.
+std::atomic<int> g_arch[kMaxDevices];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return RQ_ERR_HIP;
+  const int r = rq_device_supported(dev);
+  if (r < 0) return RQ_ERR_HIP;
+  return r == 1 ? RQ_OK : RQ_ERR_UNSUPPORTED;
+}
+
+struct Carve {
+  uint8_t* base;
+  size_t used = 0;
+  template <typename T>
+  T* take(size_t bytes) {
+    T* p = reinterpret_cast<T*>(base + used);
+    used += align_up(bytes);
+    return p;
+  }
+};
+
+struct MoeLayout {
+  size_t a_q, a_scale, offsets, tile_start, perm, pos, block_hist, y_perm;
+};
+
+MoeLayout moe_layout(int64_t T, int top_k, int64_t E, int64_t N, int64_t K, int in_layout,
+                     int out_layout) {
+  const int64_t R = T * top_k;
+  const int64_t rows = in_layout == RQ_MOE_IN_TOKENS ? T : R;
+  MoeLayout l;
+  l.a_q = (size_t)(rows * K);
+  l.a_scale = (size_t)rows * sizeof(float);
+  l.offsets = (size_t)(E + 1) * sizeof(int32_t);
+  l.tile_start = (size_t)(E + 1) * sizeof(int32_t);
+  l.perm = (size_t)R * sizeof(int32_t);
+  l.pos = (size_t)R * sizeof(int32_t);
+  l.block_hist = (size_t)(rq::moe_plan_blocks(R) * E) * sizeof(int32_t);
+  l.y_perm = out_layout == RQ_MOE_OUT_COMBINED ? (size_t)(R * N) * sizeof(uint16_t) : 0;
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rq_status_string(int status) {
+  switch (status) {
+    case RQ_OK: return "ok";
+    case RQ_ERR_NULL: return "null pointer";
+    case RQ_ERR_SHAPE: return "unsupported shape";
+    case RQ_ERR_ALIGN: return "misaligned size or pointer";
+    case RQ_ERR_WORKSPACE: return "workspace too small";
+    case RQ_ERR_UNSUPPORTED: return "device is not gfx950";
+    case RQ_ERR_HIP: return "HIP runtime error";
+    case RQ_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+int rq_device_supported(int device) {
+  if (device < 0) return -1;
+  if (device < kMaxDevices) {
+    const int c = g_arch[device].load(std::memory_order_relaxed);
+    if (c != 0) return c == 1 ? 1 : 0;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return -1;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (device < kMaxDevices) g_arch[device].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? 1 : 0;
+}
+
+int rq_fp8_quant_weights(const uint16_t* w, int64_t B, int64_t N, int64_t K, uint8_t* w_q,
+                         float* w_scale, void* stream) {
+  if (B < 0 || N < 0 || K <= 0) return RQ_ERR_SHAPE;
+  if (K % 16 != 0) return RQ_ERR_ALIGN;
+  if (B > 0 && N > 0 && B > INT64_MAX / N) return RQ_ERR_SHAPE;
+  const int64_t rows = B * N;
+  if (rows == 0) return RQ_OK;
+  if (!w || !w_q || !w_scale) return RQ_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(w_q, 16) || !aligned(w_scale, 4)) return RQ_ERR_ALIGN;
+  const int dev = check_device();
+  if (dev != RQ_OK) return dev;
+  hipError_t e = rq::launch_quant_rows(w, rows, K, RQ_ACT_NONE, w_q, w_scale, nullptr, (hipStream_t)stream);
+  return e == hipSuccess ? RQ_OK : RQ_ERR_HIP;
+}
+
+size_t rq_fp8_linear_workspace_size(int64_t M, int64_t K, int act) {
+  (void)act;
+  if (M < 0 || K <= 0) return 0;
+  return align_up((size_t)(M * K)) + align_up((size_t)M * sizeof(float));
+}
+
+int rq_fp8_linear(const uint16_t* x, int64_t M, int64_t K, int act, const uint8_t* w_q,
+                  const float* w_scale, int64_t N, uint16_t* y, void* workspace,
+                  size_t workspace_bytes, const rq_debug_out* dbg, void* stream) {
+  if (act != RQ_ACT_NONE && act != RQ_ACT_SILU_MUL) return RQ_ERR_ARG;
+  if (M < 0 || K <= 0 || N <= 0) return RQ_ERR_SHAPE;
+  if (K % 16 != 0 || N % 16 != 0) return RQ_ERR_ALIGN;
+  if (K > (int64_t)1 << 30 || N > (int64_t)1 << 30 || M > (int64_t)1 << 31) return RQ_ERR_SHAPE;
+  if (!w_q || !w_scale) return RQ_ERR_NULL;
+  if (M > 0 && (!x || !y)) return RQ_ERR_NULL;
+  uint8_t* dq = dbg ? dbg->a_q : nullptr;
+  float* ds = dbg ? dbg->a_scale : nullptr;
+  uint16_t* dh = dbg ? dbg->h : nullptr;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w_q, 16) || !aligned(w_scale, 4) ||
+      !aligned(workspace, 16) || !aligned(dq, 16) || !aligned(ds, 4) || !aligned(dh, 16))
+    return RQ_ERR_ALIGN;
+  const size_t need_q = dq ? 0 : align_up((size_t)(M * K));
+  const size_t need_s = ds ? 0 : align_up((size_t)M * sizeof(float));
+  if (need_q + need_s > 0 && (!workspace || workspace_bytes < need_q + need_s))
+    return M == 0 ? RQ_OK : RQ_ERR_WORKSPACE;
+  if (M == 0) return RQ_OK;
+  const int dev = check_device();
+  if (dev != RQ_OK) return dev;
+
+  Carve c{reinterpret_cast<uint8_t*>(workspace)};
+  uint8_t* xq = dq ? dq : c.take<uint8_t>((size_t)(M * K));
+  float* sx = ds ? ds : c.take<float>((size_t)M * sizeof(float));
+  hipStream_t s = (hipStream_t)stream;
+  if (rq::launch_quant_rows(x, M, K, act, xq, sx, act == RQ_ACT_SILU_MUL ? dh : nullptr, s) != hipSuccess)
+    return RQ_ERR_HIP;
+  rq::GemmArgs g{};
+  g.a = xq;
+  g.a_scale = sx;
+  g.b = w_q;
+  g.b_scale = w_scale;
+  g.y = y;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.E = 1;
+  return rq::launch_gemm_dense(g, s) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
+}
+
+size_t rq_fp8_moe_workspace_size(int64_t T, int top_k, int64_t E, int64_t N, int64_t K,
+                                 int in_layout, int act, int out_layout) {
+  (void)act;
+  if (T < 0 || top_k < 1 || E < 1 || N <= 0 || K <= 0) return 0;
+  const MoeLayout l = moe_layout(T, top_k, E, N, K, in_layout, out_layout);
+  return align_up(l.a_q) + align_up(l.a_scale) + align_up(l.offsets) + align_up(l.tile_start) +
+         align_up(l.perm) + align_up(l.pos) + align_up(l.block_hist) + align_up(l.y_perm);
+}
+
+int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const int32_t* topk_ids,
+                              const uint16_t* topk_w, int64_t T, int top_k, const uint8_t* w_q,
+                              const float* w_scale, int64_t E, int64_t N, int64_t K, uint16_t* y,
+                              int out_layout, void* workspace, size_t workspace_bytes,
+                              const rq_debug_out* dbg, void* stream) {
+  if (act != RQ_ACT_NONE && act != RQ_ACT_SILU_MUL) return RQ_ERR_ARG;
+  if (in_layout != RQ_MOE_IN_TOKENS && in_layout != RQ_MOE_IN_PERMUTED) return RQ_ERR_ARG;
+  if (out_layout != RQ_MOE_OUT_PERMUTED && out_layout != RQ_MOE_OUT_COMBINED) return RQ_ERR_ARG;
+  if (T < 0 || K <= 0 || N <= 0 || E < 1 || E > kMaxExperts || top_k < 1 || top_k > E)
+    return RQ_ERR_SHAPE;
+  if (K % 16 != 0 || N % 16 != 0) return RQ_ERR_ALIGN;
+  if (K > (int64_t)1 << 30 || N > (int64_t)1 << 30 || T * top_k > ((int64_t)1 << 31) - 1)
+    return RQ_ERR_SHAPE;
+  if (!w_q || !w_scale) return RQ_ERR_NULL;
+  if (T > 0 && (!x || !y || !topk_ids)) return RQ_ERR_NULL;
+  if (T > 0 && out_layout == RQ_MOE_OUT_COMBINED && !topk_w) return RQ_ERR_ARG;
+  uint8_t* dq = dbg ? dbg->a_q : nullptr;
+  float* ds = dbg ? dbg->a_scale : nullptr;
+  uint16_t* dh = dbg ? dbg->h : nullptr;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w_q, 16) || !aligned(w_scale, 4) ||
+      !aligned(topk_ids, 4) || !aligned(topk_w, 2) || !aligned(workspace, 16) || !aligned(dq, 16) ||
+      !aligned(ds, 4) || !aligned(dh, 16))
+    return RQ_ERR_ALIGN;
+  if (T == 0) return RQ_OK;
+  const size_t need = rq_fp8_moe_workspace_size(T, top_k, E, N, K, in_layout, act, out_layout);
+  if (!workspace || workspace_bytes < need) return RQ_ERR_WORKSPACE;
+  const int dev = check_device();
+  if (dev != RQ_OK) return dev;
+
+  const int64_t R = T * top_k;
+  const int64_t rows = in_layout == RQ_MOE_IN_TOKENS ? T : R;
+  const MoeLayout l = moe_layout(T, top_k, E, N, K, in_layout, out_layout);
+  Carve c{reinterpret_cast<uint8_t*>(workspace)};
+  uint8_t* aq = c.take<uint8_t>(l.a_q);
+  float* as = c.take<float>(l.a_scale);
+  int32_t* offsets = c.take<int32_t>(l.offsets);
+  int32_t* tile_start = c.take<int32_t>(l.tile_start);
+  int32_t* perm = c.take<int32_t>(l.perm);
+  int32_t* pos = c.take<int32_t>(l.pos);
+  int32_t* block_hist = c.take<int32_t>(l.block_hist);
+  uint16_t* y_perm = out_layout == RQ_MOE_OUT_COMBINED ? c.take<uint16_t>(l.y_perm) : y;
+  if (dq) aq = dq;
+  if (ds) as = ds;
+
+  hipStream_t s = (hipStream_t)stream;
+  if (rq::launch_moe_plan(topk_ids, T, top_k, E, rq::grouped_tile_m(), offsets, tile_start, perm, pos,
+                          block_hist, s) != hipSuccess)
+    return RQ_ERR_HIP;
+  if (rq::launch_quant_rows(x, rows, K, act, aq, as, act == RQ_ACT_SILU_MUL ? dh : nullptr, s) != hipSuccess)
+    return RQ_ERR_HIP;
+  rq::GemmArgs g{};
+  g.a = aq;
+  g.a_scale = as;
+  g.b = w_q;
+  g.b_scale = w_scale;
+  g.y = y_perm;
+  g.M = R;
+  g.N = N;
+  g.K = K;
+  g.offsets = offsets;
+  g.tile_start = tile_start;
+  g.perm = perm;
+  g.top_k = top_k;
+  g.E = (int32_t)E;
+  g.gather_tokens = in_layout == RQ_MOE_IN_TOKENS ? 1 : 0;
+  if (rq::launch_gemm_grouped(g, s) != hipSuccess) return RQ_ERR_HIP;
+  if (out_layout == RQ_MOE_OUT_COMBINED) {
+    if (rq::launch_moe_combine(y_perm, pos, topk_w, T, top_k, N, y, s) != hipSuccess) return RQ_ERR_HIP;
+  }
+  return RQ_OK;
+}
+
+}  // extern "C"

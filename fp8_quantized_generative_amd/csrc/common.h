@@ -1,0 +1,77 @@
+// Internal helpers of the gfx950 W8A8 FP8 library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rq {
+
+// Packed vector types.
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr float kFp8Max = 448.0f;        // largest finite OCP E4M3 magnitude
+constexpr float kScaleFloor = 0x1p-24f;  // smallest positive FP16: floor of a row's amax
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)h);
+}
+
+__device__ __forceinline__ uint32_t float_to_half_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)f);  // round to nearest even
+}
+
+__device__ __forceinline__ uint4 ld_global_16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ __forceinline__ void st_global_16(void* p, uint4 v) {
+  *reinterpret_cast<uint4*>(p) = v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+// Launch helpers ---------------------------------------------------------------------
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t K, int act,
+                             uint8_t* q, float* scale, uint16_t* h, hipStream_t stream);
+
+struct GemmArgs {
+  const uint8_t* a;       // [rows][K] E4M3 (token rows, or permuted rows)
+  const float* a_scale;   // [rows]
+  const uint8_t* b;       // [E][N][K] E4M3 (E = 1 for a dense linear)
+  const float* b_scale;   // [E][N]
+  uint16_t* y;            // [M or R][N] FP16
+  int64_t M;              // dense: rows of A and y.  grouped: R (routed rows)
+  int64_t N;
+  int64_t K;
+  // grouped only
+  const int32_t* offsets;     // [E+1] permuted row offsets per expert
+  const int32_t* tile_start;  // [E+1] first m-tile of each expert (exclusive scan)
+  const int32_t* perm;        // [R] slot of each permuted row (TOKENS input only)
+  int32_t top_k;              // token of permuted row r = perm[r] / top_k (TOKENS input)
+  int32_t E;
+  int32_t gather_tokens;      // 1: A row of permuted row r is perm[r] / top_k
+};
+
+hipError_t launch_gemm_dense(const GemmArgs& g, hipStream_t stream);
+hipError_t launch_gemm_grouped(const GemmArgs& g, hipStream_t stream);
+int64_t grouped_max_mtiles(int64_t R, int64_t E);
+int grouped_tile_m();
+
+hipError_t launch_moe_plan(const int32_t* ids, int64_t T, int top_k, int64_t E, int tile_m,
+                           int32_t* offsets, int32_t* tile_start, int32_t* perm, int32_t* pos,
+                           int32_t* block_hist, hipStream_t stream);
+int64_t moe_plan_blocks(int64_t R);
+
+hipError_t launch_moe_combine(const uint16_t* y_perm, const int32_t* pos, const uint16_t* topk_w,
+                              int64_t T, int top_k, int64_t N, uint16_t* out, hipStream_t stream);
+
+}  // namespace rq

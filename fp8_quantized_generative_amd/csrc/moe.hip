@@ -1,0 +1,199 @@
+// MoE routing plan and weighted combine for the expert grouped GEMM (gfx950).
+//
+// Page "Quantized Inference for OneRec-V2：生成式推荐开始直接吃 LLM 量化栈", section
+// 关键证据, runs the sparse-MoE experts as one grouped GEMM on the quantized path; page
+// "FP8量化在生成式推荐系统OneRec-V2中的优化实践", §2.1, keeps the routing gate in FP16, so
+// its top-k expert ids and weights are inputs here.
+//
+// Plan: slot j = t * top_k + k goes to expert ids[j].  The canonical permuted order sorts
+// slots by (expert, j) - a stable counting sort - computed without any host round trip:
+//   1. plan_hist:    per block of 1024 slots, a histogram over experts (LDS atomics on
+//                    integer counts, so the result is deterministic);
+//   2. plan_scan:    one workgroup turns the block histograms into per-expert offsets,
+//                    per-(block, expert) base rows and the per-expert M-tile prefix sum
+//                    that the grouped GEMM schedules from;
+//   3. plan_scatter: each slot's rank among equal experts inside its wavefront comes from
+//                    ballots over the bits of the expert id; ranks across the block's 16
+//                    wavefronts come from an LDS prefix; perm[row] = j and pos[j] = row.
+// Combine: out[t] = fl16(sum_k fl32(w[t][k] * y_perm[pos[t*top_k + k]])), summed in FP32 in
+// slot order (each FP16 x FP16 product is exact in FP32), 16-byte loads and stores.
+
+#include "common.h"
+
+namespace rq {
+namespace {
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
+
+__device__ __forceinline__ int expert_of(const int32_t* ids, int64_t j, int E) {
+  int e = ids[j];
+  e = e < 0 ? 0 : e;
+  return e >= E ? E - 1 : e;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_hist(const int32_t* __restrict__ ids, int64_t R, int E,
+                                                          int32_t* __restrict__ block_hist) {
+  extern __shared__ int32_t hist[];
+  for (int e = threadIdx.x; e < E; e += kPlanThreads) hist[e] = 0;
+  __syncthreads();
+  const int64_t j = (int64_t)blockIdx.x * kPlanThreads + threadIdx.x;
+  if (j < R) atomicAdd(&hist[expert_of(ids, j, E)], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kPlanThreads) block_hist[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+// Exclusive scan of one value per thread across the 1024-thread block.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wave_sums, int& total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wave_sums[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kPlanWaves ? wave_sums[lane] : 0;
+    int wi = w;
+#pragma unroll
+    for (int off = 1; off < kPlanWaves; off <<= 1) {
+      const int o = __shfl_up(wi, off, 64);
+      if (lane >= off) wi += o;
+    }
+    if (lane < kPlanWaves) wave_sums[lane] = wi - w;  // exclusive wave prefix
+    if (lane == kPlanWaves - 1) wave_sums[kPlanWaves] = wi;
+  }
+  __syncthreads();
+  total = wave_sums[kPlanWaves];
+  return wave_sums[wave] + incl - v;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_scan(int32_t* __restrict__ block_hist, int nblocks, int E,
+                                                          int tile_m, int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ tile_start) {
+  __shared__ int wave_sums[kPlanWaves + 1];
+  const int e = threadIdx.x;  // E <= 1024
+  int count = 0;
+  if (e < E)
+    for (int b = 0; b < nblocks; ++b) count += block_hist[(int64_t)b * E + e];
+  int total_rows, total_tiles;
+  const int off = block_exclusive_scan(e < E ? count : 0, wave_sums, total_rows);
+  __syncthreads();
+  const int tiles = e < E ? (count + tile_m - 1) / tile_m : 0;
+  const int tstart = block_exclusive_scan(tiles, wave_sums, total_tiles);
+  if (e < E) {
+    offsets[e] = off;
+    tile_start[e] = tstart;
+    int run = off;
+    for (int b = 0; b < nblocks; ++b) {
+      const int c = block_hist[(int64_t)b * E + e];
+      block_hist[(int64_t)b * E + e] = run;  // becomes the base row of (block b, expert e)
+      run += c;
+    }
+  }
+  if (e == 0) {
+    offsets[E] = total_rows;
+    tile_start[E] = total_tiles;
+  }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_scatter(const int32_t* __restrict__ ids, int64_t R, int E,
+                                                             int nbits, const int32_t* __restrict__ block_base,
+                                                             int32_t* __restrict__ perm, int32_t* __restrict__ pos) {
+  extern __shared__ int32_t wcount[];  // [kPlanWaves][E]
+  for (int i = threadIdx.x; i < kPlanWaves * E; i += kPlanThreads) wcount[i] = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t j = (int64_t)blockIdx.x * kPlanThreads + threadIdx.x;
+  const bool valid = j < R;
+  const int e = valid ? expert_of(ids, j, E) : 0;
+  uint64_t peers = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const uint64_t m = __ballot(((e >> b) & 1) != 0);
+    peers &= ((e >> b) & 1) ? m : ~m;
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int rank = __popcll(peers & below);
+  if (valid && rank == 0) wcount[wave * E + e] = __popcll(peers);
+  __syncthreads();
+  for (int x = threadIdx.x; x < E; x += kPlanThreads) {
+    int run = 0;
+    for (int w = 0; w < kPlanWaves; ++w) {
+      const int c = wcount[w * E + x];
+      wcount[w * E + x] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  if (valid) {
+    const int row = block_base[(int64_t)blockIdx.x * E + e] + wcount[wave * E + e] + rank;
+    perm[row] = (int32_t)j;
+    pos[j] = row;
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y_perm,
+                                                      const int32_t* __restrict__ pos,
+                                                      const uint16_t* __restrict__ topk_w, int top_k,
+                                                      int64_t N, uint16_t* __restrict__ out) {
+  const int64_t t = blockIdx.x;
+  const int64_t nchunk = N / 8;
+  for (int64_t c = threadIdx.x; c < nchunk; c += blockDim.x) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < top_k; ++k) {
+      const int64_t slot = t * top_k + k;
+      const float w = half_bits_to_float(topk_w[slot]);
+      const uint4 v = ld_global_16(y_perm + (int64_t)pos[slot] * N + 8 * c);
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = acc[2 * i] + w * half_bits_to_float(d[i] & 0xFFFFu);
+        acc[2 * i + 1] = acc[2 * i + 1] + w * half_bits_to_float(d[i] >> 16);
+      }
+    }
+    uint4 o;
+    o.x = float_to_half_bits(acc[0]) | (float_to_half_bits(acc[1]) << 16);
+    o.y = float_to_half_bits(acc[2]) | (float_to_half_bits(acc[3]) << 16);
+    o.z = float_to_half_bits(acc[4]) | (float_to_half_bits(acc[5]) << 16);
+    o.w = float_to_half_bits(acc[6]) | (float_to_half_bits(acc[7]) << 16);
+    st_global_16(out + t * N + 8 * c, o);
+  }
+}
+
+}  // namespace
+
+int64_t moe_plan_blocks(int64_t R) { return (R + kPlanThreads - 1) / kPlanThreads; }
+
+hipError_t launch_moe_plan(const int32_t* ids, int64_t T, int top_k, int64_t E, int tile_m,
+                           int32_t* offsets, int32_t* tile_start, int32_t* perm, int32_t* pos,
+                           int32_t* block_hist, hipStream_t stream) {
+  const int64_t R = T * top_k;
+  const int nb = (int)moe_plan_blocks(R);
+  const int e = (int)E;
+  int nbits = 0;
+  while ((1 << nbits) < e) ++nbits;
+  if (nb > 0) {
+    plan_hist<<<dim3(nb), dim3(kPlanThreads), e * sizeof(int32_t), stream>>>(ids, R, e, block_hist);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  plan_scan<<<dim3(1), dim3(kPlanThreads), 0, stream>>>(block_hist, nb, e, tile_m, offsets, tile_start);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || nb == 0) return err;
+  plan_scatter<<<dim3(nb), dim3(kPlanThreads), kPlanWaves * e * sizeof(int32_t), stream>>>(
+      ids, R, e, nbits, block_hist, perm, pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_combine(const uint16_t* y_perm, const int32_t* pos, const uint16_t* topk_w,
+                              int64_t T, int top_k, int64_t N, uint16_t* out, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  combine_kernel<<<dim3((unsigned)T), dim3(256), 0, stream>>>(y_perm, pos, topk_w, top_k, N, out);
+  return hipGetLastError();
+}
+
+}  // namespace rq

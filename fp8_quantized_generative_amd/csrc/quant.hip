@@ -1,0 +1,205 @@
+// Per-row FP8 E4M3 quantizer for gfx950: one 64-lane wavefront per row.
+//
+// Serves the per-output-channel weight quantization (offline) and the per-token
+// activation quantization (run time) that page "Quantized Inference for OneRec-V2：
+// 生成式推荐开始直接吃 LLM 量化栈", section 关键证据, describes; the recipe (scale from the
+// row's absolute maximum with an epsilon floor, round, saturate) is the per-token
+// quantizer of page "FP8量化在生成式推荐系统OneRec-V2中的优化实践", §2.2, read for E4M3
+// with the +/-448 range of its §1.2.
+//
+// Per row of K values:
+//   amax = max|x_i|                      (FP16 magnitudes compared as integers)
+//   s    = fl32(max(amax, 2^-24) / 448)  (correctly rounded FP32 division)
+//   q_i  = sign(x_i) | E4M3_RNE(min(fl32(|x_i| / s), 448))
+//
+// The per-element quotient uses Markstein's correction: with y = fl32(1/s) correctly
+// rounded, q0 = fl32(|x| * y), r = fma(-q0, s, |x|) (exact) and q = fma(r, y, q0) is the
+// correctly rounded |x| / s.  For this kernel's domain (|x| an FP16 value no larger than
+// the row's FP16 amax, s derived from that amax) the identity was checked exhaustively,
+// all 5.0e8 (x, amax) pairs, so the quotient is bit-identical to an IEEE division at a
+// third of its cost.  Working on |x| and OR-ing the FP16 sign bit into the byte keeps
+// -0 and negative underflow as 0x80 (RNE is symmetric in the sign).
+//
+// The FP32 -> E4M3 cast is the hardware v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950, round to
+// nearest even) on inputs already clamped to [0, 448], so it never sees an out-of-range
+// value.
+//
+// RQ_ACT_SILU_MUL rows are [g (K) | u (K)] FP16; the quantized row is
+// h = fl16(silu(g) * u) computed in FP32, so the SiLU, the FP16 rounding of h and the
+// quantization happen in one pass over HBM.
+//
+// Memory: each lane owns 16-byte chunks c = lane + 64 j of the row (8 FP16 values),
+// held in registers between the amax reduction and the cast, so the input is read from
+// HBM once; loads and stores are 16- and 8-byte vectors, contiguous across the wave.
+// Rows wider than 8192 values fall back to a two-pass loop that re-reads the row.
+
+#include "common.h"
+
+namespace rq {
+namespace {
+
+constexpr int kRowsPerBlock = 4;  // 4 wavefronts of 64 lanes, one row each
+
+__device__ __forceinline__ uint32_t absmax_packed(uint4 v, uint32_t m) {
+  // max over the 8 FP16 magnitudes; for non-NaN FP16, magnitude order = integer order
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
+    m = m > lo ? m : lo;
+    m = m > hi ? m : hi;
+  }
+  return m;
+}
+
+__device__ __forceinline__ uint32_t silu_mul_pair(uint32_t g2, uint32_t u2) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    float g = half_bits_to_float((g2 >> (16 * i)) & 0xFFFFu);
+    float u = half_bits_to_float((u2 >> (16 * i)) & 0xFFFFu);
+    float silu = __fdividef(g, 1.0f + __expf(-g));
+    out |= float_to_half_bits(silu * u) << (16 * i);
+  }
+  return out;
+}
+
+__device__ __forceinline__ uint4 silu_mul8(uint4 g, uint4 u) {
+  return make_uint4(silu_mul_pair(g.x, u.x), silu_mul_pair(g.y, u.y),
+                    silu_mul_pair(g.z, u.z), silu_mul_pair(g.w, u.w));
+}
+
+__device__ __forceinline__ float quotient(uint32_t hbits, float s, float rcp) {
+  float ax = half_bits_to_float(hbits & 0x7FFFu);
+  float q0 = ax * rcp;
+  float r = __builtin_fmaf(-q0, s, ax);
+  float q = __builtin_fmaf(r, rcp, q0);
+  return __builtin_fminf(q, kFp8Max);
+}
+
+// Four FP16 values (two packed words) -> four E4M3 bytes (one word).
+__device__ __forceinline__ uint32_t cast4(uint32_t d0, uint32_t d1, float s, float rcp) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(quotient(d0, s, rcp), quotient(d0 >> 16, s, rcp), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(quotient(d1, s, rcp), quotient(d1 >> 16, s, rcp), w, true);
+  uint32_t signs = ((d0 >> 8) & 0x80u) | ((d0 >> 16) & 0x8000u) | ((d1 << 8) & 0x800000u) |
+                   (d1 & 0x80000000u);
+  return (uint32_t)w | signs;
+}
+
+__device__ __forceinline__ void row_scale(uint32_t amax_bits, float& s, float& rcp) {
+  float amax = half_bits_to_float(amax_bits);
+  s = __fdiv_rn(__builtin_fmaxf(amax, kScaleFloor), kFp8Max);
+  rcp = __fdiv_rn(1.0f, s);
+}
+
+template <int CPL, bool SILU>
+__global__ __launch_bounds__(256) void quant_rows_regs(const uint16_t* __restrict__ x, int64_t rows,
+                                                       int K, uint8_t* __restrict__ q,
+                                                       float* __restrict__ scale,
+                                                       uint16_t* __restrict__ h_out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int nchunk = K >> 3;
+  const int64_t in_stride = SILU ? 2 * (int64_t)K : (int64_t)K;
+  const uint16_t* xr = x + row * in_stride;
+
+  uint4 v[CPL];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = lane + 64 * j;
+    v[j] = make_uint4(0, 0, 0, 0);
+    if (c < nchunk) {
+      if (SILU) {
+        v[j] = silu_mul8(ld_global_16(xr + 8 * c), ld_global_16(xr + K + 8 * c));
+      } else {
+        v[j] = ld_global_16(xr + 8 * c);
+      }
+      amax = absmax_packed(v[j], amax);
+    }
+  }
+  amax = wave_max_u32(amax);
+  float s, rcp;
+  row_scale(amax, s, rcp);
+
+  uint8_t* qr = q + row * (int64_t)K;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = lane + 64 * j;
+    if (c < nchunk) {
+      uint2 out;
+      out.x = cast4(v[j].x, v[j].y, s, rcp);
+      out.y = cast4(v[j].z, v[j].w, s, rcp);
+      *reinterpret_cast<uint2*>(qr + 8 * c) = out;
+      if (SILU && h_out != nullptr) st_global_16(h_out + row * (int64_t)K + 8 * c, v[j]);
+    }
+  }
+  if (lane == 0) scale[row] = s;
+}
+
+// Rows wider than 64 * 8 * 16 values: two passes, the second re-reading the row.
+template <bool SILU>
+__global__ __launch_bounds__(256) void quant_rows_loop(const uint16_t* __restrict__ x, int64_t rows,
+                                                       int64_t K, uint8_t* __restrict__ q,
+                                                       float* __restrict__ scale,
+                                                       uint16_t* __restrict__ h_out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int64_t nchunk = K >> 3;
+  const int64_t in_stride = SILU ? 2 * K : K;
+  const uint16_t* xr = x + row * in_stride;
+  auto chunk = [&](int64_t c) -> uint4 {
+    if (SILU) return silu_mul8(ld_global_16(xr + 8 * c), ld_global_16(xr + K + 8 * c));
+    return ld_global_16(xr + 8 * c);
+  };
+  uint32_t amax = 0;
+  for (int64_t c = lane; c < nchunk; c += 64) amax = absmax_packed(chunk(c), amax);
+  amax = wave_max_u32(amax);
+  float s, rcp;
+  row_scale(amax, s, rcp);
+  uint8_t* qr = q + row * K;
+  for (int64_t c = lane; c < nchunk; c += 64) {
+    uint4 v = chunk(c);
+    uint2 out;
+    out.x = cast4(v.x, v.y, s, rcp);
+    out.y = cast4(v.z, v.w, s, rcp);
+    *reinterpret_cast<uint2*>(qr + 8 * c) = out;
+    if (SILU && h_out != nullptr) st_global_16(h_out + row * K + 8 * c, v);
+  }
+  if (lane == 0) scale[row] = s;
+}
+
+template <bool SILU>
+hipError_t launch_impl(const uint16_t* x, int64_t rows, int64_t K, uint8_t* q, float* scale,
+                       uint16_t* h, hipStream_t stream) {
+  const int64_t nchunk = K / 8;
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  const dim3 block(64 * kRowsPerBlock);
+  const int k = (int)K;
+  if (nchunk <= 64)
+    quant_rows_regs<1, SILU><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h);
+  else if (nchunk <= 128)
+    quant_rows_regs<2, SILU><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h);
+  else if (nchunk <= 256)
+    quant_rows_regs<4, SILU><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h);
+  else if (nchunk <= 512)
+    quant_rows_regs<8, SILU><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h);
+  else if (nchunk <= 1024)
+    quant_rows_regs<16, SILU><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h);
+  else
+    quant_rows_loop<SILU><<<grid, block, 0, stream>>>(x, rows, K, q, scale, h);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t K, int act, uint8_t* q,
+                             float* scale, uint16_t* h, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  if (act == 1) return launch_impl<true>(x, rows, K, q, scale, h, stream);
+  return launch_impl<false>(x, rows, K, q, scale, nullptr, stream);
+}
+
+}  // namespace rq

@@ -1,0 +1,157 @@
+/*
+ * rq_fp8.h - C ABI of the MI355X (gfx950) W8A8 FP8 linear library.
+ *
+ * The library computes the FP8 post-training-quantized linear used for OneRec-V2
+ * serving.  Page "Quantized Inference for OneRec-V2：生成式推荐开始直接吃 LLM 量化栈",
+ * section 关键证据, states the method: weights quantized offline per output channel,
+ * activations quantized per token at run time, an FP8 matrix product accumulated in
+ * FP32, and the result cast back to FP16 before the next layer; it is applied to the
+ * attention q/k/v/o linears, the dense FFN linears and the sparse-MoE expert grouped
+ * GEMM.  Page "FP8量化在生成式推荐系统OneRec-V2中的优化实践" fixes the FP8 range at
+ * +/-448 (§1.2, i.e. OCP E4M3), sketches the per-token quantizer (§2.2) and shows the
+ * FP16 -> quantize -> FP8 GEMM -> dequantize -> FP16 flow (§2.3, Fig. 2).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensor pointers are DEVICE pointers to row-major, contiguous memory.  FP16 tensors
+ *   are IEEE binary16 bit patterns (uint16_t), FP8 tensors are OCP E4M3 bytes, scales
+ *   are FP32 dequantization multipliers (value = decode(byte) * scale).
+ * - FP16 and FP8 tensor pointers and the workspace must be 16-byte aligned; scale and
+ *   index arrays 4-byte aligned.  Otherwise the call returns RQ_ERR_ALIGN.
+ * - K and N must be positive multiples of 16 (RQ_ERR_ALIGN otherwise).  Row counts
+ *   (M, T, B) may be 0: the call then validates its arguments and enqueues nothing.
+ * - The caller owns every buffer; the library never allocates device memory.  Scratch
+ *   space comes from the caller's workspace, sized by the *_workspace_size calls.
+ * - `stream` is a hipStream_t (NULL = the default stream).  All work is enqueued
+ *   asynchronously on it; no call synchronizes the host, the ragged MoE row counts
+ *   included.  Concurrent calls must use distinct workspaces.
+ * - Arguments are validated on the host before anything is enqueued.  On any error
+ *   nothing has been enqueued.  A failing kernel launch returns RQ_ERR_HIP.  A device
+ *   other than gfx950 returns RQ_ERR_UNSUPPORTED.
+ * - Outputs are deterministic (no floating-point atomics): the same inputs give the
+ *   same bytes on every run.  Outputs must not alias inputs.
+ *
+ * Quantization (rq_fp8_quant_weights, and inside the linears): for each row x of
+ * length K, amax = max|x_i|, s = fl32(max(amax, 2^-24) / 448) with a correctly rounded
+ * FP32 division, q_i = E4M3(fl32(x_i / s)) rounded to nearest even and saturated at
+ * +/-448, the sign kept (-0 -> 0x80).
+ *
+ * Linear: y[m][n] = fl16(fl32(acc[m][n] * s_x[m]) * s_w[n]) with
+ * acc = sum_k decode(x_q[m][k]) * decode(w_q[n][k]) accumulated in FP32, rounded to
+ * nearest even.  There is no bias.
+ */
+#ifndef RQ_FP8_H
+#define RQ_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RQ_OK = 0,
+  RQ_ERR_NULL = 1,        /* a required pointer is NULL */
+  RQ_ERR_SHAPE = 2,       /* a negative or unsupported size, or an unsupported top_k / E */
+  RQ_ERR_ALIGN = 3,       /* K or N not a multiple of 16, or a misaligned pointer */
+  RQ_ERR_WORKSPACE = 4,   /* workspace smaller than the *_workspace_size result */
+  RQ_ERR_UNSUPPORTED = 5, /* the current device is not gfx950 */
+  RQ_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed */
+  RQ_ERR_ARG = 7          /* an unknown act / layout value, or a missing topk_w */
+} rq_status;
+
+/* Activation applied to the FP16 input rows before they are quantized.
+ * RQ_ACT_SILU_MUL: each input row has 2K values [g (K) | u (K)] and the quantized row is
+ * h = fl16(silu(g) * u), silu(g) = g / (1 + exp(-g)) evaluated in FP32.  This is the FFN
+ * intermediate between the gate/up and down linears. */
+enum { RQ_ACT_NONE = 0, RQ_ACT_SILU_MUL = 1 };
+
+/* MoE input rows: one per token (quantized once, before dispatch) or one per routed
+ * slot in the canonical permuted order (see rq_fp8_moe_grouped_linear). */
+enum { RQ_MOE_IN_TOKENS = 0, RQ_MOE_IN_PERMUTED = 1 };
+
+/* MoE output rows: one per routed slot in the canonical permuted order, or one per
+ * token after the routing-weighted combine. */
+enum { RQ_MOE_OUT_PERMUTED = 0, RQ_MOE_OUT_COMBINED = 1 };
+
+/* Optional debug outputs (device pointers; any field may be NULL).
+ * a_q / a_scale: when given, the activation quantizer writes the E4M3 rows and scales
+ *   that the GEMM consumes into these buffers instead of the workspace, so they hold
+ *   exactly the GEMM's operand: [rows][K] bytes and [rows] floats.
+ * h: FP16 [rows][K], the SiLU*up rows (RQ_ACT_SILU_MUL only). */
+typedef struct {
+  uint8_t* a_q;
+  float* a_scale;
+  uint16_t* h;
+} rq_debug_out;
+
+/* Offline per-output-channel weight quantization (page "Quantized Inference for
+ * OneRec-V2", section 关键证据: weights quantized per channel, offline).
+ * w [B][N][K] FP16 -> w_q [B][N][K] E4M3, w_scale [B][N] FP32.  Each of the B*N rows is
+ * quantized independently with the row quantizer above, so applied to an [M][K]
+ * activation matrix it gives exactly the per-token quantization of rq_fp8_linear.
+ * Needs no workspace.  Any B, N >= 0; K > 0, K % 16 == 0. */
+int rq_fp8_quant_weights(const uint16_t* w, int64_t B, int64_t N, int64_t K,
+                         uint8_t* w_q, float* w_scale, void* stream);
+
+/* Bytes of workspace rq_fp8_linear needs for M rows of K quantized values
+ * (the quantized activation bytes and scales, each region 256-byte aligned). */
+size_t rq_fp8_linear_workspace_size(int64_t M, int64_t K, int act);
+
+/* W8A8 FP8 linear (pages: "Quantized Inference for OneRec-V2", section 关键证据;
+ * "FP8量化在生成式推荐系统OneRec-V2中的优化实践", §2.3 and Fig. 2).
+ * x [M][K] FP16 (or [M][2K] with RQ_ACT_SILU_MUL) is quantized per token into the
+ * workspace (or dbg->a_q / dbg->a_scale), multiplied with w_q [N][K] E4M3 and
+ * dequantized with w_scale [N] into y [M][N] FP16.
+ * Two kernels on `stream`: the row quantizer, then the FP8 MFMA GEMM with the
+ * scale/FP16 epilogue.  dbg may be NULL. */
+int rq_fp8_linear(const uint16_t* x, int64_t M, int64_t K, int act,
+                  const uint8_t* w_q, const float* w_scale, int64_t N,
+                  uint16_t* y, void* workspace, size_t workspace_bytes,
+                  const rq_debug_out* dbg, void* stream);
+
+/* Bytes of workspace rq_fp8_moe_grouped_linear needs.  E <= 1024, 1 <= top_k <= E. */
+size_t rq_fp8_moe_workspace_size(int64_t T, int top_k, int64_t E, int64_t N, int64_t K,
+                                 int in_layout, int act, int out_layout);
+
+/* Sparse-MoE expert grouped linear (page "Quantized Inference for OneRec-V2", section
+ * 关键证据: the MoE grouped GEMM is on the quantized path; page "FP8量化在生成式推荐系统
+ * OneRec-V2中的优化实践", §2.1: the routing gate stays FP16, so its top-k result is an
+ * input here).
+ *
+ * Routing: slot j = t * top_k + k of token t goes to expert topk_ids[t][k] (int32,
+ * must lie in [0, E); out-of-range ids are clamped into that range).  The canonical
+ * permuted order sorts the R = T * top_k slots by (expert, j) ascending; expert e owns
+ * permuted rows [offset_e, offset_e + count_e).
+ *
+ * Input rows: RQ_MOE_IN_TOKENS: x [T][K (or 2K)], one row per token, quantized once
+ * per token before dispatch; RQ_MOE_IN_PERMUTED: x [R][K (or 2K)] in canonical order.
+ * Permuted row r of expert e computes fl16(dequant(A_r . w_q[e]^T)) with w_q [E][N][K]
+ * E4M3 and w_scale [E][N].
+ * Output: RQ_MOE_OUT_PERMUTED: y [R][N] FP16 in canonical order;
+ * RQ_MOE_OUT_COMBINED: y [T][N] = fl16(sum_k fl32(topk_w[t][k] * y_perm[pos(t,k)])),
+ * summed in FP32 in slot order, topk_w [T][top_k] FP16 required.
+ * Experts with no rows read no weights.  A gate/up + SiLU + down expert FFN is two
+ * calls: (TOKENS, NONE, PERMUTED) then (PERMUTED, SILU_MUL, COMBINED).
+ * dbg->a_q / a_scale: T rows (TOKENS) or R rows (PERMUTED); dbg->h: R rows. */
+int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act,
+                              const int32_t* topk_ids, const uint16_t* topk_w,
+                              int64_t T, int top_k,
+                              const uint8_t* w_q, const float* w_scale,
+                              int64_t E, int64_t N, int64_t K,
+                              uint16_t* y, int out_layout,
+                              void* workspace, size_t workspace_bytes,
+                              const rq_debug_out* dbg, void* stream);
+
+/* Static description of a status code ("ok", "null pointer", ...). */
+const char* rq_status_string(int status);
+
+/* 1 if `device` is a gfx950 GPU the library can run on, 0 if not, -1 on a HIP error. */
+int rq_device_supported(int device);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RQ_FP8_H */

@@ -1,0 +1,150 @@
+"""The C ABI library loads, exports every symbol the header declares, and rejects bad
+arguments on the host with the documented status codes before touching a device.
+
+No compute call is made here (no GPU): every case fails validation, or is a documented
+no-op (zero rows), which returns before any device query.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rq_fp8.h")
+
+lib_mod = pytest.importorskip("fp8_quantized_generative_amd._lib")
+
+if not os.path.exists(lib_mod.LIB_PATH):
+    pytest.skip("librq_fp8.so not built", allow_module_level=True)
+
+RQ_ERR_NULL, RQ_ERR_SHAPE, RQ_ERR_ALIGN, RQ_ERR_WORKSPACE, RQ_ERR_ARG = 1, 2, 3, 4, 7
+FAKE = 0x10000  # a 16-byte-aligned, never dereferenced "device" address
+
+
+def _declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(rq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    lib = ctypes.CDLL(lib_mod.LIB_PATH)
+    names = _declared_symbols()
+    assert "rq_fp8_linear" in names and "rq_fp8_moe_grouped_linear" in names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(lib_mod.SIGNATURES)
+
+
+def test_status_strings():
+    lib = lib_mod.load()
+    assert lib.rq_status_string(0) == b"ok"
+    assert lib.rq_status_string(4) == b"workspace too small"
+    assert lib.rq_status_string(99) == b"unknown status"
+
+
+def test_workspace_sizes():
+    lib = lib_mod.load()
+    assert lib.rq_fp8_linear_workspace_size(4096, 2048, 0) == 4096 * 2048 + 4096 * 4
+    assert lib.rq_fp8_linear_workspace_size(3, 16, 0) == 256 + 256
+    assert lib.rq_fp8_linear_workspace_size(-1, 16, 0) == 0
+    a = lib.rq_fp8_moe_workspace_size(16384, 2, 32, 8192, 2048, 0, 0, 0)
+    b = lib.rq_fp8_moe_workspace_size(16384, 2, 32, 2048, 4096, 1, 1, 1)
+    assert a >= 16384 * 2048 and b >= 32768 * 4096 + 32768 * 2048 * 2
+
+
+def _linear(**kw):
+    args = dict(x=FAKE, M=64, K=512, act=0, w_q=FAKE, w_scale=FAKE, N=512, y=FAKE,
+                ws=FAKE, ws_bytes=1 << 30, dbg=None, stream=None)
+    args.update(kw)
+    lib = lib_mod.load()
+    return lib.rq_fp8_linear(args["x"], args["M"], args["K"], args["act"], args["w_q"], args["w_scale"],
+                             args["N"], args["y"], args["ws"], args["ws_bytes"], args["dbg"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(act=2), RQ_ERR_ARG),
+    (dict(M=-1), RQ_ERR_SHAPE),
+    (dict(K=0), RQ_ERR_SHAPE),
+    (dict(N=-16), RQ_ERR_SHAPE),
+    (dict(K=24), RQ_ERR_ALIGN),
+    (dict(N=40), RQ_ERR_ALIGN),
+    (dict(w_q=None), RQ_ERR_NULL),
+    (dict(w_scale=None), RQ_ERR_NULL),
+    (dict(x=None), RQ_ERR_NULL),
+    (dict(y=None), RQ_ERR_NULL),
+    (dict(x=FAKE + 8), RQ_ERR_ALIGN),
+    (dict(y=FAKE + 2), RQ_ERR_ALIGN),
+    (dict(w_scale=FAKE + 2), RQ_ERR_ALIGN),
+    (dict(ws_bytes=64 * 512), RQ_ERR_WORKSPACE),
+    (dict(ws=None), RQ_ERR_WORKSPACE),
+])
+def test_linear_rejects(kw, code):
+    assert _linear(**kw) == code
+
+
+def test_linear_zero_rows_is_noop():
+    assert _linear(M=0, x=None, y=None, ws=None, ws_bytes=0) == 0
+
+
+def test_linear_debug_buffers_replace_workspace():
+    d = lib_mod.DebugOut(FAKE, FAKE + 4, 0)
+    assert _linear(M=0, dbg=ctypes.byref(d)) == 0
+    d = lib_mod.DebugOut(FAKE + 4, 0, 0)
+    assert _linear(dbg=ctypes.byref(d)) == RQ_ERR_ALIGN
+
+
+def _moe(**kw):
+    args = dict(x=FAKE, il=0, act=0, ids=FAKE, w=FAKE, T=128, top_k=2, w_q=FAKE, w_scale=FAKE,
+                E=8, N=64, K=64, y=FAKE, ol=0, ws=FAKE, ws_bytes=1 << 30, dbg=None, stream=None)
+    args.update(kw)
+    lib = lib_mod.load()
+    return lib.rq_fp8_moe_grouped_linear(args["x"], args["il"], args["act"], args["ids"], args["w"], args["T"],
+                                         args["top_k"], args["w_q"], args["w_scale"], args["E"], args["N"],
+                                         args["K"], args["y"], args["ol"], args["ws"], args["ws_bytes"],
+                                         args["dbg"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(il=2), RQ_ERR_ARG),
+    (dict(ol=5), RQ_ERR_ARG),
+    (dict(act=-1), RQ_ERR_ARG),
+    (dict(T=-1), RQ_ERR_SHAPE),
+    (dict(E=0), RQ_ERR_SHAPE),
+    (dict(E=1025), RQ_ERR_SHAPE),
+    (dict(top_k=0), RQ_ERR_SHAPE),
+    (dict(top_k=9), RQ_ERR_SHAPE),
+    (dict(K=40), RQ_ERR_ALIGN),
+    (dict(N=8), RQ_ERR_ALIGN),
+    (dict(ids=None), RQ_ERR_NULL),
+    (dict(w_q=None), RQ_ERR_NULL),
+    (dict(ol=1, w=None), RQ_ERR_ARG),
+    (dict(ids=FAKE + 2), RQ_ERR_ALIGN),
+    (dict(ws_bytes=100), RQ_ERR_WORKSPACE),
+])
+def test_moe_rejects(kw, code):
+    assert _moe(**kw) == code
+
+
+def test_moe_zero_tokens_is_noop():
+    assert _moe(T=0, x=None, ids=None, y=None, ws=None, ws_bytes=0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), RQ_ERR_SHAPE),
+    (dict(K=8), RQ_ERR_ALIGN),
+    (dict(w=None), RQ_ERR_NULL),
+    (dict(w_scale=FAKE + 1), RQ_ERR_ALIGN),
+])
+def test_quant_weights_rejects(kw, code):
+    args = dict(w=FAKE, B=1, N=64, K=64, w_q=FAKE, w_scale=FAKE, stream=None)
+    args.update(kw)
+    lib = lib_mod.load()
+    assert lib.rq_fp8_quant_weights(args["w"], args["B"], args["N"], args["K"], args["w_q"],
+                                    args["w_scale"], args["stream"]) == code
+
+
+def test_quant_weights_zero_rows_is_noop():
+    lib = lib_mod.load()
+    assert lib.rq_fp8_quant_weights(None, 0, 64, 64, None, None, None) == 0

@@ -1,0 +1,146 @@
+"""GPU W8A8 linear vs the oracle.
+
+Quantized activations (the bytes and scales the GEMM actually consumed, returned through
+the debug outputs) must equal the oracle's bit for bit; FP16 outputs must lie within
+
+    |y - y_ref| <= 2 ulp16(y_ref) + 1e-3 * s_x[m] * s_w[n] * sum_k |dec(x_q) dec(w_q)|
+
+of the oracle's exactly accumulated result (``oracle.linear.check``).  Small shapes span
+several 128-wide tiles with ragged M, N and K tails; the full-size workloads (dense 64 x
+512 x 512, attention QKV/O at 4096 tokens, the FFN at 4096 tokens) are checked on every
+quantized byte and on sampled output rows, in the same launch configuration the
+benchmark uses.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import ffn, linear, quant
+from tests.gpu_util import case, dev, host, require_gpu, ulp_diff16
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_linear(x16, w16, act="none", rows=None):
+    rq = require_gpu()
+    w_q, w_s = rq.quant_weights(dev(w16))
+    y, dbg = rq.linear(dev(x16), w_q, w_s, act=act, debug=True)
+    return host(y), {k: (host(v) if v is not None else None) for k, v in dbg.items()}, host(w_q), host(w_s)
+
+
+def _check(x16, w16, act="none", sample_rows=None):
+    y, dbg, wq, ws = _run_linear(x16, w16, act)
+    wq_ref, ws_ref = quant.quantize_rows(w16)
+    assert np.array_equal(wq, wq_ref) and np.array_equal(ws.view(np.uint32), ws_ref.view(np.uint32))
+    if act == "silu_mul":
+        k = w16.shape[1]
+        assert ulp_diff16(dbg["h"], ffn.silu_mul(x16, k)).max() <= 1
+        rows_in = dbg["h"]
+    else:
+        rows_in = x16
+    xq_ref, sx_ref = quant.quantize_rows(rows_in)
+    assert np.array_equal(dbg["a_scale"].view(np.uint32), sx_ref.view(np.uint32))
+    assert np.array_equal(dbg["a_q"], xq_ref)
+    r = np.arange(x16.shape[0]) if sample_rows is None else sample_rows
+    ok, ratio, _ = linear.check(y[r], xq_ref[r], sx_ref[r], wq_ref, ws_ref)
+    assert ok, "max |d|/tol = %.3f" % ratio
+    return ratio
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (1, 16, 16), (3, 48, 112), (16, 128, 128), (64, 512, 512), (130, 144, 144),
+    (257, 272, 528), (200, 384, 2048), (129, 256, 8192), (5, 1040, 272),
+])
+def test_small_shapes(m, n, k):
+    case("linear m=%d n=%d k=%d" % (m, n, k))
+    rng = np.random.default_rng(m * 7 + n * 3 + k)
+    x = workloads.acts_outliers(rng, m, k)
+    w = workloads.weights(rng, (n, k))
+    _check(x, w)
+
+
+@pytest.mark.parametrize("m,n,k", [(5, 32, 64), (130, 144, 528), (64, 2048, 4096)])
+def test_silu_mul_linear(m, n, k):
+    case("linear silu m=%d n=%d k=%d" % (m, n, k))
+    rng = np.random.default_rng(m + n + k)
+    gu = (rng.standard_normal((m, 2 * k)) * 2).astype(np.float16)
+    w = workloads.weights(rng, (n, k))
+    _check(gu, w, act="silu_mul")
+
+
+def test_zero_rows_and_zero_row_output():
+    rq = require_gpu()
+    case("linear: M = 0 and an all-zero row")
+    w_q, w_s = rq.quant_weights(dev(workloads.weights(np.random.default_rng(0), (32, 64))))
+    y = rq.linear(torch.zeros((0, 64), dtype=torch.float16, device="cuda"), w_q, w_s)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 32)
+    x = np.random.default_rng(1).standard_normal((3, 64)).astype(np.float16)
+    x[1] = 0
+    y = host(rq.linear(dev(x), w_q, w_s))
+    assert np.all(y[1] == 0)
+
+
+def test_dense_small_full():
+    case("workload 1: dense 64 x 512 x 512")
+    d = workloads.make(1)
+    _check(d["x"], d["w"])
+
+
+def test_merged_qkv_equals_split():
+    rq = require_gpu()
+    case("attention: merged QKV equals three linears")
+    d = workloads.make(2, m=300, k=256)
+    w_q, w_s = rq.quant_weights(dev(d["w_qkv"]))
+    x = dev(d["x"])
+    merged = host(rq.linear(x, w_q, w_s))
+    parts = [host(rq.linear(x, w_q[i:i + 256].contiguous(), w_s[i:i + 256].contiguous())) for i in (0, 256, 512)]
+    assert np.array_equal(merged, np.concatenate(parts, axis=1))
+
+
+def _sample(m, rng, count=48):
+    r = rng.choice(m, size=count, replace=False)
+    return np.sort(np.concatenate([r, [0, m - 1]]))
+
+
+@pytest.mark.slow
+def test_attention_full_size():
+    case("workload 2: attention 4096 tokens, QKV 6144 and O 2048")
+    d = workloads.make(2)
+    rng = np.random.default_rng(2)
+    _check(d["x"], d["w_qkv"], sample_rows=_sample(4096, rng))
+    _check(d["attn_out"], d["w_o"], sample_rows=_sample(4096, rng))
+
+
+@pytest.mark.slow
+def test_ffn_full_size_chain():
+    rq = require_gpu()
+    case("workload 3: FFN 4096 tokens, gate/up 16384, down 2048 over K = 8192")
+    d = workloads.make(3)
+    rng = np.random.default_rng(3)
+    rows = _sample(4096, rng, 32)
+    _check(d["x"], d["w_gu"], sample_rows=rows)
+    # down projection over the GPU's own gate/up output
+    wgu_q, wgu_s = rq.quant_weights(dev(d["w_gu"]))
+    gu = rq.linear(dev(d["x"]), wgu_q, wgu_s)
+    wdn_q, wdn_s = rq.quant_weights(dev(d["w_dn"]))
+    y, dbg = rq.linear(gu, wdn_q, wdn_s, act="silu_mul", debug=True)
+    gu_h, h, aq, a_s, y = host(gu), host(dbg["h"]), host(dbg["a_q"]), host(dbg["a_scale"]), host(y)
+    assert ulp_diff16(h[rows], ffn.silu_mul(gu_h[rows], 8192)).max() <= 1
+    hq, hs = quant.quantize_rows(h)
+    assert np.array_equal(aq, hq) and np.array_equal(a_s.view(np.uint32), hs.view(np.uint32))
+    ok, ratio, _ = linear.check(y[rows], hq[rows], hs[rows], host(wdn_q), host(wdn_s))
+    assert ok, ratio
+
+
+def test_determinism():
+    rq = require_gpu()
+    case("linear determinism 512 x 2048 x 2048")
+    d = workloads.make(5, m=512, k=2048, f=64, f_moe=32, e=4)
+    w_q, w_s = rq.quant_weights(dev(d["w_o"]))
+    x = dev(d["x_o"])
+    a = host(rq.linear(x, w_q, w_s))
+    b = host(rq.linear(x, w_q, w_s))
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
