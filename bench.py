@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Throughput of the W8A8 FP8 linear hot path on one MI355X (gfx950).
+
+A step is one pass of the whole path over one batch of each synthetic workload, at full
+size, with inputs and quantized weights resident in HBM:
+
+* attention projections: 4096 tokens x hidden 2048, merged QKV (N = 6144) and O (2048);
+* dense FFN: 4096 tokens, gate/up (N = 16384), SiLU*up re-quantization, down (K = 8192);
+* sparse MoE: 16384 tokens, top-2 of 32 Zipf-loaded experts, grouped gate/up (8192),
+  SiLU*up, grouped down (K = 4096) and the weighted combine;
+* small-M layer: 512 rows through QKV, O, the dense FFN and the MoE expert FFN.
+
+Each linear runs per-token activation quantization, the FP8 MFMA GEMM with FP32
+accumulation and the fused dequantization to FP16 (weights are quantized once, offline,
+before timing).  ``value`` is algorithmic FP8 TFLOP/s: sum of 2*M*N*K over the real rows
+of every GEMM in the step (MoE counted over routed rows, no padding), divided by the
+wall time of K steps bracketed by device synchronizations.
+
+Also reported: the roofline of the dominant kernel (the MoE gate/up grouped GEMM),
+timed with HIP events around that launch inside every timed step; per-kernel event
+timings after the timed region; and the CPU oracle timed on a bounded sample.
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, published
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel breakdown")
+    ap.add_argument("--rocprof-summary", default=None, metavar="PATH",
+                    help="print per-(kernel, grid) dispatch statistics of a rocprofv3 output "
+                         "(a *_results.db, a *_kernel_trace.csv, or a directory holding one) and exit")
+    ap.add_argument("--only", default=None,
+                    help="comma list of attention,ffn,moe,layer_small_m to restrict the step (profiling)")
+    return ap.parse_args()
+
+
+class Hip:
+    """The HIP runtime already loaded by torch: events for kernel-level timing."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.lib.hipEventSynchronize(b) == 0
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return float(ms.value)
+
+
+class Path:
+    """Device-resident inputs, quantized weights, outputs and workspaces of one step."""
+
+    def __init__(self, rq, torch, only=None):
+        import workloads
+        self.rq, self.torch = rq, torch
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+        self.calls = []     # (workload, label, kind, flops, bytes_moved, fn)
+        self.flops = 0
+        want = set(only.split(",")) if only else {"attention", "ffn", "moe", "layer_small_m"}
+
+        def qw(w16):
+            wq, ws = rq.quant_weights(dev(w16))
+            return wq, ws
+
+        def add_linear(work, label, x, wq, ws, act="none"):
+            m = x.shape[0]
+            n, k = wq.shape
+            out = torch.empty((m, n), dtype=torch.float16, device="cuda")
+            ws_t = torch.empty(max(rq.linear_workspace_size(m, k, act), 1), dtype=torch.uint8, device="cuda")
+            fl = 2 * m * n * k
+            # bytes that must cross HBM at least once: activations in, weights, output
+            by = x.numel() * 2 + wq.numel() + m * n * 2
+            self.calls.append((work, label, "linear", fl, by,
+                               lambda: rq.linear(x, wq, ws, act=act, out=out, workspace=ws_t)))
+            self.flops += fl
+            return out
+
+        def add_moe(work, label, x, ids, wq, ws, il, act, ol, topk_w=None):
+            t, top_k = ids.shape
+            e, n, k = wq.shape
+            r = t * top_k
+            out = torch.empty((t if ol == "combined" else r, n), dtype=torch.float16, device="cuda")
+            ws_t = torch.empty(rq.moe_workspace_size(t, top_k, e, n, k, il, act, ol), dtype=torch.uint8,
+                               device="cuda")
+            fl = 2 * r * n * k
+            by = x.numel() * 2 + wq.numel() + r * n * 2
+            self.calls.append((work, label, "moe", fl, by,
+                               lambda: rq.moe_grouped_linear(x, ids, wq, ws, il, act, ol, topk_w=topk_w,
+                                                             out=out, workspace=ws_t)))
+            self.flops += fl
+            return out
+
+        self.config = {}
+        if "attention" in want:
+            d = workloads.make(2)
+            wqkv = qw(d["w_qkv"])
+            wo = qw(d["w_o"])
+            add_linear("attention", "qkv", dev(d["x"]), *wqkv)
+            add_linear("attention", "o", dev(d["attn_out"]), *wo)
+            self.config["attention"] = "4096 tokens x 2048; QKV 6144, O 2048"
+        if "ffn" in want:
+            d = workloads.make(3)
+            wgu, wdn = qw(d["w_gu"]), qw(d["w_dn"])
+            gu = add_linear("ffn", "gate_up", dev(d["x"]), *wgu)
+            add_linear("ffn", "down", gu, *wdn, act="silu_mul")
+            self.config["ffn"] = "4096 tokens x 2048; gate/up 2x8192, down K=8192"
+        if "moe" in want:
+            d = workloads.make(4)
+            wgu, wdn = qw(d["w_gu"]), qw(d["w_dn"])
+            ids, tw = dev(d["ids"].astype(np.int32)), dev(d["topk_w"])
+            counts = np.bincount(d["ids"].reshape(-1), minlength=32)
+            gu = add_moe("moe", "gate_up", dev(d["x"]), ids, *wgu, "tokens", "none", "permuted")
+            self.dominant = len(self.calls) - 1
+            add_moe("moe", "down", gu, ids, *wdn, "permuted", "silu_mul", "combined", topk_w=tw)
+            self.config["moe"] = ("16384 tokens x 2048; top-2 of 32 experts (Zipf 1.1; max %d, min nonzero %d, "
+                                  "%d empty rows of 32768); gate/up 2x4096, down K=4096"
+                                  % (counts.max(), counts[counts > 0].min(), int((counts == 0).sum())))
+            del d
+        if "layer_small_m" in want:
+            d = workloads.make(5)
+            add_linear("layer_small_m", "qkv", dev(d["x_qkv"]), *qw(d["w_qkv"]))
+            add_linear("layer_small_m", "o", dev(d["x_o"]), *qw(d["w_o"]))
+            gu = add_linear("layer_small_m", "gate_up", dev(d["x_ffn"]), *qw(d["w_gu"]))
+            add_linear("layer_small_m", "down", gu, *qw(d["w_dn"]), act="silu_mul")
+            ids, tw = dev(d["ids"].astype(np.int32)), dev(d["topk_w"])
+            g2 = add_moe("layer_small_m", "moe_gate_up", dev(d["x_moe"]), ids, *qw(d["w_gu_moe"]),
+                         "tokens", "none", "permuted")
+            add_moe("layer_small_m", "moe_down", g2, ids, *qw(d["w_dn_moe"]), "permuted", "silu_mul",
+                    "combined", topk_w=tw)
+            self.config["layer_small_m"] = "512 rows (32 requests x 16 beams); one layer: QKV, O, FFN 8192, MoE 4096"
+            del d
+        if not hasattr(self, "dominant"):
+            self.dominant = max(range(len(self.calls)), key=lambda i: self.calls[i][3])
+        torch.cuda.synchronize()
+
+    def step(self, hook=None):
+        for i, c in enumerate(self.calls):
+            if hook is not None and i == hook[0]:
+                self.rq._lib.load().rq_time_next_kernel(hook[1], hook[2], hook[3])
+            c[5]()
+
+
+def kernel_breakdown(path, hip, reps=5):
+    """Per-call event timing of the GEMM and quantization kernels (after the timed region)."""
+    from fp8_quantized_generative_amd import _lib
+    lib = _lib.load()
+    rows = []
+    for i, (work, label, kind, fl, by, fn) in enumerate(path.calls):
+        res = {}
+        for kname, kid in (("gemm", _lib.RQ_KERNEL_GEMM), ("quant", _lib.RQ_KERNEL_QUANT)):
+            ts = []
+            for _ in range(reps):
+                a, b = hip.event(), hip.event()
+                lib.rq_time_next_kernel(kid, a, b)
+                fn()
+                ts.append(hip.elapsed_ms(a, b))
+            res[kname] = float(np.median(ts))
+        rows.append({"workload": work, "call": label, "gemm_us": round(res["gemm"] * 1e3, 2),
+                     "gemm_tflops": round(fl / (res["gemm"] * 1e-3) / 1e12, 1),
+                     "gemm_frac_fp8_peak": round(fl / (res["gemm"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                     "gemm_min_hbm_gbs": round(by / (res["gemm"] * 1e-3) / 1e9, 1),
+                     "quant_us": round(res["quant"] * 1e3, 2)})
+    return rows
+
+
+def cpu_baseline(seconds_hint=15.0):
+    """The CPU oracle on a bounded sample of the same workloads (rows sampled per linear)."""
+    import workloads
+    from oracle import ffn, linear, moe, quant
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+    rows = 64
+    d2 = workloads.make(2, m=rows)
+    d3 = workloads.make(3, m=rows)
+    d4 = workloads.make(4, t=rows, e=4)
+    # offline weight quantization (untimed); one expert's weights for the MoE sample
+    wqkv = quant.quantize_rows(d2["w_qkv"])
+    wo = quant.quantize_rows(d2["w_o"])
+    wgu = quant.quantize_rows(d3["w_gu"])
+    wdn = quant.quantize_rows(d3["w_dn"])
+    egu = [quant.quantize_rows(d4["w_gu"][e]) for e in range(4)]
+    edn = [quant.quantize_rows(d4["w_dn"][e]) for e in range(4)]
+    egu_q = np.stack([q for q, _ in egu]); egu_s = np.stack([s for _, s in egu])
+    edn_q = np.stack([q for q, _ in edn]); edn_s = np.stack([s for _, s in edn])
+    flops = 0
+    t0 = time.perf_counter()
+    xq, xs = quant.quantize_rows(d2["x"])
+    linear.linear(xq, xs, *wqkv)
+    flops += 2 * rows * 6144 * 2048
+    aq, as_ = quant.quantize_rows(d2["attn_out"])
+    linear.linear(aq, as_, *wo)
+    flops += 2 * rows * 2048 * 2048
+    xq, xs = quant.quantize_rows(d3["x"])
+    gu = linear.linear(xq, xs, *wgu)
+    hq, hs = quant.quantize_rows(ffn.silu_mul(gu, 8192))
+    linear.linear(hq, hs, *wdn)
+    flops += 2 * rows * 16384 * 2048 + 2 * rows * 2048 * 8192
+    r1 = moe.grouped_linear(d4["x"], moe.IN_TOKENS, moe.ACT_NONE, d4["ids"], egu_q, egu_s)
+    moe.grouped_linear(r1["y"], moe.IN_PERMUTED, moe.ACT_SILU_MUL, d4["ids"], edn_q, edn_s,
+                       moe.OUT_COMBINED, d4["topk_w"])
+    flops += 2 * rows * 2 * 8192 * 2048 + 2 * rows * 2 * 2048 * 4096
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "blas_threads": blas_threads, "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "64 token rows through each linear of the step: attention QKV and O, dense FFN "
+                      "gate/up + SiLU + down, and the MoE expert FFN (F = 4096) over 64 tokens, top-2 of 4 "
+                      "full-size experts; "
+                      "float64 exact GEMMs; weights quantized beforehand (untimed)"}
+
+
+def _rocprof_rows(path):
+    """(kernel name, grid threads, workgroup threads, duration ns) for every dispatch."""
+    import glob
+    import sqlite3
+    if os.path.isdir(path):
+        found = sorted(glob.glob(os.path.join(path, "**", "*_results.db"), recursive=True) +
+                       glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True))
+        if not found:
+            raise SystemExit("no rocprofv3 output under %s" % path)
+        path = found[0]
+    if path.endswith(".db"):
+        db = sqlite3.connect(path)
+        q = "select name, grid_x * grid_y * grid_z, workgroup_x * workgroup_y * workgroup_z, duration from kernels"
+        return path, [(r[0], int(r[1]), int(r[2]), int(r[3])) for r in db.execute(q)]
+    import csv
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            grid = int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1)) * int(r.get("Grid_Size_Z", 1))
+            wg = int(r["Workgroup_Size_X"]) * int(r.get("Workgroup_Size_Y", 1)) * int(r.get("Workgroup_Size_Z", 1))
+            rows.append((r["Kernel_Name"], grid, wg, int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    return path, rows
+
+
+def rocprof_summary(path):
+    src, rows = _rocprof_rows(path)
+    groups = {}
+    for name, grid, wg, dur in rows:
+        groups.setdefault((name, grid // max(wg, 1)), []).append(dur)
+    total = sum(d for v in groups.values() for d in v)
+    print("# rocprofv3 kernel trace: %s" % os.path.basename(src))
+    print("# %-72s %9s %6s %11s %11s %11s %6s" % ("kernel", "workgroups", "calls", "avg_us", "min_us", "max_us", "pct"))
+    for (name, nwg), durs in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        short = name.replace("rq::(anonymous namespace)::", "").replace("unsigned short", "u16")
+        short = short.split("(")[0] if len(short) > 72 else short
+        print("  %-72s %9d %6d %11.2f %11.2f %11.2f %5.1f%%" % (
+            short[:72], nwg, len(durs), np.mean(durs) / 1e3, min(durs) / 1e3, max(durs) / 1e3,
+            100.0 * sum(durs) / total))
+
+
+def main():
+    args = parse()
+    if args.rocprof_summary:
+        rocprof_summary(args.rocprof_summary)
+        return
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import fp8_quantized_generative_amd as rq
+    from fp8_quantized_generative_amd import _lib
+
+    torch.cuda.set_device(0)
+    hip = Hip()
+    print("[bench] building inputs", file=sys.stderr, flush=True)
+    path = Path(rq, torch, args.only)
+    print("[bench] %d calls per step, %.1f GFLOP" % (len(path.calls), path.flops / 1e9), file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        path.step()
+    torch.cuda.synchronize()
+
+    evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        path.step(hook=(path.dominant, _lib.RQ_KERNEL_GEMM, evs[s][0], evs[s][1]))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    value = path.flops * args.steps / elapsed / 1e12
+    print("[bench] timed %d steps: %.3f ms/step" % (args.steps, ms_per_step), file=sys.stderr, flush=True)
+
+    dom = path.calls[path.dominant]
+    dom_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in evs]))
+    achieved = dom[3] / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "gemm_fp8_kernel<grouped> (%s %s)" % (dom[0], dom[1]),
+                "flops_per_launch": dom[3], "avg_launch_us": round(dom_ms * 1e3, 2)}
+
+    result = {
+        "metric": "FP8 linear TFLOP/s (dense + MoE grouped) and % of MI355X FP8 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate, fp16 out)",
+        "data": "synthetic",
+        "frac_fp8_peak": round(value / FP8_PEAK_TFLOPS, 4),
+        "config": {"workload": "+".join(path.config) + " (full-size W8A8 FP8 linears, one step each)",
+                   **path.config, "gflop_per_step": round(path.flops / 1e9, 2)},
+        "roofline": roofline,
+    }
+    if not args.no_kernels:
+        print("[bench] per-kernel breakdown", file=sys.stderr, flush=True)
+        result["kernels"] = kernel_breakdown(path, hip)
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        del path
+        torch.cuda.empty_cache()
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -13,6 +13,7 @@ RQ_OK = 0
 RQ_ACT_NONE, RQ_ACT_SILU_MUL = 0, 1
 RQ_MOE_IN_TOKENS, RQ_MOE_IN_PERMUTED = 0, 1
 RQ_MOE_OUT_PERMUTED, RQ_MOE_OUT_COMBINED = 0, 1
+RQ_KERNEL_QUANT, RQ_KERNEL_GEMM, RQ_KERNEL_COMBINE = 0, 1, 2
 
 # Every symbol the header declares, with (restype, argtypes).
 _P = ctypes.c_void_p
@@ -33,6 +34,7 @@ SIGNATURES = {
     "rq_fp8_moe_workspace_size": (_SZ, [_I64, _I, _I64, _I64, _I64, _I, _I, _I]),
     "rq_fp8_moe_grouped_linear": (_I, [_P, _I, _I, _P, _P, _I64, _I, _P, _P, _I64, _I64, _I64,
                                        _P, _I, _P, _SZ, ctypes.POINTER(DebugOut), _P]),
+    "rq_time_next_kernel": (_I, [_I, _P, _P]),
     "rq_status_string": (ctypes.c_char_p, [_I]),
     "rq_device_supported": (_I, [_I]),
 }

@@ -13,6 +13,26 @@ constexpr size_t kAlign = 256;
 constexpr int64_t kMaxExperts = 1024;
 constexpr int kMaxDevices = 64;
 
+// One-shot per-thread timing hooks (rq_time_next_kernel).
+thread_local hipEvent_t t_hook_start[RQ_KERNEL_KINDS] = {};
+thread_local hipEvent_t t_hook_stop[RQ_KERNEL_KINDS] = {};
+
+struct Hook {
+  int kind;
+  hipStream_t stream;
+  bool armed;
+  Hook(int k, hipStream_t s) : kind(k), stream(s), armed(t_hook_start[k] != nullptr) {
+    if (armed) hipEventRecord(t_hook_start[kind], stream);
+  }
+  ~Hook() {
+    if (armed) {
+      hipEventRecord(t_hook_stop[kind], stream);
+      t_hook_start[kind] = nullptr;
+      t_hook_stop[kind] = nullptr;
+    }
+  }
+};
+
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -77,6 +97,14 @@ const char* rq_status_string(int status) {
   }
 }
 
+int rq_time_next_kernel(int kernel, void* start_event, void* stop_event) {
+  if (kernel < 0 || kernel >= RQ_KERNEL_KINDS) return RQ_ERR_ARG;
+  if ((start_event == nullptr) != (stop_event == nullptr)) return RQ_ERR_NULL;
+  t_hook_start[kernel] = (hipEvent_t)start_event;
+  t_hook_stop[kernel] = (hipEvent_t)stop_event;
+  return RQ_OK;
+}
+
 int rq_device_supported(int device) {
   if (device < 0) return -1;
   if (device < kMaxDevices) {
@@ -101,6 +129,7 @@ int rq_fp8_quant_weights(const uint16_t* w, int64_t B, int64_t N, int64_t K, uin
   if (!aligned(w, 16) || !aligned(w_q, 16) || !aligned(w_scale, 4)) return RQ_ERR_ALIGN;
   const int dev = check_device();
   if (dev != RQ_OK) return dev;
+  Hook hook(RQ_KERNEL_QUANT, (hipStream_t)stream);
   hipError_t e = rq::launch_quant_rows(w, rows, K, RQ_ACT_NONE, w_q, w_scale, nullptr, (hipStream_t)stream);
   return e == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
@@ -138,8 +167,11 @@ int rq_fp8_linear(const uint16_t* x, int64_t M, int64_t K, int act, const uint8_
   uint8_t* xq = dq ? dq : c.take<uint8_t>((size_t)(M * K));
   float* sx = ds ? ds : c.take<float>((size_t)M * sizeof(float));
   hipStream_t s = (hipStream_t)stream;
-  if (rq::launch_quant_rows(x, M, K, act, xq, sx, act == RQ_ACT_SILU_MUL ? dh : nullptr, s) != hipSuccess)
-    return RQ_ERR_HIP;
+  {
+    Hook hook(RQ_KERNEL_QUANT, s);
+    if (rq::launch_quant_rows(x, M, K, act, xq, sx, act == RQ_ACT_SILU_MUL ? dh : nullptr, s) != hipSuccess)
+      return RQ_ERR_HIP;
+  }
   rq::GemmArgs g{};
   g.a = xq;
   g.a_scale = sx;
@@ -150,6 +182,7 @@ int rq_fp8_linear(const uint16_t* x, int64_t M, int64_t K, int act, const uint8_
   g.N = N;
   g.K = K;
   g.E = 1;
+  Hook hook(RQ_KERNEL_GEMM, s);
   return rq::launch_gemm_dense(g, s) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 
@@ -210,8 +243,11 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const i
   if (rq::launch_moe_plan(topk_ids, T, top_k, E, rq::grouped_tile_m(), offsets, tile_start, perm, pos,
                           block_hist, s) != hipSuccess)
     return RQ_ERR_HIP;
-  if (rq::launch_quant_rows(x, rows, K, act, aq, as, act == RQ_ACT_SILU_MUL ? dh : nullptr, s) != hipSuccess)
-    return RQ_ERR_HIP;
+  {
+    Hook hook(RQ_KERNEL_QUANT, s);
+    if (rq::launch_quant_rows(x, rows, K, act, aq, as, act == RQ_ACT_SILU_MUL ? dh : nullptr, s) != hipSuccess)
+      return RQ_ERR_HIP;
+  }
   rq::GemmArgs g{};
   g.a = aq;
   g.a_scale = as;
@@ -227,8 +263,12 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const i
   g.top_k = top_k;
   g.E = (int32_t)E;
   g.gather_tokens = in_layout == RQ_MOE_IN_TOKENS ? 1 : 0;
-  if (rq::launch_gemm_grouped(g, s) != hipSuccess) return RQ_ERR_HIP;
+  {
+    Hook hook(RQ_KERNEL_GEMM, s);
+    if (rq::launch_gemm_grouped(g, s) != hipSuccess) return RQ_ERR_HIP;
+  }
   if (out_layout == RQ_MOE_OUT_COMBINED) {
+    Hook hook(RQ_KERNEL_COMBINE, s);
     if (rq::launch_moe_combine(y_perm, pos, topk_w, T, top_k, N, y, s) != hipSuccess) return RQ_ERR_HIP;
   }
   return RQ_OK;

@@ -144,6 +144,16 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act,
                               void* workspace, size_t workspace_bytes,
                               const rq_debug_out* dbg, void* stream);
 
+/* Kernel-level timing for benchmarks and profilers.  After this call, the next kernel
+ * of the given kind that the calling thread enqueues (through any entry point above) is
+ * bracketed by hipEventRecord(start_event) just before its launch and
+ * hipEventRecord(stop_event) just after it, on the stream it is launched on; the hook
+ * then disarms itself.  start_event / stop_event are hipEvent_t handles owned by the
+ * caller; passing NULL for both disarms the hook.  Each kind has its own one-shot slot.
+ * Returns RQ_ERR_ARG for an unknown kind and RQ_ERR_NULL if only one event is NULL. */
+enum { RQ_KERNEL_QUANT = 0, RQ_KERNEL_GEMM = 1, RQ_KERNEL_COMBINE = 2, RQ_KERNEL_KINDS = 3 };
+int rq_time_next_kernel(int kernel, void* start_event, void* stop_event);
+
 /* Static description of a status code ("ok", "null pointer", ...). */
 const char* rq_status_string(int status);
 
