@@ -12,6 +12,8 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int64_t kMaxExperts = 1024;
 constexpr int kMaxDevices = 64;
+constexpr int64_t kMaxOperandBytes = ((int64_t)1 << 31) - 1;  // 32-bit buffer offsets
+constexpr int64_t kMaxK = (int64_t)1 << 22;  // rows just past a tile edge stay out of range
 
 // One-shot per-thread timing hooks (rq_time_next_kernel).
 thread_local hipEvent_t t_hook_start[RQ_KERNEL_KINDS] = {};
@@ -146,7 +148,8 @@ int rq_fp8_linear(const uint16_t* x, int64_t M, int64_t K, int act, const uint8_
   if (act != RQ_ACT_NONE && act != RQ_ACT_SILU_MUL) return RQ_ERR_ARG;
   if (M < 0 || K <= 0 || N <= 0) return RQ_ERR_SHAPE;
   if (K % 16 != 0 || N % 16 != 0) return RQ_ERR_ALIGN;
-  if (K > (int64_t)1 << 30 || N > (int64_t)1 << 30 || M > (int64_t)1 << 31) return RQ_ERR_SHAPE;
+  if (K > kMaxK || N > (int64_t)1 << 30 || M > (int64_t)1 << 31) return RQ_ERR_SHAPE;
+  if (M * K > kMaxOperandBytes || N * K > kMaxOperandBytes) return RQ_ERR_SHAPE;
   if (!w_q || !w_scale) return RQ_ERR_NULL;
   if (M > 0 && (!x || !y)) return RQ_ERR_NULL;
   uint8_t* dq = dbg ? dbg->a_q : nullptr;
@@ -179,6 +182,7 @@ int rq_fp8_linear(const uint16_t* x, int64_t M, int64_t K, int act, const uint8_
   g.b_scale = w_scale;
   g.y = y;
   g.M = M;
+  g.a_rows = M;
   g.N = N;
   g.K = K;
   g.E = 1;
@@ -206,8 +210,9 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const i
   if (T < 0 || K <= 0 || N <= 0 || E < 1 || E > kMaxExperts || top_k < 1 || top_k > E)
     return RQ_ERR_SHAPE;
   if (K % 16 != 0 || N % 16 != 0) return RQ_ERR_ALIGN;
-  if (K > (int64_t)1 << 30 || N > (int64_t)1 << 30 || T * top_k > ((int64_t)1 << 31) - 1)
+  if (K > kMaxK || N > (int64_t)1 << 30 || T * top_k > ((int64_t)1 << 31) - 1)
     return RQ_ERR_SHAPE;
+  if (T * top_k * K > kMaxOperandBytes || N * K > kMaxOperandBytes) return RQ_ERR_SHAPE;
   if (!w_q || !w_scale) return RQ_ERR_NULL;
   if (T > 0 && (!x || !y || !topk_ids)) return RQ_ERR_NULL;
   if (T > 0 && out_layout == RQ_MOE_OUT_COMBINED && !topk_w) return RQ_ERR_ARG;
@@ -255,6 +260,7 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const i
   g.b_scale = w_scale;
   g.y = y_perm;
   g.M = R;
+  g.a_rows = rows;
   g.N = N;
   g.K = K;
   g.offsets = offsets;

@@ -50,6 +50,7 @@ struct GemmArgs {
   const float* b_scale;   // [E][N]
   uint16_t* y;            // [M or R][N] FP16
   int64_t M;              // dense: rows of A and y.  grouped: R (routed rows)
+  int64_t a_rows;         // rows of the A array (dense: M; grouped: T or R)
   int64_t N;
   int64_t K;
   // grouped only

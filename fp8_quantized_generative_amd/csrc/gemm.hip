@@ -9,46 +9,97 @@
 // weights [N][K] in the nn.Linear layout.
 //
 // Design (CDNA4):
-// * Matrix core: v_mfma_f32_16x16x128_f8f6f4 (FP8 x FP8, K = 128 per instruction, the
-//   full-rate FP8 MFMA of gfx950).  Each lane feeds 32 bytes of one A row and 32 bytes of
-//   one B column; the four 16-lane groups take the four 32-byte quarters of the 128-byte
-//   K block.  A and B use the same K assignment, so the dot product is the plain one.
-// * Tiles: 128 x 128 outputs per 256-thread workgroup, 4 wavefronts in a 2 x 2 grid, each
-//   owning 64 x 64 outputs = 4 x 4 MFMA tiles (64 FP32 accumulators per lane).
-// * LDS: A and B K-slabs of 128 x 128 bytes, double-buffered (64 KB).  Rows are 128 bytes;
-//   the 16-byte granule g of row r is stored at granule g ^ (r & 7) ^ ((r >> 3) & 1), so the
-//   16-byte fragment reads of 16 consecutive rows and the 16-byte stores of 8 lanes along a
-//   row both spread over all banks.
-// * Global loads are 16-byte vectors, 8 lanes per 128-byte row segment; the next K-slab is
-//   fetched into registers while the MFMAs consume the current one; one barrier per slab.
+// * Matrix core: v_mfma_f32_32x32x64_f8f6f4 (FP8 x FP8, 32 x 32 outputs, K = 64 per
+//   instruction, full FP8 rate on gfx950).  Lane l feeds 32 bytes of A row (l & 31) and of
+//   B column (l & 31); the two 32-lane halves take the two 32-byte halves of the 64-byte K
+//   slab.  A and B use the same K assignment, so the dot product is the plain one.
+// * Tiles: BM x BN outputs per 256-thread workgroup (256x256, 256x128 or 128x128), four
+//   wavefronts in a 2 x 2 grid, each owning (BM/2) x (BN/2) outputs as 32x32 MFMA tiles.
+// * Pipeline: K advances in 64-byte slabs (BM A rows + BN B rows, 32 KB at 256x256) held
+//   in a ring of four LDS buffers.  Slabs are fetched three ahead of the one being
+//   multiplied with buffer loads that write LDS directly (no registers held for data in
+//   flight), so each wave always has up to three slabs of global loads outstanding; one
+//   vmcnt wait and one barrier per slab.  Measured on MI355X, a single slab of lookahead
+//   left the matrix cores idle about 70% of the time waiting for global loads.
+// * LDS layout: 64-byte rows; the 16-byte granule g of row r sits at granule
+//   g ^ ((r>>1)&1) ^ ((r>>1)&2) ^ ((r>>3)&1), so a fragment read (32 consecutive rows, one
+//   granule) touches every bank once per 8- or 16-lane phase.  Each direct-to-LDS load
+//   fills 16 consecutive rows; lanes fetch the granule that the swizzle puts at their slot.
+//   Rows outside the tile and K past the end read as zero through the buffer range check.
 // * Tile order: the hardware hands consecutive workgroup ids to the 8 XCDs in turn; ids are
 //   remapped so each XCD receives a contiguous range of the logical order, and the logical
 //   order walks groups of 8 M-tiles across all N-tiles, so tiles that share A rows or B
 //   columns run on the same XCD and hit its L2.
-// * Epilogue: per-row and per-column FP32 scales, round to nearest even to FP16.
+// * Epilogue: accumulators are scaled (FP32 per-row and per-column scales), rounded to
+//   FP16, staged through LDS one 32-row strip per wave, and written with 16-byte stores so
+//   each output row segment is one contiguous burst.
 //
 // Grouped (MoE) mode: the M-tiles are the concatenation over experts of
-// ceil(count_e / 128) tiles each (tile_start = exclusive scan, built on the device by the
+// ceil(count_e / BM) tiles each (tile_start = exclusive scan, built on the device by the
 // routing plan).  A workgroup finds its expert by binary search, reads A rows through the
-// permutation (token perm[r] / top_k) when the input is per token, uses expert e's
-// weights and scales, and writes permuted output rows.  Tiles past the device-side total
-// exit at once, so the host never needs the per-expert counts.
-// Ragged edges (M, N not multiples of 128, K not a multiple of 128) are zero-filled in LDS
-// and masked in the epilogue.
+// permutation (token perm[r] / top_k) when the input is per token, uses expert e's weights
+// and scales, and writes permuted output rows.  Tiles past the device-side total exit at
+// once, so the host never needs the per-expert counts.
 
 #include "common.h"
 
 namespace rq {
 namespace {
 
-constexpr int BM = 128;
-constexpr int BN = 128;
-constexpr int BK = 128;
 constexpr int kThreads = 256;
 constexpr int kGroupM = 8;
-constexpr int kLoadsPerThread = BM * BK / 16 / kThreads;  // 16-byte granules per operand
+constexpr int BK = 64;          // K bytes per slab
+constexpr int kStages = 4;      // LDS ring depth; slabs in flight = kStages - 1
+constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset that always reads zero
 
-__device__ __forceinline__ int swz(int row, int g) { return g ^ (row & 7) ^ ((row >> 3) & 1); }
+template <int BM_, int BN_>
+struct Cfg {
+  static constexpr int BM = BM_;
+  static constexpr int BN = BN_;
+  static constexpr int WM = BM / 2;              // wave tile rows
+  static constexpr int WN = BN / 2;              // wave tile columns
+  static constexpr int TI = WM / 32;             // 32x32 MFMA tiles per wave, M direction
+  static constexpr int TJ = WN / 32;             // ... N direction
+  static constexpr int ROWS = BM + BN;           // A rows then B rows in one LDS slab
+  static constexpr int STAGE = ROWS * BK;        // bytes per slab
+  static constexpr int ROWS_PER_WAVE = ROWS / 4;
+  static constexpr int LOADS = ROWS_PER_WAVE / 16;  // direct-to-LDS loads per lane per slab
+  static constexpr int EPI_STRIDE = WN * 2 + 16;    // padded FP16 strip row (bytes)
+  static constexpr int EPI_BYTES = 32 * EPI_STRIDE;
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
+  static_assert(ROWS_PER_WAVE % 16 == 0, "whole 16-row load groups per wave");
+  static_assert(4 * EPI_BYTES <= kStages * STAGE, "epilogue staging fits in the ring");
+};
+
+__device__ __forceinline__ int swz(int row, int g) {
+  return g ^ ((row >> 1) & 1) ^ ((row >> 1) & 2) ^ ((row >> 3) & 1);
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | vmcnt[5:4] << 14,
+// expcnt and lgkmcnt at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// The same, also waiting for all LDS reads (lgkmcnt = 0).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Scheduling pattern: MFMA q followed by its share of the next slab's fragment reads.
+template <int Q, int M, int R>
+__device__ __forceinline__ void interleave_mfma_reads() {
+  if constexpr (Q < M) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    constexpr int n = (Q + 1) * R / M - Q * R / M;
+    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);  // n DS reads
+    interleave_mfma_reads<Q + 1, M, R>();
+  }
+}
 
 struct TileInfo {
   int64_t row_begin;
@@ -57,7 +108,7 @@ struct TileInfo {
   int expert;
 };
 
-template <bool GROUPED>
+template <int BM, bool GROUPED>
 __device__ __forceinline__ bool map_tile(const GemmArgs& p, int m_tiles, int n_tiles, TileInfo& t) {
   const int total = (int)gridDim.x;
   int bid = (int)blockIdx.x;
@@ -95,151 +146,248 @@ __device__ __forceinline__ int64_t a_source_row(const GemmArgs& p, int64_t r) {
   return r;
 }
 
-template <bool GROUPED>
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor: base, stride 0, num_records = bytes (reads at or past it return
+// zero), gfx9 data format word.
+__device__ __forceinline__ v4i make_desc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return (v4i){__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFFu)),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+
+// One 16-byte-per-lane buffer load that writes LDS directly: lane l's 16 bytes land at
+// LDS byte address lds + 16 l.  Written as inline asm so that the compiler does not treat
+// the outstanding LDS writes as aliasing every later LDS read (it would otherwise wait for
+// all loads in flight before each fragment read); completion is tracked with explicit
+// vmcnt waits instead.  The asm has no output registers.
+__device__ __forceinline__ void load_lds_16(const v4i& desc, uint32_t voffset, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds), "v"(voffset), "s"(desc)
+      : "memory", "m0");
+}
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+template <class C, bool GROUPED>
 __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(GemmArgs p, int m_tiles, int n_tiles) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * BK];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * C::STAGE];
   TileInfo t;
-  if (!map_tile<GROUPED>(p, m_tiles, n_tiles, t)) return;
+  if (!map_tile<C::BM, GROUPED>(p, m_tiles, n_tiles, t)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps addressing scalar
   const int64_t K = p.K;
   const int64_t N = p.N;
-  const uint8_t* __restrict__ B = p.b + (int64_t)t.expert * N * K;
+  const int n0 = t.nt * C::BN;
+  const v4i a_desc = make_desc(p.a, (uint32_t)(p.a_rows * K));
+  const v4i b_desc = make_desc(p.b + (int64_t)t.expert * N * K, (uint32_t)(N * K));
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   const float* __restrict__ sb = p.b_scale + (int64_t)t.expert * N;
-  const int n0 = t.nt * BN;
 
-  // ---- global -> LDS assignment: granule (row, g) with g = tid & 7
-  const int g = tid & 7;
-  const uint8_t* a_src[kLoadsPerThread];
-  const uint8_t* b_src[kLoadsPerThread];
-  int lds_off[kLoadsPerThread];
+  // ---- direct-to-LDS loads.  Load t of wave w fills slab rows [row0, row0 + 16) with
+  // row0 = w * ROWS_PER_WAVE + 16 t; lane l writes 16 bytes at row row0 + l / 4, physical
+  // granule l % 4, so it fetches logical granule (l % 4) ^ f(row) of that row.
+  uint32_t src_off[C::LOADS];
+  int gran[C::LOADS];
 #pragma unroll
-  for (int i = 0; i < kLoadsPerThread; ++i) {
-    const int row = (tid >> 3) + 32 * i;
-    const int64_t r = t.row_begin + row;
-    a_src[i] = (r < t.row_end) ? p.a + a_source_row<GROUPED>(p, r) * K + 16 * g : nullptr;
-    const int64_t n = n0 + row;
-    b_src[i] = (n < N) ? B + n * K + 16 * g : nullptr;
-    lds_off[i] = row * BK + 16 * swz(row, g);
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int row0 = wave * C::ROWS_PER_WAVE + 16 * i;
+    const int row = row0 + (lane >> 2);
+    const int g = swz(row, lane & 3);  // XOR swizzle is its own inverse
+    gran[i] = g;
+    if (row0 < C::BM) {
+      const int64_t r = t.row_begin + row;
+      const bool ok = GROUPED ? r < t.row_end : true;  // dense rows past M read zero
+      src_off[i] = ok ? (uint32_t)(a_source_row<GROUPED>(p, r) * K + 16 * g) : kOutOfRange;
+    } else {
+      src_off[i] = (uint32_t)((n0 + (row - C::BM)) * K + 16 * g);  // rows past N read zero
+    }
   }
-
-  uint4 ra[kLoadsPerThread], rb[kLoadsPerThread];
-  auto load_slab = [&](int64_t k0) {
-    const bool kin = (k0 + 16 * g) < K;
-#pragma unroll
-    for (int i = 0; i < kLoadsPerThread; ++i) {
-      ra[i] = (kin && a_src[i]) ? ld_global_16(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
-      rb[i] = (kin && b_src[i]) ? ld_global_16(b_src[i] + k0) : make_uint4(0, 0, 0, 0);
-    }
+  auto issue_one = [&](int slab, int buf, int i) {
+    const uint32_t k0 = (uint32_t)slab * BK;
+    const int row0 = wave * C::ROWS_PER_WAVE + 16 * i;
+    const bool kin = (int64_t)k0 + 16 * gran[i] < K;
+    const uint32_t off = kin ? src_off[i] + k0 : kOutOfRange;
+    load_lds_16(row0 < C::BM ? a_desc : b_desc, off,
+                (uint32_t)__builtin_amdgcn_readfirstlane((int)(smem_lds + buf * C::STAGE + row0 * BK)));
   };
-  auto store_slab = [&](int buf) {
-    uint8_t* As = smem + buf * (BM + BN) * BK;
-    uint8_t* Bs = As + BM * BK;
+  auto issue_slab = [&](int slab, int buf) {
 #pragma unroll
-    for (int i = 0; i < kLoadsPerThread; ++i) {
-      *reinterpret_cast<uint4*>(As + lds_off[i]) = ra[i];
-      *reinterpret_cast<uint4*>(Bs + lds_off[i]) = rb[i];
-    }
+    for (int i = 0; i < C::LOADS; ++i) issue_one(slab, buf, i);
   };
 
-  // ---- MFMA fragment addressing: lane -> (row within 16, K quarter)
+  // ---- MFMA fragment addressing: lane -> (row within 32, K half).  A fragment is two
+  // 16-byte LDS reads (granules 2 half and 2 half + 1 of its row).
   const int wm = wave >> 1;
   const int wn = wave & 1;
-  const int frow = lane & 15;
-  const int quarter = lane >> 4;
-  const int f_off0 = frow * BK + 16 * swz(frow, 2 * quarter);
-  const int f_off1 = frow * BK + 16 * swz(frow, 2 * quarter + 1);
+  const int frow = lane & 31;
+  const int half = lane >> 5;
+  const int f_off[2] = {frow * BK + 16 * swz(frow, 2 * half), frow * BK + 16 * swz(frow, 2 * half + 1)};
+  constexpr int kReads = 2 * (C::TI + C::TJ);   // 16-byte fragment reads per slab
+  constexpr int kMfma = C::TI * C::TJ;
+  // read r of a slab: A fragments first, then B; r / 2 selects the fragment, r % 2 the half
+  auto read_one = [&](const uint8_t* S, int r) -> uint4 {
+    const int f = r >> 1;
+    const int row = f < C::TI ? wm * C::WM + 32 * f : C::BM + wn * C::WN + 32 * (f - C::TI);
+    return *reinterpret_cast<const uint4*>(S + row * BK + f_off[r & 1]);
+  };
 
-  v4f acc[4][4];
+  v16f acc[C::TI][C::TJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < C::TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < C::TJ; ++j) acc[i][j] = (v16f){};
+
+  // Two fragment register sets: the MFMAs of slab kt use one while the reads of slab kt+1
+  // fill the other.
+  uint4 fr0[kReads], fr1[kReads];
+  auto as_v8 = [](const uint4& lo, const uint4& hi) -> v8i {
+    return (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
 
   const int ktiles = (int)((K + BK - 1) / BK);
-  load_slab(0);
-  store_slab(0);
+  // prologue: slabs 0..3 in flight, then slab 0's fragments
+#pragma unroll
+  for (int s = 0; s < kStages; ++s)
+    if (s < ktiles) issue_slab(s, s);
+  if (ktiles >= kStages) wait_vmcnt<(kStages - 1) * C::LOADS>();
+  else if (ktiles == 3) wait_vmcnt<2 * C::LOADS>();
+  else if (ktiles == 2) wait_vmcnt<C::LOADS>();
+  else wait_vmcnt<0>();
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kReads; ++r) fr0[r] = read_one(smem, r);
+
+  // One slab: wait for slab kt+1 and the reads of slab kt, barrier (slab kt's buffer is then
+  // free for slab kt+4), then the MFMAs of slab kt interleaved with the fragment reads of
+  // slab kt+1 and the direct-to-LDS loads of slab kt+4.
+  auto step = [&](int kt, uint4 (&cur)[kReads], uint4 (&nxt)[kReads]) {
+    const int ahead = ktiles - 2 - kt;  // slabs issued after kt+1 that may stay in flight
+    if (ahead >= 2) wait_vmcnt_lgkm0<2 * C::LOADS>();
+    else if (ahead == 1) wait_vmcnt_lgkm0<C::LOADS>();
+    else wait_vmcnt_lgkm0<0>();
+    __syncthreads();
+    const bool has_next = kt + 1 < ktiles;
+    const bool has_load = kt + kStages < ktiles;
+    const uint8_t* Sn = smem + ((kt + 1) % kStages) * C::STAGE;
+    int r = 0, l = 0;
+#pragma unroll
+    for (int q = 0; q < kMfma; ++q) {
+      const int i = q / C::TJ, j = q % C::TJ;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          as_v8(cur[2 * i], cur[2 * i + 1]), as_v8(cur[2 * (C::TI + j)], cur[2 * (C::TI + j) + 1]),
+          acc[i][j], 0, 0, 0, 0, 0, 0);
+      const int r_end = (q + 1) * kReads / kMfma;
+      for (; r < r_end; ++r)
+        if (has_next) nxt[r] = read_one(Sn, r);
+      const int l_end = (q + 1) * C::LOADS / kMfma;
+      for (; l < l_end; ++l)
+        if (has_load) issue_one(kt + kStages, kt % kStages, l);
+    }
+    interleave_mfma_reads<0, kMfma, kReads>();
+  };
+
+  int kt = 0;
+  for (; kt + 1 < ktiles; kt += 2) {
+    step(kt, fr0, fr1);
+    step(kt + 1, fr1, fr0);
+  }
+  if (kt < ktiles) step(kt, fr0, fr1);
   __syncthreads();
 
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < ktiles) load_slab((int64_t)(kt + 1) * BK);
-
-    const uint8_t* As = smem + cur * (BM + BN) * BK + (wm * 64) * BK;
-    const uint8_t* Bs = smem + cur * (BM + BN) * BK + BM * BK + (wn * 64) * BK;
-    v8i af[4], bf[4];
+  // ---- epilogue: one 32-row strip of the wave tile at a time, staged through LDS.
+  // 32x32 MFMA output layout: lane holds column (lane & 31) and, for register r, row
+  // 8 (r / 4) + 4 (lane / 32) + r % 4.  Strip rows are EPI_STRIDE bytes apart (padded so
+  // the two lane halves hit different banks); read back as 16-byte chunks of 8 columns.
+  uint8_t* strip = smem + wave * C::EPI_BYTES;
+  float sbv[C::TJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 lo = *reinterpret_cast<const uint4*>(As + i * 16 * BK + f_off0);
-      const uint4 hi = *reinterpret_cast<const uint4*>(As + i * 16 * BK + f_off1);
-      af[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  for (int j = 0; j < C::TJ; ++j) {
+    const int64_t n = n0 + wn * C::WN + 32 * j + frow;
+    sbv[j] = n < N ? sb[n] : 0.f;
+  }
+  constexpr int kChunksPerRow = C::WN / 8;
+  constexpr int kChunks = 32 * kChunksPerRow;
+#pragma unroll
+  for (int i = 0; i < C::TI; ++i) {
+    const int64_t strip_row0 = t.row_begin + wm * C::WM + 32 * i;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int srow = 8 * (r >> 2) + 4 * half + (r & 3);
+      const int64_t row = strip_row0 + srow;
+      const float sa = row < t.row_end ? p.a_scale[a_source_row<GROUPED>(p, row)] : 0.f;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(strip + srow * C::EPI_STRIDE) + frow;
+#pragma unroll
+      for (int j = 0; j < C::TJ; ++j) dst[32 * j] = (uint16_t)float_to_half_bits((acc[i][j][r] * sa) * sbv[j]);
     }
+    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint4 lo = *reinterpret_cast<const uint4*>(Bs + j * 16 * BK + f_off0);
-      const uint4 hi = *reinterpret_cast<const uint4*>(Bs + j * 16 * BK + f_off1);
-      bf[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    for (int c = lane; c < kChunks; c += 64) {
+      const int srow = c / kChunksPerRow;
+      const int scol = (c % kChunksPerRow) * 8;
+      const int64_t row = strip_row0 + srow;
+      const int64_t col = n0 + wn * C::WN + scol;
+      const uint4 v = *reinterpret_cast<const uint4*>(strip + srow * C::EPI_STRIDE + 2 * scol);
+      if (row < t.row_end && col < N) st_global_16(p.y + row * N + col, v);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], acc[i][j],
-                                                                      0, 0, 0, 0, 0, 0);
-
-    if (kt + 1 < ktiles) store_slab(cur ^ 1);
     __syncthreads();
   }
+}
 
-  // ---- epilogue: lane holds rows 4*quarter + r, column frow of each 16x16 tile
-  float sbv[4];
-  int64_t ncol[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    ncol[j] = n0 + wn * 64 + 16 * j + frow;
-    sbv[j] = ncol[j] < N ? sb[ncol[j]] : 0.f;
+template <class C, bool GROUPED>
+hipError_t launch(const GemmArgs& g, int m_tiles, hipStream_t stream) {
+  const int n_tiles = (int)((g.N + C::BN - 1) / C::BN);
+  gemm_fp8_kernel<C, GROUPED><<<dim3(m_tiles * n_tiles), dim3(kThreads), 0, stream>>>(g, m_tiles, n_tiles);
+  return hipGetLastError();
+}
+
+using Big = Cfg<256, 256>;
+using Wide = Cfg<256, 128>;
+using Small = Cfg<128, 128>;
+
+// Pick the tile for a dense M x N problem: fewest waves of workgroups over the 256 CUs,
+// weighted by the relative cost of one tile of each shape (smaller tiles reuse less).
+int pick_dense(int64_t M, int64_t N) {
+  const int64_t cus = 256;
+  struct Opt { int bm, bn, per_cu; double cost; } opts[] = {
+      {256, 256, 1, 4.0}, {256, 128, 1, 2.3}, {128, 128, 2, 1.4}};
+  int best = 0;
+  double best_t = 1e30;
+  for (int o = 0; o < 3; ++o) {
+    const int64_t tiles = ((M + opts[o].bm - 1) / opts[o].bm) * ((N + opts[o].bn - 1) / opts[o].bn);
+    const int64_t slots = cus * opts[o].per_cu;
+    const double waves = (double)((tiles + slots - 1) / slots);
+    const double t = waves * opts[o].cost * opts[o].per_cu;
+    if (t < best_t - 1e-9) { best_t = t; best = o; }
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = t.row_begin + wm * 64 + 16 * i + 4 * quarter + r;
-      if (row >= t.row_end) continue;
-      const float sa = p.a_scale[a_source_row<GROUPED>(p, row)];
-      uint16_t* yr = p.y + row * N;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (ncol[j] < N) {
-          const float v = (acc[i][j][r] * sa) * sbv[j];
-          yr[ncol[j]] = (uint16_t)float_to_half_bits(v);
-        }
-      }
-    }
-  }
+  return best;
 }
 
 }  // namespace
 
-int grouped_tile_m() { return BM; }
+int grouped_tile_m() { return Big::BM; }
 
-int64_t grouped_max_mtiles(int64_t R, int64_t E) { return (R + BM - 1) / BM + E; }
+int64_t grouped_max_mtiles(int64_t R, int64_t E) { return (R + Big::BM - 1) / Big::BM + E; }
 
 hipError_t launch_gemm_dense(const GemmArgs& g, hipStream_t stream) {
   if (g.M <= 0) return hipSuccess;
-  const int m_tiles = (int)((g.M + BM - 1) / BM);
-  const int n_tiles = (int)((g.N + BN - 1) / BN);
-  gemm_fp8_kernel<false><<<dim3(m_tiles * n_tiles), dim3(kThreads), 0, stream>>>(g, m_tiles, n_tiles);
-  return hipGetLastError();
+  switch (pick_dense(g.M, g.N)) {
+    case 0: return launch<Big, false>(g, (int)((g.M + Big::BM - 1) / Big::BM), stream);
+    case 1: return launch<Wide, false>(g, (int)((g.M + Wide::BM - 1) / Wide::BM), stream);
+    default: return launch<Small, false>(g, (int)((g.M + Small::BM - 1) / Small::BM), stream);
+  }
 }
 
 hipError_t launch_gemm_grouped(const GemmArgs& g, hipStream_t stream) {
   if (g.M <= 0) return hipSuccess;
-  const int m_tiles = (int)grouped_max_mtiles(g.M, g.E);
-  const int n_tiles = (int)((g.N + BN - 1) / BN);
-  gemm_fp8_kernel<true><<<dim3(m_tiles * n_tiles), dim3(kThreads), 0, stream>>>(g, m_tiles, n_tiles);
-  return hipGetLastError();
+  return launch<Big, true>(g, (int)grouped_max_mtiles(g.M, g.E), stream);
 }
 
 }  // namespace rq

@@ -20,6 +20,8 @@
  *   index arrays 4-byte aligned.  Otherwise the call returns RQ_ERR_ALIGN.
  * - K and N must be positive multiples of 16 (RQ_ERR_ALIGN otherwise).  Row counts
  *   (M, T, B) may be 0: the call then validates its arguments and enqueues nothing.
+ * - Size limits (RQ_ERR_SHAPE beyond them): K <= 2^22 for the linears, and every FP8
+ *   operand of one GEMM (activation rows x K, one expert's N x K) below 2^31 bytes.
  * - The caller owns every buffer; the library never allocates device memory.  Scratch
  *   space comes from the caller's workspace, sized by the *_workspace_size calls.
  * - `stream` is a hipStream_t (NULL = the default stream).  All work is enqueued
