@@ -41,6 +41,8 @@
 // and scales, and writes permuted output rows.  Tiles past the device-side total exit at
 // once, so the host never needs the per-expert counts.
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace rq {
@@ -68,7 +70,7 @@ struct Cfg {
   static constexpr int EPI_BYTES = 32 * EPI_STRIDE;
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
   static_assert(ROWS_PER_WAVE % 16 == 0, "whole 16-row load groups per wave");
-  static_assert(4 * EPI_BYTES <= kStages * STAGE, "epilogue staging fits in the ring");
+  static_assert(4 * EPI_BYTES + 4 * (BM + BN) <= kStages * STAGE, "epilogue staging fits in the ring");
 };
 
 __device__ __forceinline__ int swz(int row, int g) {
@@ -90,14 +92,16 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
-// Scheduling pattern: MFMA q followed by its share of the next slab's fragment reads.
-template <int Q, int M, int R>
+// Scheduling pattern: MFMA q followed by its share of the next slab's fragment reads, the
+// R reads spread over the first RM of the M MFMAs.
+template <int Q, int M, int R, int RM>
 __device__ __forceinline__ void interleave_mfma_reads() {
   if constexpr (Q < M) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    constexpr int n = (Q + 1) * R / M - Q * R / M;
-    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);  // n DS reads
-    interleave_mfma_reads<Q + 1, M, R>();
+    constexpr int hi = (Q + 1) * R / RM < R ? (Q + 1) * R / RM : R;
+    constexpr int lo = Q * R / RM < R ? Q * R / RM : R;
+    if constexpr (hi - lo > 0) __builtin_amdgcn_sched_group_barrier(0x100, hi - lo, 0);  // DS reads
+    interleave_mfma_reads<Q + 1, M, R, RM>();
   }
 }
 
@@ -158,18 +162,20 @@ __device__ __forceinline__ v4i make_desc(const void* base, uint32_t bytes) {
 }
 
 // One 16-byte-per-lane buffer load that writes LDS directly: lane l's 16 bytes land at
-// LDS byte address lds + 16 l.  Written as inline asm so that the compiler does not treat
-// the outstanding LDS writes as aliasing every later LDS read (it would otherwise wait for
-// all loads in flight before each fragment read); completion is tracked with explicit
-// vmcnt waits instead.  The asm has no output registers.
-__device__ __forceinline__ void load_lds_16(const v4i& desc, uint32_t voffset, uint32_t lds) {
+// LDS byte address lds_base + lds_imm + 16 l; the global address is base + voffset + soffset.
+// Written as inline asm so that the compiler does not treat the outstanding LDS writes as
+// aliasing every later LDS read (it would otherwise wait for all loads in flight before
+// each fragment read); completion is tracked with explicit vmcnt waits instead.  The asm
+// has no output registers.  One wait state separates the m0 write from the load.
+__device__ __forceinline__ void load_lds_16(const v4i& desc, uint32_t voffset, uint32_t soffset,
+                                            uint32_t lds_base, int lds_imm) {
   asm volatile(
-      "s_mov_b32 m0, %0\n\t"
+      "s_add_u32 m0, %0, %4\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
       :
-      : "s"(lds), "v"(voffset), "s"(desc)
-      : "memory", "m0");
+      : "s"(lds_base), "v"(voffset), "s"(desc), "s"(soffset), "i"(lds_imm)
+      : "memory", "m0", "scc");
 }
 
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -191,17 +197,27 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(GemmArgs p, int m_ti
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   const float* __restrict__ sb = p.b_scale + (int64_t)t.expert * N;
 
+  // Row / column scales for the epilogue: issued before the first direct-to-LDS load, so
+  // they complete before it (vector memory loads return in order) and cost no wait later.
+  float my_sa = 0.f, my_sb = 0.f;
+  if (tid < C::BM) {
+    const int64_t r = t.row_begin + tid;
+    if (r < t.row_end) my_sa = p.a_scale[a_source_row<GROUPED>(p, r)];
+  }
+  if (tid < C::BN && n0 + tid < N) my_sb = sb[n0 + tid];
+
   // ---- direct-to-LDS loads.  Load t of wave w fills slab rows [row0, row0 + 16) with
   // row0 = w * ROWS_PER_WAVE + 16 t; lane l writes 16 bytes at row row0 + l / 4, physical
   // granule l % 4, so it fetches logical granule (l % 4) ^ f(row) of that row.
+  // The swizzle depends only on row bits 1..3, which (lane >> 2) fixes for every load, so
+  // each lane fetches the same granule in all of its loads.
+  const int gran = swz(lane >> 2, lane & 3);  // XOR swizzle is its own inverse
   uint32_t src_off[C::LOADS];
-  int gran[C::LOADS];
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i) {
     const int row0 = wave * C::ROWS_PER_WAVE + 16 * i;
     const int row = row0 + (lane >> 2);
-    const int g = swz(row, lane & 3);  // XOR swizzle is its own inverse
-    gran[i] = g;
+    const int g = gran;
     if (row0 < C::BM) {
       const int64_t r = t.row_begin + row;
       const bool ok = GROUPED ? r < t.row_end : true;  // dense rows past M read zero
@@ -210,13 +226,24 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(GemmArgs p, int m_ti
       src_off[i] = (uint32_t)((n0 + (row - C::BM)) * K + 16 * g);  // rows past N read zero
     }
   }
+  // Wave-uniform LDS byte address of this wave's first 16-row group in ring buffer `buf`.
+  auto wave_lds = [&](int buf) -> uint32_t {
+    return (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(smem_lds + buf * C::STAGE + wave * C::ROWS_PER_WAVE * BK));
+  };
+  // Full slab (all 64 K bytes in range): the K offset travels in the scalar soffset.
+  auto issue_full = [&](int slab, uint32_t lds, int i) {
+    const int row0 = wave * C::ROWS_PER_WAVE + 16 * i;
+    load_lds_16(row0 < C::BM ? a_desc : b_desc, src_off[i], (uint32_t)__builtin_amdgcn_readfirstlane(slab * BK),
+                lds, 16 * BK * i);
+  };
+  // Any slab, including the ragged last one: granules past K read zero.
   auto issue_one = [&](int slab, int buf, int i) {
     const uint32_t k0 = (uint32_t)slab * BK;
     const int row0 = wave * C::ROWS_PER_WAVE + 16 * i;
-    const bool kin = (int64_t)k0 + 16 * gran[i] < K;
+    const bool kin = (int64_t)k0 + 16 * gran < K;
     const uint32_t off = kin ? src_off[i] + k0 : kOutOfRange;
-    load_lds_16(row0 < C::BM ? a_desc : b_desc, off,
-                (uint32_t)__builtin_amdgcn_readfirstlane((int)(smem_lds + buf * C::STAGE + row0 * BK)));
+    load_lds_16(row0 < C::BM ? a_desc : b_desc, off, 0u, wave_lds(buf), 16 * BK * i);
   };
   auto issue_slab = [&](int slab, int buf) {
 #pragma unroll
@@ -232,6 +259,9 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(GemmArgs p, int m_ti
   const int f_off[2] = {frow * BK + 16 * swz(frow, 2 * half), frow * BK + 16 * swz(frow, 2 * half + 1)};
   constexpr int kReads = 2 * (C::TI + C::TJ);   // 16-byte fragment reads per slab
   constexpr int kMfma = C::TI * C::TJ;
+  // The next slab's fragment reads go out during the first half of the MFMAs, so they have
+  // landed by the lgkmcnt wait that precedes the next barrier.
+  constexpr int kReadMfmas = kMfma / 2 > 0 ? kMfma / 2 : 1;
   // read r of a slab: A fragments first, then B; r / 2 selects the fragment, r % 2 the half
   auto read_one = [&](const uint8_t* S, int r) -> uint4 {
     const int f = r >> 1;
@@ -267,16 +297,26 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(GemmArgs p, int m_ti
 
   // One slab: wait for slab kt+1 and the reads of slab kt, barrier (slab kt's buffer is then
   // free for slab kt+4), then the MFMAs of slab kt interleaved with the fragment reads of
-  // slab kt+1 and the direct-to-LDS loads of slab kt+4.
-  auto step = [&](int kt, uint4 (&cur)[kReads], uint4 (&nxt)[kReads]) {
-    const int ahead = ktiles - 2 - kt;  // slabs issued after kt+1 that may stay in flight
-    if (ahead >= 2) wait_vmcnt_lgkm0<2 * C::LOADS>();
-    else if (ahead == 1) wait_vmcnt_lgkm0<C::LOADS>();
-    else wait_vmcnt_lgkm0<0>();
+  // slab kt+1 and the direct-to-LDS loads of slab kt+4.  A single wave can issue only about
+  // a dozen other instructions in the shadow of one 32x32x64 MFMA, so the steady-state step
+  // (every slab involved complete and in range) carries no run-time conditions and no
+  // vector address arithmetic; the generic step handles the last slabs and a ragged K.
+  auto step = [&](auto steady, int kt, uint4 (&cur)[kReads], uint4 (&nxt)[kReads]) {
+    constexpr bool kSteady = decltype(steady)::value;
+    bool has_next = true, has_load = true;
+    if constexpr (kSteady) {
+      wait_vmcnt_lgkm0<2 * C::LOADS>();
+    } else {
+      const int ahead = ktiles - 2 - kt;  // slabs issued after kt+1 that may stay in flight
+      if (ahead >= 2) wait_vmcnt_lgkm0<2 * C::LOADS>();
+      else if (ahead == 1) wait_vmcnt_lgkm0<C::LOADS>();
+      else wait_vmcnt_lgkm0<0>();
+      has_next = kt + 1 < ktiles;
+      has_load = kt + kStages < ktiles;
+    }
     __syncthreads();
-    const bool has_next = kt + 1 < ktiles;
-    const bool has_load = kt + kStages < ktiles;
     const uint8_t* Sn = smem + ((kt + 1) % kStages) * C::STAGE;
+    const uint32_t lds_dst = wave_lds(kt % kStages);
     int r = 0, l = 0;
 #pragma unroll
     for (int q = 0; q < kMfma; ++q) {
@@ -284,35 +324,47 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(GemmArgs p, int m_ti
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
           as_v8(cur[2 * i], cur[2 * i + 1]), as_v8(cur[2 * (C::TI + j)], cur[2 * (C::TI + j) + 1]),
           acc[i][j], 0, 0, 0, 0, 0, 0);
-      const int r_end = (q + 1) * kReads / kMfma;
+      const int r_end = (q + 1) * kReads / kReadMfmas < kReads ? (q + 1) * kReads / kReadMfmas : kReads;
       for (; r < r_end; ++r)
-        if (has_next) nxt[r] = read_one(Sn, r);
+        if (kSteady || has_next) nxt[r] = read_one(Sn, r);
       const int l_end = (q + 1) * C::LOADS / kMfma;
-      for (; l < l_end; ++l)
-        if (has_load) issue_one(kt + kStages, kt % kStages, l);
+      for (; l < l_end; ++l) {
+        if constexpr (kSteady) issue_full(kt + kStages, lds_dst, l);
+        else if (has_load) issue_one(kt + kStages, kt % kStages, l);
+      }
     }
-    interleave_mfma_reads<0, kMfma, kReads>();
+    interleave_mfma_reads<0, kMfma, kReads, kReadMfmas>();
   };
 
+  using Steady = std::integral_constant<bool, true>;
+  using Generic = std::integral_constant<bool, false>;
+  const int full_slabs = (int)(K / BK);
   int kt = 0;
-  for (; kt + 1 < ktiles; kt += 2) {
-    step(kt, fr0, fr1);
-    step(kt + 1, fr1, fr0);
+  for (; kt + 1 + kStages < full_slabs; kt += 2) {  // kt and kt+1 steady: kt+1+4 < full_slabs
+    step(Steady{}, kt, fr0, fr1);
+    step(Steady{}, kt + 1, fr1, fr0);
   }
-  if (kt < ktiles) step(kt, fr0, fr1);
+  for (; kt + 1 < ktiles; kt += 2) {
+    step(Generic{}, kt, fr0, fr1);
+    step(Generic{}, kt + 1, fr1, fr0);
+  }
+  if (kt < ktiles) step(Generic{}, kt, fr0, fr1);
   __syncthreads();
 
   // ---- epilogue: one 32-row strip of the wave tile at a time, staged through LDS.
   // 32x32 MFMA output layout: lane holds column (lane & 31) and, for register r, row
   // 8 (r / 4) + 4 (lane / 32) + r % 4.  Strip rows are EPI_STRIDE bytes apart (padded so
   // the two lane halves hit different banks); read back as 16-byte chunks of 8 columns.
+  // The row and column scales, loaded into registers at kernel start, go to LDS first.
   uint8_t* strip = smem + wave * C::EPI_BYTES;
+  float* s_sa = reinterpret_cast<float*>(smem + 4 * C::EPI_BYTES);
+  float* s_sb = s_sa + C::BM;
+  if (tid < C::BM) s_sa[tid] = my_sa;
+  if (tid < C::BN) s_sb[tid] = my_sb;
+  __syncthreads();
   float sbv[C::TJ];
 #pragma unroll
-  for (int j = 0; j < C::TJ; ++j) {
-    const int64_t n = n0 + wn * C::WN + 32 * j + frow;
-    sbv[j] = n < N ? sb[n] : 0.f;
-  }
+  for (int j = 0; j < C::TJ; ++j) sbv[j] = s_sb[wn * C::WN + 32 * j + frow];
   constexpr int kChunksPerRow = C::WN / 8;
   constexpr int kChunks = 32 * kChunksPerRow;
 #pragma unroll
@@ -321,8 +373,7 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(GemmArgs p, int m_ti
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int srow = 8 * (r >> 2) + 4 * half + (r & 3);
-      const int64_t row = strip_row0 + srow;
-      const float sa = row < t.row_end ? p.a_scale[a_source_row<GROUPED>(p, row)] : 0.f;
+      const float sa = s_sa[wm * C::WM + 32 * i + srow];
       uint16_t* dst = reinterpret_cast<uint16_t*>(strip + srow * C::EPI_STRIDE) + frow;
 #pragma unroll
       for (int j = 0; j < C::TJ; ++j) dst[32 * j] = (uint16_t)float_to_half_bits((acc[i][j][r] * sa) * sbv[j]);
