@@ -62,7 +62,7 @@ struct Carve {
 };
 
 struct MoeLayout {
-  size_t a_q, a_scale, offsets, tile_start, perm, pos, block_hist, y_perm;
+  size_t a_q, a_scale, offsets, tile_start, tile_table, perm, pos, block_hist, y_perm;
 };
 
 MoeLayout moe_layout(int64_t T, int top_k, int64_t E, int64_t N, int64_t K, int in_layout,
@@ -74,6 +74,7 @@ MoeLayout moe_layout(int64_t T, int top_k, int64_t E, int64_t N, int64_t K, int 
   l.a_scale = (size_t)rows * sizeof(float);
   l.offsets = (size_t)(E + 1) * sizeof(int32_t);
   l.tile_start = (size_t)(E + 1) * sizeof(int32_t);
+  l.tile_table = (size_t)rq::grouped_max_mtiles(R, E) * 4 * sizeof(int32_t);
   l.perm = (size_t)R * sizeof(int32_t);
   l.pos = (size_t)R * sizeof(int32_t);
   l.block_hist = (size_t)(rq::moe_plan_blocks(R) * E) * sizeof(int32_t);
@@ -196,7 +197,7 @@ size_t rq_fp8_moe_workspace_size(int64_t T, int top_k, int64_t E, int64_t N, int
   if (T < 0 || top_k < 1 || E < 1 || N <= 0 || K <= 0) return 0;
   const MoeLayout l = moe_layout(T, top_k, E, N, K, in_layout, out_layout);
   return align_up(l.a_q) + align_up(l.a_scale) + align_up(l.offsets) + align_up(l.tile_start) +
-         align_up(l.perm) + align_up(l.pos) + align_up(l.block_hist) + align_up(l.y_perm);
+         align_up(l.tile_table) + align_up(l.perm) + align_up(l.pos) + align_up(l.block_hist) + align_up(l.y_perm);
 }
 
 int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const int32_t* topk_ids,
@@ -237,6 +238,7 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const i
   float* as = c.take<float>(l.a_scale);
   int32_t* offsets = c.take<int32_t>(l.offsets);
   int32_t* tile_start = c.take<int32_t>(l.tile_start);
+  int32_t* tile_table = c.take<int32_t>(l.tile_table);
   int32_t* perm = c.take<int32_t>(l.perm);
   int32_t* pos = c.take<int32_t>(l.pos);
   int32_t* block_hist = c.take<int32_t>(l.block_hist);
@@ -245,8 +247,8 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const i
   if (ds) as = ds;
 
   hipStream_t s = (hipStream_t)stream;
-  if (rq::launch_moe_plan(topk_ids, T, top_k, E, rq::grouped_tile_m(), offsets, tile_start, perm, pos,
-                          block_hist, s) != hipSuccess)
+  if (rq::launch_moe_plan(topk_ids, T, top_k, E, rq::grouped_tile_m(), offsets, tile_start, tile_table,
+                          perm, pos, block_hist, s) != hipSuccess)
     return RQ_ERR_HIP;
   {
     Hook hook(RQ_KERNEL_QUANT, s);
@@ -265,6 +267,7 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const i
   g.K = K;
   g.offsets = offsets;
   g.tile_start = tile_start;
+  g.tile_table = tile_table;
   g.perm = perm;
   g.top_k = top_k;
   g.E = (int32_t)E;

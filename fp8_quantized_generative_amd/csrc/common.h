@@ -55,7 +55,8 @@ struct GemmArgs {
   int64_t K;
   // grouped only
   const int32_t* offsets;     // [E+1] permuted row offsets per expert
-  const int32_t* tile_start;  // [E+1] first m-tile of each expert (exclusive scan)
+  const int32_t* tile_start;  // [E+1] first m-tile of each expert (exclusive scan); [E] = total
+  const int32_t* tile_table;  // [m-tiles][4] {expert, first row, end row, 0}
   const int32_t* perm;        // [R] slot of each permuted row (TOKENS input only)
   int32_t top_k;              // token of permuted row r = perm[r] / top_k (TOKENS input)
   int32_t E;
@@ -68,8 +69,8 @@ int64_t grouped_max_mtiles(int64_t R, int64_t E);
 int grouped_tile_m();
 
 hipError_t launch_moe_plan(const int32_t* ids, int64_t T, int top_k, int64_t E, int tile_m,
-                           int32_t* offsets, int32_t* tile_start, int32_t* perm, int32_t* pos,
-                           int32_t* block_hist, hipStream_t stream);
+                           int32_t* offsets, int32_t* tile_start, int32_t* tile_table, int32_t* perm,
+                           int32_t* pos, int32_t* block_hist, hipStream_t stream);
 int64_t moe_plan_blocks(int64_t R);
 
 hipError_t launch_moe_combine(const uint16_t* y_perm, const int32_t* pos, const uint16_t* topk_w,

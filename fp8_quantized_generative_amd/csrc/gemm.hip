@@ -35,8 +35,8 @@
 //   each output row segment is one contiguous burst.
 //
 // Grouped (MoE) mode: the M-tiles are the concatenation over experts of
-// ceil(count_e / BM) tiles each (tile_start = exclusive scan, built on the device by the
-// routing plan).  A workgroup finds its expert by binary search, reads A rows through the
+// ceil(count_e / BM) tiles each, listed by the routing plan on the device in a table of
+// {expert, first row, end row}.  A workgroup reads its entry with one load, reads A rows through the
 // permutation (token perm[r] / top_k) when the input is per token, uses expert e's weights
 // and scales, and writes permuted output rows.  Tiles past the device-side total exit at
 // once, so the host never needs the per-expert counts.
@@ -114,9 +114,23 @@ struct TileInfo {
 
 template <int BM, bool GROUPED>
 __device__ __forceinline__ bool map_tile(const GemmArgs& p, int m_tiles, int n_tiles, TileInfo& t) {
-  const int total = (int)gridDim.x;
+  // Workgroup ids go round-robin over the 8 XCDs.  Give each XCD a contiguous slice of the
+  // logical tile order (neighbouring tiles share operands in that XCD's L2).  In grouped
+  // mode the grid is sized for the worst case, so the slices cover only the real tiles
+  // (known on the device) and the surplus workgroups of every XCD exit.
+  int total = (int)gridDim.x;
+  if (GROUPED) {
+    m_tiles = p.tile_start[p.E];  // real M-tiles; the grid covers the worst case
+    total = m_tiles * n_tiles;
+  }
   int bid = (int)blockIdx.x;
-  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+  if ((gridDim.x & 7) == 0) {
+    const int per_xcd = (total + 7) >> 3;
+    bid = (bid & 7) * per_xcd + (bid >> 3);
+    if (bid >= total || (int)(blockIdx.x >> 3) >= per_xcd) return false;
+  } else if (bid >= total) {
+    return false;
+  }
   const int per_group = kGroupM * n_tiles;
   const int group = bid / per_group;
   const int first_m = group * kGroupM;
@@ -125,17 +139,10 @@ __device__ __forceinline__ bool map_tile(const GemmArgs& p, int m_tiles, int n_t
   const int mt = first_m + in_group % gm;
   t.nt = in_group / gm;
   if (GROUPED) {
-    const int real_tiles = p.tile_start[p.E];
-    if (mt >= real_tiles) return false;
-    int lo = 0, hi = p.E - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.tile_start[mid] <= mt) lo = mid; else hi = mid - 1;
-    }
-    t.expert = lo;
-    t.row_begin = (int64_t)p.offsets[lo] + (int64_t)(mt - p.tile_start[lo]) * BM;
-    const int64_t end = p.offsets[lo + 1];
-    t.row_end = t.row_begin + BM < end ? t.row_begin + BM : end;
+    const int4 ent = *reinterpret_cast<const int4*>(p.tile_table + 4 * (int64_t)mt);
+    t.expert = ent.x;
+    t.row_begin = ent.y;
+    t.row_end = ent.z;
   } else {
     t.expert = 0;
     t.row_begin = (int64_t)mt * BM;

@@ -10,8 +10,8 @@
 //   1. plan_hist:    per block of 1024 slots, a histogram over experts (LDS atomics on
 //                    integer counts, so the result is deterministic);
 //   2. plan_scan:    one workgroup turns the block histograms into per-expert offsets,
-//                    per-(block, expert) base rows and the per-expert M-tile prefix sum
-//                    that the grouped GEMM schedules from;
+//                    per-(block, expert) base rows, the per-expert M-tile prefix sum and
+//                    the M-tile table {expert, first row, end row} the grouped GEMM reads;
 //   3. plan_scatter: each slot's rank among equal experts inside its wavefront comes from
 //                    ballots over the bits of the expert id; ranks across the block's 16
 //                    wavefronts come from an LDS prefix; perm[row] = j and pos[j] = row.
@@ -73,7 +73,8 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_sums, int& 
 
 __global__ __launch_bounds__(kPlanThreads) void plan_scan(int32_t* __restrict__ block_hist, int nblocks, int E,
                                                           int tile_m, int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ tile_start) {
+                                                          int32_t* __restrict__ tile_start,
+                                                          int32_t* __restrict__ tile_table) {
   __shared__ int wave_sums[kPlanWaves + 1];
   const int e = threadIdx.x;  // E <= 1024
   int count = 0;
@@ -87,6 +88,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_scan(int32_t* __restrict__ 
   if (e < E) {
     offsets[e] = off;
     tile_start[e] = tstart;
+    // one {expert, first row, end row} entry per M-tile, so a GEMM workgroup finds its
+    // tile with a single load
+    for (int t = 0; t < tiles; ++t) {
+      int32_t* ent = tile_table + 4 * (int64_t)(tstart + t);
+      const int lo = off + t * tile_m;
+      ent[0] = e;
+      ent[1] = lo;
+      ent[2] = lo + tile_m < off + count ? lo + tile_m : off + count;
+      ent[3] = 0;
+    }
     int run = off;
     for (int b = 0; b < nblocks; ++b) {
       const int c = block_hist[(int64_t)b * E + e];
@@ -169,8 +180,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 int64_t moe_plan_blocks(int64_t R) { return (R + kPlanThreads - 1) / kPlanThreads; }
 
 hipError_t launch_moe_plan(const int32_t* ids, int64_t T, int top_k, int64_t E, int tile_m,
-                           int32_t* offsets, int32_t* tile_start, int32_t* perm, int32_t* pos,
-                           int32_t* block_hist, hipStream_t stream) {
+                           int32_t* offsets, int32_t* tile_start, int32_t* tile_table, int32_t* perm,
+                           int32_t* pos, int32_t* block_hist, hipStream_t stream) {
   const int64_t R = T * top_k;
   const int nb = (int)moe_plan_blocks(R);
   const int e = (int)E;
@@ -181,7 +192,8 @@ hipError_t launch_moe_plan(const int32_t* ids, int64_t T, int top_k, int64_t E, 
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  plan_scan<<<dim3(1), dim3(kPlanThreads), 0, stream>>>(block_hist, nb, e, tile_m, offsets, tile_start);
+  plan_scan<<<dim3(1), dim3(kPlanThreads), 0, stream>>>(block_hist, nb, e, tile_m, offsets, tile_start,
+                                                        tile_table);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nb == 0) return err;
   plan_scatter<<<dim3(nb), dim3(kPlanThreads), kPlanWaves * e * sizeof(int32_t), stream>>>(
