@@ -194,6 +194,11 @@ __device__ __forceinline__ v4i make_desc(const void* base, uint32_t bytes) {
 // aliasing every later LDS read (it would otherwise wait for all loads in flight before
 // each fragment read); completion is tracked with explicit vmcnt waits instead.  The asm
 // has no output registers.  One wait state separates the m0 write from the load.
+// m0 is a reserved register, so clang warns about it in a clobber list: the clobber is only
+// safe while no compiler-generated code in this file relies on m0, which a host-side ISA test
+// (tests/test_kernel_isa.py) checks on every build.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void load_lds_16(const v4i& desc, uint32_t voffset, uint32_t soffset,
                                             uint32_t lds_base, int lds_imm) {
   asm volatile(
@@ -204,6 +209,7 @@ __device__ __forceinline__ void load_lds_16(const v4i& desc, uint32_t voffset, u
       : "s"(lds_base), "v"(voffset), "s"(desc), "s"(soffset), "i"(lds_imm)
       : "memory", "m0", "scc");
 }
+#pragma clang diagnostic pop
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
