@@ -24,11 +24,11 @@ struct Hook {
   hipStream_t stream;
   bool armed;
   Hook(int k, hipStream_t s) : kind(k), stream(s), armed(t_hook_start[k] != nullptr) {
-    if (armed) hipEventRecord(t_hook_start[kind], stream);
+    if (armed) (void)hipEventRecord(t_hook_start[kind], stream);
   }
   ~Hook() {
     if (armed) {
-      hipEventRecord(t_hook_stop[kind], stream);
+      (void)hipEventRecord(t_hook_stop[kind], stream);
       t_hook_start[kind] = nullptr;
       t_hook_stop[kind] = nullptr;
     }
@@ -74,7 +74,7 @@ MoeLayout moe_layout(int64_t T, int top_k, int64_t E, int64_t N, int64_t K, int 
   l.a_scale = (size_t)rows * sizeof(float);
   l.offsets = (size_t)(E + 1) * sizeof(int32_t);
   l.tile_start = (size_t)(E + 1) * sizeof(int32_t);
-  l.tile_table = (size_t)rq::grouped_max_mtiles(R, E) * 4 * sizeof(int32_t);
+  l.tile_table = (size_t)rq::grouped_max_mtiles(R, E, rq::tile_rows(rq::pick_grouped(R, E))) * 4 * sizeof(int32_t);
   l.perm = (size_t)R * sizeof(int32_t);
   l.pos = (size_t)R * sizeof(int32_t);
   l.block_hist = (size_t)(rq::moe_plan_blocks(R) * E) * sizeof(int32_t);
@@ -247,7 +247,8 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const i
   if (ds) as = ds;
 
   hipStream_t s = (hipStream_t)stream;
-  if (rq::launch_moe_plan(topk_ids, T, top_k, E, rq::grouped_tile_m(), offsets, tile_start, tile_table,
+  const int kind = rq::pick_grouped(R, E);
+  if (rq::launch_moe_plan(topk_ids, T, top_k, E, rq::tile_rows(kind), offsets, tile_start, tile_table,
                           perm, pos, block_hist, s) != hipSuccess)
     return RQ_ERR_HIP;
   {
@@ -274,7 +275,7 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const i
   g.gather_tokens = in_layout == RQ_MOE_IN_TOKENS ? 1 : 0;
   {
     Hook hook(RQ_KERNEL_GEMM, s);
-    if (rq::launch_gemm_grouped(g, s) != hipSuccess) return RQ_ERR_HIP;
+    if (rq::launch_gemm_grouped(g, kind, s) != hipSuccess) return RQ_ERR_HIP;
   }
   if (out_layout == RQ_MOE_OUT_COMBINED) {
     Hook hook(RQ_KERNEL_COMBINE, s);

@@ -63,10 +63,14 @@ struct GemmArgs {
   int32_t gather_tokens;      // 1: A row of permuted row r is perm[r] / top_k
 };
 
+// GEMM tile shapes (rows x columns of output per workgroup).
+enum { kTileBig = 0, kTileWide, kTileSmall, kTileThin, kTileThinWide, kTileKinds };
+
 hipError_t launch_gemm_dense(const GemmArgs& g, hipStream_t stream);
-hipError_t launch_gemm_grouped(const GemmArgs& g, hipStream_t stream);
-int64_t grouped_max_mtiles(int64_t R, int64_t E);
-int grouped_tile_m();
+hipError_t launch_gemm_grouped(const GemmArgs& g, int kind, hipStream_t stream);
+int pick_grouped(int64_t R, int64_t E);        // tile shape for R routed rows over E experts
+int tile_rows(int kind);                       // M rows of a tile shape
+int64_t grouped_max_mtiles(int64_t R, int64_t E, int tile_m);
 
 hipError_t launch_moe_plan(const int32_t* ids, int64_t T, int top_k, int64_t E, int tile_m,
                            int32_t* offsets, int32_t* tile_start, int32_t* tile_table, int32_t* perm,

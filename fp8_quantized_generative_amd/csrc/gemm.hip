@@ -40,6 +40,8 @@
 // and scales, and writes permuted output rows.  Tiles past the device-side total exit at
 // once, so the host never needs the per-expert counts.
 
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "common.h"
@@ -429,47 +431,80 @@ hipError_t launch(const GemmArgs& g, int m_tiles, hipStream_t stream) {
 // Eight wavefronts (two per SIMD) for the large tiles: while one wavefront of a SIMD waits
 // on a load issue, an LDS read or the barrier, the other keeps the matrix core busy.
 // Measured on MI355X: +8% (256x256) and +5% (256x128) over four wavefronts of twice the
-// tile each.
-using Big = Cfg<256, 256, 4, 2, 4>;    // 128 KB ring, 128x64 per wavefront
-using Wide = Cfg<256, 128, 4, 4, 2>;   // 96 KB ring, 64x64 per wavefront
-using Small = Cfg<128, 128, 4, 2, 2>;  // 64 KB ring, two workgroups per CU
+// tile each.  The 64-row tiles serve small M (the weight-streaming regime) and MoE experts
+// with few rows, where 256-row tiles would spend most MFMA work on padding.
+using Big = Cfg<256, 256, 4, 2, 4>;      // 128 KB ring, 128x64 per wavefront
+using Wide = Cfg<256, 128, 4, 4, 2>;     // 96 KB ring, 64x64 per wavefront
+using Small = Cfg<128, 128, 4, 2, 2>;    // 64 KB ring, two workgroups per CU
+using Thin = Cfg<64, 128, 4, 1, 4>;      // 48 KB ring, three workgroups per CU
+using ThinWide = Cfg<64, 256, 4, 1, 4>;  // 80 KB ring, two workgroups per CU
 
-// Pick the tile for a dense M x N problem: fewest waves of workgroups over the 256 CUs,
-// weighted by the relative cost of one tile of each shape (smaller tiles reuse less).
+struct TileDesc {
+  const char* name;
+  int bm, bn;
+};
+const TileDesc kTiles[kTileKinds] = {
+    {"256x256", 256, 256}, {"256x128", 256, 128}, {"128x128", 128, 128}, {"64x128", 64, 128}, {"64x256", 64, 256},
+};
+
+int tile_override() {
+  const char* e = std::getenv("RQ_GEMM_TILE");
+  if (e == nullptr) return -1;
+  for (int k = 0; k < kTileKinds; ++k)
+    if (std::strcmp(e, kTiles[k].name) == 0) return k;
+  return -1;
+}
+
+// Pick the tile for a dense M x N problem: the largest tile (most operand reuse per byte
+// loaded) that still yields enough workgroups to occupy the 256 CUs, else the thinnest.
+// On MI355X this rule picks the fastest shape for every linear of the workloads (measured
+// over all five shapes at M = 512 and M = 4096).
 int pick_dense(int64_t M, int64_t N) {
-  const int64_t cus = 256;
-  struct Opt { int bm, bn, per_cu; double cost; } opts[] = {
-      {256, 256, 1, 4.0}, {256, 128, 1, 2.3}, {128, 128, 2, 1.4}};
-  int best = 0;
-  double best_t = 1e30;
-  for (int o = 0; o < 3; ++o) {
-    const int64_t tiles = ((M + opts[o].bm - 1) / opts[o].bm) * ((N + opts[o].bn - 1) / opts[o].bn);
-    const int64_t slots = cus * opts[o].per_cu;
-    const double waves = (double)((tiles + slots - 1) / slots);
-    const double t = waves * opts[o].cost * opts[o].per_cu;
-    if (t < best_t - 1e-9) { best_t = t; best = o; }
+  const int forced = tile_override();
+  if (forced >= 0) return forced;
+  const int order[] = {kTileBig, kTileWide, kTileSmall, kTileThin};
+  for (int o : order) {
+    const TileDesc& d = kTiles[o];
+    const int64_t tiles = ((M + d.bm - 1) / d.bm) * ((N + d.bn - 1) / d.bn);
+    if (tiles >= 192) return o;
   }
-  return best;
+  return kTileThin;
+}
+
+template <class C>
+hipError_t launch_dense(const GemmArgs& g, hipStream_t stream) {
+  return launch<C, false>(g, (int)((g.M + C::BM - 1) / C::BM), stream);
 }
 
 }  // namespace
 
-int grouped_tile_m() { return Big::BM; }
+int pick_grouped(int64_t R, int64_t E) {
+  const int forced = tile_override();
+  if (forced == kTileBig || forced == kTileThinWide) return forced;
+  // experts average R / E rows: 64-row tiles once 256-row tiles would be mostly padding
+  return R >= 192 * E ? kTileBig : kTileThinWide;
+}
 
-int64_t grouped_max_mtiles(int64_t R, int64_t E) { return (R + Big::BM - 1) / Big::BM + E; }
+int tile_rows(int kind) { return kTiles[kind].bm; }
+
+int64_t grouped_max_mtiles(int64_t R, int64_t E, int tile_m) { return (R + tile_m - 1) / tile_m + E; }
 
 hipError_t launch_gemm_dense(const GemmArgs& g, hipStream_t stream) {
   if (g.M <= 0) return hipSuccess;
   switch (pick_dense(g.M, g.N)) {
-    case 0: return launch<Big, false>(g, (int)((g.M + Big::BM - 1) / Big::BM), stream);
-    case 1: return launch<Wide, false>(g, (int)((g.M + Wide::BM - 1) / Wide::BM), stream);
-    default: return launch<Small, false>(g, (int)((g.M + Small::BM - 1) / Small::BM), stream);
+    case kTileBig: return launch_dense<Big>(g, stream);
+    case kTileWide: return launch_dense<Wide>(g, stream);
+    case kTileSmall: return launch_dense<Small>(g, stream);
+    case kTileThin: return launch_dense<Thin>(g, stream);
+    default: return launch_dense<ThinWide>(g, stream);
   }
 }
 
-hipError_t launch_gemm_grouped(const GemmArgs& g, hipStream_t stream) {
+hipError_t launch_gemm_grouped(const GemmArgs& g, int kind, hipStream_t stream) {
   if (g.M <= 0) return hipSuccess;
-  return launch<Big, true>(g, (int)grouped_max_mtiles(g.M, g.E), stream);
+  if (kind == kTileThinWide)
+    return launch<ThinWide, true>(g, (int)grouped_max_mtiles(g.M, g.E, ThinWide::BM), stream);
+  return launch<Big, true>(g, (int)grouped_max_mtiles(g.M, g.E, Big::BM), stream);
 }
 
 }  // namespace rq

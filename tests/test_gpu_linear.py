@@ -144,3 +144,14 @@ def test_determinism():
     a = host(rq.linear(x, w_q, w_s))
     b = host(rq.linear(x, w_q, w_s))
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+@pytest.mark.parametrize("tile", ["256x256", "256x128", "128x128", "64x128", "64x256"])
+@pytest.mark.parametrize("m,n,k", [(130, 272, 528), (257, 144, 192), (64, 512, 512), (300, 384, 2048)])
+def test_every_tile_shape(monkeypatch, tile, m, n, k):
+    case("linear tile=%s m=%d n=%d k=%d" % (tile, m, n, k))
+    monkeypatch.setenv("RQ_GEMM_TILE", tile)
+    rng = np.random.default_rng(m + 3 * n + 7 * k)
+    x = workloads.acts_channel_lognormal(rng, m, k)
+    w = workloads.weights(rng, (n, k))
+    _check(x, w)

@@ -127,3 +127,13 @@ def test_moe_full_size_sampled():
     sample += [int(offsets[ex + 1]) - 1 for ex in range(32) if counts[ex] > 0]  # last row of each expert
     sample += list(rng.choice(32768, size=64, replace=False))
     _expert_ffn(d, 16384, 2048, 4096, 32, 2, sample=np.unique(np.array(sample)))
+
+
+@pytest.mark.parametrize("tile", ["256x256", "64x256", None])
+def test_grouped_tile_shapes(monkeypatch, tile):
+    # 600 tokens, top-2 of 4 experts: about 300 rows per expert (256-row tiles by default)
+    case("moe tile=%s" % tile)
+    if tile is not None:
+        monkeypatch.setenv("RQ_GEMM_TILE", tile)
+    d = workloads.make(4, t=600, k=128, f=144, e=4)
+    _expert_ffn(d, 600, 128, 144, 4, 2)
