@@ -83,12 +83,12 @@ def moe_workspace_size(t, top_k, e, n, k, in_layout="tokens", act="none", out_la
         _code(OUT_LAYOUTS, out_layout, "out_layout")))
 
 
-def _debug(debug, rows, k, act, device):
+def _debug(debug, q_rows, h_rows, k, act, device):
     if not debug:
         return None, None
-    d = {"a_q": torch.empty((rows, k), dtype=torch.uint8, device=device),
-         "a_scale": torch.empty((rows,), dtype=torch.float32, device=device),
-         "h": torch.empty((rows, k), dtype=torch.float16, device=device) if act == RQ_ACT_SILU_MUL else None}
+    d = {"a_q": torch.empty((q_rows, k), dtype=torch.uint8, device=device),
+         "a_scale": torch.empty((q_rows,), dtype=torch.float32, device=device),
+         "h": torch.empty((h_rows, k), dtype=torch.float16, device=device) if act == RQ_ACT_SILU_MUL else None}
     s = DebugOut(d["a_q"].data_ptr(), d["a_scale"].data_ptr(), d["h"].data_ptr() if d["h"] is not None else 0)
     return d, s
 
@@ -115,7 +115,7 @@ def linear(x, w_q, w_scale, act="none", out=None, workspace=None, debug=False, s
     lib = _lib.load()
     ws_bytes = lib.rq_fp8_linear_workspace_size(m, k, a)
     ws = _workspace(ws_bytes, x.device, workspace)
-    dbg, dbg_s = _debug(debug, m, k, a, x.device)
+    dbg, dbg_s = _debug(debug, m, m, k, a, x.device)
     st = lib.rq_fp8_linear(_ptr(x), m, k, a, _ptr(w_q), _ptr(w_scale), n, _ptr(out), _ptr(ws),
                            ws.numel(), ctypes.byref(dbg_s) if dbg_s is not None else None,
                            _stream(x, stream))
@@ -132,7 +132,8 @@ def moe_grouped_linear(x, topk_ids, w_q, w_scale, in_layout="tokens", act="none"
     ``topk_ids``: int32 [T, top_k]; ``w_q``: uint8 [E, N, K]; ``w_scale``: FP32 [E, N];
     ``topk_w``: FP16 [T, top_k] for ``out_layout='combined'``.
     Returns FP16 [T*top_k, N] (permuted) or [T, N] (combined), plus the debug dict when
-    ``debug=True``.
+    ``debug=True``: ``a_q`` / ``a_scale`` hold the GEMM operand, one row per routed slot in
+    the permuted order; ``h`` (``silu_mul``) one row per input row.
     """
     il = _code(IN_LAYOUTS, in_layout, "in_layout")
     a = _code(ACTS, act, "act")
@@ -155,7 +156,7 @@ def moe_grouped_linear(x, topk_ids, w_q, w_scale, in_layout="tokens", act="none"
     lib = _lib.load()
     ws_bytes = lib.rq_fp8_moe_workspace_size(t, top_k, e, n, k, il, a, ol)
     ws = _workspace(ws_bytes, x.device, workspace)
-    dbg, dbg_s = _debug(debug, rows, k, a, x.device)
+    dbg, dbg_s = _debug(debug, r, rows, k, a, x.device)
     st = lib.rq_fp8_moe_grouped_linear(
         _ptr(x), il, a, _ptr(topk_ids), _ptr(topk_w), t, top_k, _ptr(w_q), _ptr(w_scale), e, n, k,
         _ptr(out), ol, _ptr(ws), ws.numel(), ctypes.byref(dbg_s) if dbg_s is not None else None,

@@ -67,14 +67,14 @@ struct MoeLayout {
 
 MoeLayout moe_layout(int64_t T, int top_k, int64_t E, int64_t N, int64_t K, int in_layout,
                      int out_layout) {
+  (void)in_layout;
   const int64_t R = T * top_k;
-  const int64_t rows = in_layout == RQ_MOE_IN_TOKENS ? T : R;
   MoeLayout l;
-  l.a_q = (size_t)(rows * K);
-  l.a_scale = (size_t)rows * sizeof(float);
+  l.a_q = (size_t)(R * K);  // the GEMM operand: one quantized row per routed slot
+  l.a_scale = (size_t)R * sizeof(float);
   l.offsets = (size_t)(E + 1) * sizeof(int32_t);
   l.tile_start = (size_t)(E + 1) * sizeof(int32_t);
-  l.tile_table = (size_t)rq::grouped_max_mtiles(R, E, rq::tile_rows(rq::pick_grouped(R, E))) * 4 * sizeof(int32_t);
+  l.tile_table = (size_t)rq::grouped_max_mtiles(R, E, rq::kMinTileRows) * 4 * sizeof(int32_t);
   l.perm = (size_t)R * sizeof(int32_t);
   l.pos = (size_t)R * sizeof(int32_t);
   l.block_hist = (size_t)(rq::moe_plan_blocks(R) * E) * sizeof(int32_t);
@@ -133,7 +133,8 @@ int rq_fp8_quant_weights(const uint16_t* w, int64_t B, int64_t N, int64_t K, uin
   const int dev = check_device();
   if (dev != RQ_OK) return dev;
   Hook hook(RQ_KERNEL_QUANT, (hipStream_t)stream);
-  hipError_t e = rq::launch_quant_rows(w, rows, K, RQ_ACT_NONE, w_q, w_scale, nullptr, (hipStream_t)stream);
+  hipError_t e = rq::launch_quant_rows(w, rows, K, RQ_ACT_NONE, w_q, w_scale, nullptr, nullptr, 0,
+                                       (hipStream_t)stream);
   return e == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 
@@ -173,7 +174,8 @@ int rq_fp8_linear(const uint16_t* x, int64_t M, int64_t K, int act, const uint8_
   hipStream_t s = (hipStream_t)stream;
   {
     Hook hook(RQ_KERNEL_QUANT, s);
-    if (rq::launch_quant_rows(x, M, K, act, xq, sx, act == RQ_ACT_SILU_MUL ? dh : nullptr, s) != hipSuccess)
+    if (rq::launch_quant_rows(x, M, K, act, xq, sx, act == RQ_ACT_SILU_MUL ? dh : nullptr, nullptr, 0, s) !=
+        hipSuccess)
       return RQ_ERR_HIP;
   }
   rq::GemmArgs g{};
@@ -182,10 +184,10 @@ int rq_fp8_linear(const uint16_t* x, int64_t M, int64_t K, int act, const uint8_
   g.b = w_q;
   g.b_scale = w_scale;
   g.y = y;
-  g.M = M;
-  g.a_rows = M;
-  g.N = N;
-  g.K = K;
+  g.M = (int32_t)M;  // sizes validated above: every product fits 31 bits
+  g.a_rows = (int32_t)M;
+  g.N = (int32_t)N;
+  g.K = (int32_t)K;
   g.E = 1;
   Hook hook(RQ_KERNEL_GEMM, s);
   return rq::launch_gemm_dense(g, s) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
@@ -253,7 +255,10 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const i
     return RQ_ERR_HIP;
   {
     Hook hook(RQ_KERNEL_QUANT, s);
-    if (rq::launch_quant_rows(x, rows, K, act, aq, as, act == RQ_ACT_SILU_MUL ? dh : nullptr, s) != hipSuccess)
+    // per-token rows are written to each of the token's permuted slots
+    const bool tokens = in_layout == RQ_MOE_IN_TOKENS;
+    if (rq::launch_quant_rows(x, rows, K, act, aq, as, act == RQ_ACT_SILU_MUL ? dh : nullptr,
+                              tokens ? pos : nullptr, tokens ? top_k : 0, s) != hipSuccess)
       return RQ_ERR_HIP;
   }
   rq::GemmArgs g{};
@@ -262,17 +267,13 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const i
   g.b = w_q;
   g.b_scale = w_scale;
   g.y = y_perm;
-  g.M = R;
-  g.a_rows = rows;
-  g.N = N;
-  g.K = K;
-  g.offsets = offsets;
+  g.M = (int32_t)R;  // sizes validated above: every product fits 31 bits
+  g.a_rows = (int32_t)R;
+  g.N = (int32_t)N;
+  g.K = (int32_t)K;
   g.tile_start = tile_start;
   g.tile_table = tile_table;
-  g.perm = perm;
-  g.top_k = top_k;
   g.E = (int32_t)E;
-  g.gather_tokens = in_layout == RQ_MOE_IN_TOKENS ? 1 : 0;
   {
     Hook hook(RQ_KERNEL_GEMM, s);
     if (rq::launch_gemm_grouped(g, kind, s) != hipSuccess) return RQ_ERR_HIP;

@@ -40,31 +40,32 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 // Launch helpers ---------------------------------------------------------------------
 
+// Quantize `rows` FP16 rows (act: 0 none, 1 SiLU*up).  With pos == nullptr row t goes to
+// output row t; otherwise to output rows pos[t * fanout + k], k < fanout (a token's copies
+// in the permuted MoE order).  h (SiLU only, may be null) receives the FP16 SiLU*up rows.
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t K, int act,
-                             uint8_t* q, float* scale, uint16_t* h, hipStream_t stream);
+                             uint8_t* q, float* scale, uint16_t* h, const int32_t* pos, int fanout,
+                             hipStream_t stream);
 
 struct GemmArgs {
-  const uint8_t* a;       // [rows][K] E4M3 (token rows, or permuted rows)
-  const float* a_scale;   // [rows]
+  const uint8_t* a;       // [a_rows][K] E4M3 (token rows, or permuted rows in grouped mode)
+  const float* a_scale;   // [a_rows]
   const uint8_t* b;       // [E][N][K] E4M3 (E = 1 for a dense linear)
   const float* b_scale;   // [E][N]
-  uint16_t* y;            // [M or R][N] FP16
-  int64_t M;              // dense: rows of A and y.  grouped: R (routed rows)
-  int64_t a_rows;         // rows of the A array (dense: M; grouped: T or R)
-  int64_t N;
-  int64_t K;
+  uint16_t* y;            // [a_rows][N] FP16
+  int32_t M;              // dense: rows of A and y.  grouped: R (routed rows)
+  int32_t a_rows;         // rows of the A array (M, or R)
+  int32_t N;
+  int32_t K;
   // grouped only
-  const int32_t* offsets;     // [E+1] permuted row offsets per expert
   const int32_t* tile_start;  // [E+1] first m-tile of each expert (exclusive scan); [E] = total
   const int32_t* tile_table;  // [m-tiles][4] {expert, first row, end row, 0}
-  const int32_t* perm;        // [R] slot of each permuted row (TOKENS input only)
-  int32_t top_k;              // token of permuted row r = perm[r] / top_k (TOKENS input)
   int32_t E;
-  int32_t gather_tokens;      // 1: A row of permuted row r is perm[r] / top_k
 };
 
 // GEMM tile shapes (rows x columns of output per workgroup).
 enum { kTileBig = 0, kTileWide, kTileSmall, kTileThin, kTileThinWide, kTileKinds };
+constexpr int kMinTileRows = 64;  // fewest rows of any tile shape (sizes the MoE tile table)
 
 hipError_t launch_gemm_dense(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemm_grouped(const GemmArgs& g, int kind, hipStream_t stream);

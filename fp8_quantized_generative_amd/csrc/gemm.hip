@@ -1,7 +1,7 @@
 // FP8 (OCP E4M3) x FP8 GEMM with FP32 accumulation and a fused per-token x per-channel
 // dequantization to FP16, for gfx950 (MI355X).
 //
-// Computes y[m][n] = fl16(fl32(acc * s_a[m]) * s_b[n]), acc = sum_k a[m][k] * b[n][k]:
+// Computes y[m][n] = fl16(fl32(fl32(acc * s_a[m]) * s_b[n])), acc = sum_k a[m][k] * b[n][k]:
 // the FP8 product with FP32 accumulation and the cast back to FP16 of page "Quantized
 // Inference for OneRec-V2：生成式推荐开始直接吃 LLM 量化栈", section 关键证据, with the
 // quantize -> FP8 GEMM -> dequantize flow of page "FP8量化在生成式推荐系统OneRec-V2中的
@@ -10,35 +10,46 @@
 //
 // Design (CDNA4):
 // * Matrix core: v_mfma_f32_32x32x64_f8f6f4 (FP8 x FP8, 32 x 32 outputs, K = 64 per
-//   instruction, full FP8 rate on gfx950).  Lane l feeds 32 bytes of A row (l & 31) and of
-//   B column (l & 31); the two 32-lane halves take the two 32-byte halves of the 64-byte K
-//   slab.  A and B use the same K assignment, so the dot product is the plain one.
-// * Tiles: BM x BN outputs per workgroup (256x256, 256x128 or 128x128) split over a grid of
-//   wavefronts (2 x 4, 4 x 2 or 2 x 2), each owning a block of 32x32 MFMA tiles.
+//   instruction, full FP8 rate on gfx950).  Lane l feeds 32 bytes of row (l & 31) of each
+//   operand; the two 32-lane halves take the two 32-byte halves of the 64-byte K slab.  Both
+//   operands use the same K assignment, so the dot product is the plain one.  The weight
+//   fragment is the instruction's first operand and the activation fragment its second, so
+//   the 32 x 32 result comes out transposed: lane l holds token row (l & 31) and, in
+//   register r, output column 8 (r / 4) + 4 (l / 32) + r % 4 - four consecutive columns
+//   per group of four registers, which the epilogue writes straight to memory.
+// * Tiles: BM x BN outputs per workgroup (256x256, 256x128, 128x128, 64x128 or 64x256)
+//   split over a grid of wavefronts, each owning a block of 32x32 MFMA tiles.
+// * Persistent workgroups: the grid holds as many workgroups as the CUs keep resident and
+//   each walks a list of tiles, so one tile's epilogue overlaps the loads of the next.
 // * Pipeline: K advances in 64-byte slabs (BM A rows + BN B rows, 32 KB at 256x256) held
-//   in a ring of S LDS buffers (5 at 256x256, filling the 160 KB LDS).  Slabs are fetched
-//   S - 1 ahead of the one being multiplied with buffer loads that write LDS directly (no
-//   registers held for data in flight); one vmcnt wait and one barrier per slab.  Measured on MI355X, a single slab of lookahead
-//   left the matrix cores idle about 70% of the time waiting for global loads.
+//   in a ring of S LDS buffers.  Slabs are fetched S - 1 ahead of the one being multiplied
+//   with buffer loads that write LDS directly (no registers held for data in flight); one
+//   vmcnt wait and one barrier per slab.  The ring runs on across tiles: the last S steps
+//   of a tile fetch the first S slabs of the workgroup's next tile, and the row and column
+//   scales of each tile arrive the same way in a small double-buffered LDS area.  Measured
+//   on MI355X, a single slab of lookahead left the matrix cores idle about 70% of the time
+//   waiting for global loads.
 // * LDS layout: 64-byte rows; the 16-byte granule g of row r sits at granule
 //   g ^ ((r>>1)&1) ^ ((r>>1)&2) ^ ((r>>3)&1), so a fragment read (32 consecutive rows, one
 //   granule) touches every bank once per 8- or 16-lane phase.  Each direct-to-LDS load
 //   fills 16 consecutive rows; lanes fetch the granule that the swizzle puts at their slot.
 //   Rows outside the tile and K past the end read as zero through the buffer range check.
-// * Tile order: the hardware hands consecutive workgroup ids to the 8 XCDs in turn; ids are
-//   remapped so each XCD receives a contiguous range of the logical order, and the logical
-//   order walks groups of 8 M-tiles across all N-tiles, so tiles that share A rows or B
-//   columns run on the same XCD and hit its L2.
-// * Epilogue: accumulators are scaled (FP32 per-row and per-column scales), rounded to
-//   FP16, staged through LDS one 32-row strip per wave, and written with 16-byte stores so
-//   each output row segment is one contiguous burst.
+// * Tile order: the hardware hands consecutive workgroup ids to the 8 XCDs in turn; each
+//   XCD's workgroups share a contiguous slice of the logical order, and the logical order
+//   walks groups of 8 M-tiles across all N-tiles, so tiles that share A rows or B columns
+//   run on the same XCD at the same time and hit its L2.
+// * Epilogue: each lane scales its four-column groups (FP32 row and column scales read from
+//   LDS) and rounds them to FP16; 32-row strips staged in LDS turn them into 16-byte stores
+//   that write whole 128-byte row segments.
+// * Wavefront roles: half the wavefronts issue every global load and never store, the
+//   other half issue every output store and never wait for loads to land (see the kernel).
 //
 // Grouped (MoE) mode: the M-tiles are the concatenation over experts of
 // ceil(count_e / BM) tiles each, listed by the routing plan on the device in a table of
-// {expert, first row, end row}.  A workgroup reads its entry with one load, reads A rows through the
-// permutation (token perm[r] / top_k) when the input is per token, uses expert e's weights
-// and scales, and writes permuted output rows.  Tiles past the device-side total exit at
-// once, so the host never needs the per-expert counts.
+// {expert, first row, end row}.  A tile reads its entry with one scalar load, multiplies
+// permuted rows [first, end) of A with expert e's weights and scales, and writes the same
+// permuted output rows.  The device-side tile total bounds the walk, so the host never
+// needs the per-expert counts.
 
 #include <cstdlib>
 #include <cstring>
@@ -68,17 +79,26 @@ struct Cfg {
   static constexpr int TJ = WN / 32;             // ... N direction
   static constexpr int ROWS = BM + BN;           // A rows then B rows in one LDS slab
   static constexpr int STAGE = ROWS * BK;        // bytes per slab
-  static constexpr int ROWS_PER_WAVE = ROWS / WAVES;
-  static constexpr int LOADS = ROWS_PER_WAVE / 16;  // direct-to-LDS loads per lane per slab
-  static constexpr int EPI_STRIDE = WN * 2 + 16;    // padded FP16 strip row (bytes)
-  static constexpr int EPI_BYTES = 32 * EPI_STRIDE;
+  // Wavefront roles: waves 0..LOADERS-1 issue every load, waves LOADERS.. every output
+  // store (see the kernel), so no wave ever waits for its stores to retire.
+  static constexpr int LOADERS = WAVES / 2;
+  static constexpr int LOADS = ROWS / 16 / LOADERS;  // direct-to-LDS loads per loader lane per slab
+  static constexpr int A_LOADS = BM / 16 / LOADERS;  // the first A_LOADS of them fetch A rows
+  static constexpr int SCALE_BYTES = 4 * ROWS;       // BM row scales, then BN column scales
+  static constexpr int SCALE_LOADS = ROWS / 64;      // 4-byte-per-lane loads per tile
+  static constexpr int EPI_STRIDE = 2 * WN + 16;     // padded FP16 row of an output strip
+  static constexpr int STRIP = 32 * EPI_STRIDE;     // one per loader/storer pair
+  static constexpr int SCALE_OFF = S * STAGE;
+  static constexpr int EPI_OFF = SCALE_OFF + 2 * SCALE_BYTES;
+  static constexpr int LDS = EPI_OFF + LOADERS * STRIP;
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
-  static_assert(ROWS_PER_WAVE % 16 == 0, "whole 16-row load groups per wave");
-  static_assert(WAVES * EPI_BYTES + 4 * (BM + BN) <= S * STAGE, "epilogue staging fits in the ring");
-  static_assert(NT >= BM && NT >= BN, "one thread per row / column scale");
+  static_assert(WAVES % 2 == 0 && (ROWS / 16) % LOADERS == 0, "whole 16-row load groups per loader");
+  static_assert((BM / 16) % LOADERS == 0, "each load fetches only A rows or only B rows");
+  static_assert((16 * WN / 8) % 64 == 0, "whole strip reads per lane");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile of whole 32x32 MFMA tiles");
-  static_assert(S * STAGE <= 160 * 1024, "ring fits in the 160 KB LDS of a CU");
-  static_assert((S - 1) * LOADS < 64, "outstanding loads fit the 6-bit vmcnt");
+  static_assert(LDS <= 160 * 1024, "ring, scales and strips fit in the 160 KB LDS of a CU");
+  static_assert(S >= 2 && S * LOADS + (SCALE_LOADS + LOADERS - 1) / LOADERS < 64,
+                "outstanding loads fit the 6-bit vmcnt");
 };
 
 __device__ __forceinline__ int swz(int row, int g) {
@@ -100,20 +120,26 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
-// Scheduling pattern: MFMA q followed by its share of the next slab's fragment reads, the
-// R reads spread over the first RM of the M MFMAs.
-template <int Q, int M, int R, int RM>
+// Only the LDS reads (lgkmcnt = 0; vmcnt and expcnt at their maxima).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+// Scheduling pattern of one slab (M MFMAs over TI x TJ tiles, i-major): each MFMA followed
+// by the fragment reads it frees or that are due - two B reads after each of the first TJ
+// MFMAs, and A fragment i's two reads after the last MFMA that uses it.
+template <int Q, int M, int TJ>
 __device__ __forceinline__ void interleave_mfma_reads() {
   if constexpr (Q < M) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    constexpr int hi = (Q + 1) * R / RM < R ? (Q + 1) * R / RM : R;
-    constexpr int lo = Q * R / RM < R ? Q * R / RM : R;
-    if constexpr (hi - lo > 0) __builtin_amdgcn_sched_group_barrier(0x100, hi - lo, 0);  // DS reads
-    interleave_mfma_reads<Q + 1, M, R, RM>();
+    constexpr int reads = (Q < TJ ? 2 : 0) + (Q % TJ == TJ - 1 ? 2 : 0);
+    if constexpr (reads > 0) __builtin_amdgcn_sched_group_barrier(0x100, reads, 0);  // DS reads
+    interleave_mfma_reads<Q + 1, M, TJ>();
   }
 }
 
 // Wait until at most n slabs of L loads each remain outstanding (n clamped to [0, MAXN]).
+// Loads return in issue order, so every slab issued before the last n is then in LDS.
+// Any other vector memory operation issued later (scale loads, output stores) only makes
+// the wait stricter.
 template <int L, int MAXN, bool LGKM0>
 __device__ __forceinline__ void wait_slabs(int n) {
   if constexpr (MAXN > 0) {
@@ -127,56 +153,10 @@ __device__ __forceinline__ void wait_slabs(int n) {
   }
 }
 
-struct TileInfo {
-  int64_t row_begin;
-  int64_t row_end;
-  int nt;
-  int expert;
-};
-
-template <int BM, bool GROUPED>
-__device__ __forceinline__ bool map_tile(const GemmArgs& p, int m_tiles, int n_tiles, TileInfo& t) {
-  // Workgroup ids go round-robin over the 8 XCDs.  Give each XCD a contiguous slice of the
-  // logical tile order (neighbouring tiles share operands in that XCD's L2).  In grouped
-  // mode the grid is sized for the worst case, so the slices cover only the real tiles
-  // (known on the device) and the surplus workgroups of every XCD exit.
-  int total = (int)gridDim.x;
-  if (GROUPED) {
-    m_tiles = p.tile_start[p.E];  // real M-tiles; the grid covers the worst case
-    total = m_tiles * n_tiles;
-  }
-  int bid = (int)blockIdx.x;
-  if ((gridDim.x & 7) == 0) {
-    const int per_xcd = (total + 7) >> 3;
-    bid = (bid & 7) * per_xcd + (bid >> 3);
-    if (bid >= total || (int)(blockIdx.x >> 3) >= per_xcd) return false;
-  } else if (bid >= total) {
-    return false;
-  }
-  const int per_group = kGroupM * n_tiles;
-  const int group = bid / per_group;
-  const int first_m = group * kGroupM;
-  const int gm = min(m_tiles - first_m, kGroupM);
-  const int in_group = bid - group * per_group;
-  const int mt = first_m + in_group % gm;
-  t.nt = in_group / gm;
-  if (GROUPED) {
-    const int4 ent = *reinterpret_cast<const int4*>(p.tile_table + 4 * (int64_t)mt);
-    t.expert = ent.x;
-    t.row_begin = ent.y;
-    t.row_end = ent.z;
-  } else {
-    t.expert = 0;
-    t.row_begin = (int64_t)mt * BM;
-    t.row_end = t.row_begin + BM < p.M ? t.row_begin + BM : p.M;
-  }
-  return true;
-}
-
-template <bool GROUPED>
-__device__ __forceinline__ int64_t a_source_row(const GemmArgs& p, int64_t r) {
-  if (GROUPED && p.gather_tokens) return (int64_t)(p.perm[r] / p.top_k);
-  return r;
+// A wave-uniform load through the scalar cache, from memory that no kernel writes while
+// this one runs (the routing plan's tables).
+__device__ __forceinline__ int load_uniform(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)(p);
 }
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -190,8 +170,9 @@ __device__ __forceinline__ v4i make_desc(const void* base, uint32_t bytes) {
                __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
 }
 
-// One 16-byte-per-lane buffer load that writes LDS directly: lane l's 16 bytes land at
-// LDS byte address lds_base + lds_imm + 16 l; the global address is base + voffset + soffset.
+// Buffer loads that write LDS directly: lane l's 16 bytes land at LDS byte address
+// lds_base + lds_imm + 16 l (4 bytes at lds_addr + 4 l for the dword form); the global
+// address is base + voffset + soffset.
 // Written as inline asm so that the compiler does not treat the outstanding LDS writes as
 // aliasing every later LDS read (it would otherwise wait for all loads in flight before
 // each fragment read); completion is tracked with explicit vmcnt waits instead.  The asm
@@ -211,78 +192,162 @@ __device__ __forceinline__ void load_lds_16(const v4i& desc, uint32_t voffset, u
       : "s"(lds_base), "v"(voffset), "s"(desc), "s"(soffset), "i"(lds_imm)
       : "memory", "m0", "scc");
 }
+
+__device__ __forceinline__ void load_lds_4(const v4i& desc, uint32_t voffset, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds"
+      :
+      : "s"(lds_addr), "v"(voffset), "s"(desc)
+      : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// Two FP32 values rounded to FP16 (nearest even), packed low then high.
+__device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
+  const h2 v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+struct TileInfo {
+  int row_begin;  // first output row (permuted row in grouped mode)
+  int row_end;    // one past the last valid row
+  int n0;         // first output column
+  int expert;
+};
+
+// Logical tile L -> rows and columns: groups of kGroupM M-tiles walked column by column.
+template <int BM, int BN, bool GROUPED>
+__device__ __forceinline__ TileInfo tile_info(const GemmArgs& p, int L, int m_tiles, int n_tiles) {
+  const int per_group = kGroupM * n_tiles;
+  const int group = L / per_group;
+  const int first_m = group * kGroupM;
+  const int gm = min(m_tiles - first_m, kGroupM);
+  const int in_group = L - group * per_group;
+  const int mt = first_m + in_group % gm;
+  TileInfo t;
+  t.n0 = (in_group / gm) * BN;
+  if (GROUPED) {
+    const int32_t* ent = p.tile_table + 4 * (int64_t)mt;
+    t.expert = load_uniform(ent);
+    t.row_begin = load_uniform(ent + 1);
+    t.row_end = load_uniform(ent + 2);
+  } else {
+    t.expert = 0;
+    t.row_begin = mt * BM;
+    t.row_end = min(t.row_begin + BM, p.M);
+  }
+  return t;
+}
+
+// Buffer descriptors of one tile: A covers its valid rows, B its valid weight rows, so
+// everything past them reads zero.
+struct TileDesc2 {
+  v4i a, b;
+};
+
+// Selects between descriptor values (a conditional on references would force them into
+// memory).
+__device__ __forceinline__ v4i pick(bool c, v4i x, v4i y) { return c ? x : y; }
+
+template <int BN>
+__device__ __forceinline__ TileDesc2 tile_descs(const GemmArgs& p, const TileInfo& t) {
+  TileDesc2 d;
+  d.a = make_desc(p.a + (int64_t)t.row_begin * p.K, (uint32_t)((t.row_end - t.row_begin) * p.K));
+  d.b = make_desc(p.b + ((int64_t)t.expert * p.N + t.n0) * p.K, (uint32_t)(min(BN, p.N - t.n0) * p.K));
+  return d;
+}
 
 template <class C, bool GROUPED>
 __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles, int n_tiles) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[C::S * C::STAGE];
-  TileInfo t;
-  if (!map_tile<C::BM, GROUPED>(p, m_tiles, n_tiles, t)) return;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
+
+  // ---- this workgroup's tiles: logical tiles first, first + stride, ... below last.
+  // Workgroup ids go round-robin over the 8 XCDs; each XCD's workgroups share a contiguous
+  // slice of the logical order.  In grouped mode the real M-tile count is on the device.
+  if (GROUPED) m_tiles = load_uniform(p.tile_start + p.E);
+  const int total = m_tiles * n_tiles;
+  int first, stride, last;
+  {
+    const int bid = (int)blockIdx.x;
+    if ((gridDim.x & 7) == 0) {
+      const int per_xcd = (total + 7) >> 3;
+      const int xcd = bid & 7;
+      first = xcd * per_xcd + (bid >> 3);
+      stride = (int)(gridDim.x >> 3);
+      last = min(total, (xcd + 1) * per_xcd);
+    } else {
+      first = bid;
+      stride = (int)gridDim.x;
+      last = total;
+    }
+  }
+  if (first >= last) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps addressing scalar
-  const int64_t K = p.K;
-  const int64_t N = p.N;
-  const int n0 = t.nt * C::BN;
-  const v4i a_desc = make_desc(p.a, (uint32_t)(p.a_rows * K));
-  const v4i b_desc = make_desc(p.b + (int64_t)t.expert * N * K, (uint32_t)(N * K));
+  // gfx9 counts loads and stores in one vmcnt per wave, so a wave that stored its outputs
+  // would wait for those stores to retire at its next slab wait - with every CU writing its
+  // tile at once, several microseconds.  Loader waves therefore issue all loads and never
+  // store; storer waves issue all output stores (their own rows and their partner loader's,
+  // handed over in LDS) and never wait on vmcnt - the barrier after the loaders' waits
+  // tells them a slab has landed.
+  const bool loader = wave < C::LOADERS;
+  const int K = p.K;
+  const int N = p.N;
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  const float* __restrict__ sb = p.b_scale + (int64_t)t.expert * N;
+  const int ktiles = (K + BK - 1) / BK;
+  const int full_slabs = K / BK;
 
-  // Row / column scales for the epilogue: issued before the first direct-to-LDS load, so
-  // they complete before it (vector memory loads return in order) and cost no wait later.
-  float my_sa = 0.f, my_sb = 0.f;
-  if (tid < C::BM) {
-    const int64_t r = t.row_begin + tid;
-    if (r < t.row_end) my_sa = p.a_scale[a_source_row<GROUPED>(p, r)];
-  }
-  if (tid < C::BN && n0 + tid < N) my_sb = sb[n0 + tid];
-
-  // ---- direct-to-LDS loads.  Load t of wave w fills slab rows [row0, row0 + 16) with
-  // row0 = w * ROWS_PER_WAVE + 16 t; lane l writes 16 bytes at row row0 + l / 4, physical
-  // granule l % 4, so it fetches logical granule (l % 4) ^ f(row) of that row.
+  // ---- direct-to-LDS loads.  Load i of loader w fills slab rows [row0, row0 + 16) with
+  // row0 = 16 (i * LOADERS + w); lane l writes 16 bytes at row row0 + l / 4, physical
+  // granule l % 4, so it fetches logical granule (l % 4) ^ f(row) of that row.  Loads
+  // i < A_LOADS cover the BM A rows, the rest the BN B rows.
   // The swizzle depends only on row bits 1..3, which (lane >> 2) fixes for every load, so
-  // each lane fetches the same granule in all of its loads.
+  // each lane fetches the same granule in all of its loads.  Offsets are relative to the
+  // tile's descriptors, so they are the same for every tile.
   const int gran = swz(lane >> 2, lane & 3);  // XOR swizzle is its own inverse
-  uint32_t src_off[C::LOADS];
+  uint32_t voff[C::LOADS];
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i) {
-    const int row0 = wave * C::ROWS_PER_WAVE + 16 * i;
-    const int row = row0 + (lane >> 2);
-    const int g = gran;
-    if (row0 < C::BM) {
-      const int64_t r = t.row_begin + row;
-      const bool ok = GROUPED ? r < t.row_end : true;  // dense rows past M read zero
-      src_off[i] = ok ? (uint32_t)(a_source_row<GROUPED>(p, r) * K + 16 * g) : kOutOfRange;
-    } else {
-      src_off[i] = (uint32_t)((n0 + (row - C::BM)) * K + 16 * g);  // rows past N read zero
-    }
+    const int row = 16 * (i * C::LOADERS + wave) + (lane >> 2);
+    voff[i] = (uint32_t)((i < C::A_LOADS ? row : row - C::BM) * K + 16 * gran);
   }
   // Wave-uniform LDS byte address of this wave's first 16-row group in ring buffer `buf`.
   auto wave_lds = [&](int buf) -> uint32_t {
-    return (uint32_t)__builtin_amdgcn_readfirstlane(
-        (int)(smem_lds + buf * C::STAGE + wave * C::ROWS_PER_WAVE * BK));
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(smem_lds + buf * C::STAGE + wave * 16 * BK));
   };
   // Full slab (all 64 K bytes in range): the K offset travels in the scalar soffset.
-  auto issue_full = [&](int slab, uint32_t lds, int i) {
-    const int row0 = wave * C::ROWS_PER_WAVE + 16 * i;
-    load_lds_16(row0 < C::BM ? a_desc : b_desc, src_off[i], (uint32_t)__builtin_amdgcn_readfirstlane(slab * BK),
-                lds, 16 * BK * i);
+  auto issue_full = [&](const TileDesc2& d, int slab, uint32_t lds, int i) {
+    load_lds_16(i < C::A_LOADS ? d.a : d.b, voff[i], (uint32_t)__builtin_amdgcn_readfirstlane(slab * BK), lds,
+                16 * BK * C::LOADERS * i);
   };
   // Any slab, including the ragged last one: granules past K read zero.
-  auto issue_one = [&](int slab, int buf, int i) {
+  auto issue_one = [&](const TileDesc2& d, int slab, uint32_t lds, int i) {
     const uint32_t k0 = (uint32_t)slab * BK;
-    const int row0 = wave * C::ROWS_PER_WAVE + 16 * i;
-    const bool kin = (int64_t)k0 + 16 * gran < K;
-    const uint32_t off = kin ? src_off[i] + k0 : kOutOfRange;
-    load_lds_16(row0 < C::BM ? a_desc : b_desc, off, 0u, wave_lds(buf), 16 * BK * i);
+    const bool kin = (int)k0 + 16 * gran < K;
+    load_lds_16(i < C::A_LOADS ? d.a : d.b, kin ? voff[i] + k0 : kOutOfRange, 0u, lds, 16 * BK * C::LOADERS * i);
   };
-  auto issue_slab = [&](int slab, int buf) {
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) issue_one(slab, buf, i);
+  // The tile's BM row scales and BN column scales into scale area `region` (0 or 1);
+  // entries past the tile's rows or columns read zero and are never used.
+  auto issue_scales = [&](const TileInfo& t, int region) {
+    if (!loader) return;
+    const uint32_t base = smem_lds + C::SCALE_OFF + region * C::SCALE_BYTES;
+    for (int q = wave; q < C::SCALE_LOADS; q += C::LOADERS) {
+      const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane((int)(base + 256 * q));
+      if (q < C::BM / 64) {
+        const v4i d = make_desc(p.a_scale + t.row_begin, (uint32_t)(4 * (t.row_end - t.row_begin)));
+        load_lds_4(d, (uint32_t)(4 * (64 * q + lane)), dst);
+      } else {
+        const v4i d = make_desc(p.b_scale + (int64_t)t.expert * N + t.n0, (uint32_t)(4 * min(C::BN, N - t.n0)));
+        load_lds_4(d, (uint32_t)(4 * (64 * (q - C::BM / 64) + lane)), dst);
+      }
+    }
   };
 
   // ---- MFMA fragment addressing: lane -> (row within 32, K half).  A fragment is two
@@ -292,139 +357,253 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
   const int frow = lane & 31;
   const int half = lane >> 5;
   const int f_off[2] = {frow * BK + 16 * swz(frow, 2 * half), frow * BK + 16 * swz(frow, 2 * half + 1)};
-  constexpr int kReads = 2 * (C::TI + C::TJ);   // 16-byte fragment reads per slab
   constexpr int kMfma = C::TI * C::TJ;
-  // The next slab's fragment reads go out during the first half of the MFMAs, so they have
-  // landed by the lgkmcnt wait that precedes the next barrier.
-  constexpr int kReadMfmas = kMfma / 2 > 0 ? kMfma / 2 : 1;
-  // read r of a slab: A fragments first, then B; r / 2 selects the fragment, r % 2 the half
-  auto read_one = [&](const uint8_t* S, int r) -> uint4 {
-    const int f = r >> 1;
-    const int row = f < C::TI ? wm * C::WM + 32 * f : C::BM + wn * C::WN + 32 * (f - C::TI);
-    return *reinterpret_cast<const uint4*>(S + row * BK + f_off[r & 1]);
+  // Fragment r (= 2 f + h) of the A (or B) rows of a slab: half h of 32-row fragment f.
+  auto read_a = [&](const uint8_t* S, int r) -> uint4 {
+    return *reinterpret_cast<const uint4*>(S + (wm * C::WM + 32 * (r >> 1)) * BK + f_off[r & 1]);
   };
-
-  v16f acc[C::TI][C::TJ];
-#pragma unroll
-  for (int i = 0; i < C::TI; ++i)
-#pragma unroll
-    for (int j = 0; j < C::TJ; ++j) acc[i][j] = (v16f){};
-
-  // Two fragment register sets: the MFMAs of slab kt use one while the reads of slab kt+1
-  // fill the other.
-  uint4 fr0[kReads], fr1[kReads];
+  auto read_b = [&](const uint8_t* S, int r) -> uint4 {
+    return *reinterpret_cast<const uint4*>(S + (C::BM + wn * C::WN + 32 * (r >> 1)) * BK + f_off[r & 1]);
+  };
   auto as_v8 = [](const uint4& lo, const uint4& hi) -> v8i {
     return (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
 
-  const int ktiles = (int)((K + BK - 1) / BK);
-  // prologue: slabs 0..S-1 in flight, then slab 0's fragments
-#pragma unroll
-  for (int s = 0; s < C::S; ++s)
-    if (s < ktiles) issue_slab(s, s);
-  wait_slabs<C::LOADS, C::S - 1, false>((ktiles < C::S ? ktiles : C::S) - 1);
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < kReads; ++r) fr0[r] = read_one(smem, r);
+  v16f acc[C::TI][C::TJ];
+  // Fragments: the A fragments of a slab live in one register set, each reloaded with the
+  // next slab's data as soon as the MFMAs that use it have issued; the B fragments, used by
+  // every MFMA of the slab, alternate between two sets.
+  uint4 fa[2 * C::TI], fb0[2 * C::TJ], fb1[2 * C::TJ];
 
-  // One slab: wait for slab kt+1 and the reads of slab kt, barrier (slab kt's buffer is then
-  // free for slab kt+4), then the MFMAs of slab kt interleaved with the fragment reads of
-  // slab kt+1 and the direct-to-LDS loads of slab kt+4.  A single wave can issue only about
-  // a dozen other instructions in the shadow of one 32x32x64 MFMA, so the steady-state step
-  // (every slab involved complete and in range) carries no run-time conditions and no
-  // vector address arithmetic; the generic step handles the last slabs and a ragged K.
-  auto step = [&](auto steady, int kt, uint4 (&cur)[kReads], uint4 (&nxt)[kReads]) {
-    constexpr bool kSteady = decltype(steady)::value;
-    bool has_next = true, has_load = true;
-    if constexpr (kSteady) {
-      wait_vmcnt_lgkm0<(C::S - 2) * C::LOADS>();
-    } else {
-      wait_slabs<C::LOADS, C::S - 2, true>(ktiles - 2 - kt);  // slabs issued after kt+1
-      has_next = kt + 1 < ktiles;
-      has_load = kt + C::S < ktiles;
-    }
-    __syncthreads();
-    const uint8_t* Sn = smem + ((kt + 1) % C::S) * C::STAGE;
-    const uint32_t lds_dst = wave_lds(kt % C::S);
-    int r = 0, l = 0;
+  // ---- current and next tile
+  TileInfo cur = tile_info<C::BM, C::BN, GROUPED>(p, first, m_tiles, n_tiles);
+  TileDesc2 dc = tile_descs<C::BN>(p, cur);
+  int rb = 0;  // ring buffer that holds slab 0 of the current tile
+
+  // A tile's scales and slabs 0..min(S, ktiles)-1 into ring buffers 0.., then (after the
+  // wait) slab 0's fragments.
+  auto prologue = [&](const TileInfo& t, TileDesc2 d, int region) {
+    if (!loader) return;
+    issue_scales(t, region);
+    // An opaque zero keeps the compiler from computing these offsets once for all tiles
+    // and holding them (or spilling them) across the whole tile loop.
+    int s0 = 0;
+    asm volatile("" : "+s"(s0));
 #pragma unroll
-    for (int q = 0; q < kMfma; ++q) {
-      const int i = q / C::TJ, j = q % C::TJ;
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          as_v8(cur[2 * i], cur[2 * i + 1]), as_v8(cur[2 * (C::TI + j)], cur[2 * (C::TI + j) + 1]),
-          acc[i][j], 0, 0, 0, 0, 0, 0);
-      const int r_end = (q + 1) * kReads / kReadMfmas < kReads ? (q + 1) * kReads / kReadMfmas : kReads;
-      for (; r < r_end; ++r)
-        if (kSteady || has_next) nxt[r] = read_one(Sn, r);
-      const int l_end = (q + 1) * C::LOADS / kMfma;
-      for (; l < l_end; ++l) {
-        if constexpr (kSteady) issue_full(kt + C::S, lds_dst, l);
-        else if (has_load) issue_one(kt + C::S, kt % C::S, l);
+    for (int s = 0; s < C::S; ++s)
+      if (s < ktiles)
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i) issue_one(d, s + s0, wave_lds(s), i);
+  };
+  // Wait for slab 0 of a tile (in ring buffer `buf`), then read its fragments.
+  auto wait_read_first = [&](int buf) {
+    if (loader) wait_slabs<C::LOADS, C::S - 1, false>((ktiles < C::S ? ktiles : C::S) - 1);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 2 * C::TI; ++r) fa[r] = read_a(smem + buf * C::STAGE, r);
+#pragma unroll
+    for (int r = 0; r < 2 * C::TJ; ++r) fb0[r] = read_b(smem + buf * C::STAGE, r);
+  };
+  prologue(cur, dc, 0);
+  wait_read_first(0);
+
+  using True = std::integral_constant<bool, true>;
+  using False = std::integral_constant<bool, false>;
+
+  for (int L = first, j = 0; L < last; L += stride, ++j) {
+    const bool has_next = L + stride < last;
+    TileInfo nxt = cur;
+    TileDesc2 dn = dc;
+    if (has_next) {
+      nxt = tile_info<C::BM, C::BN, GROUPED>(p, L + stride, m_tiles, n_tiles);
+      dn = tile_descs<C::BN>(p, nxt);
+    }
+    // With K of at least S slabs the last S steps fetch slabs 0..S-1 of the next tile.
+    const bool pre = has_next && ktiles >= C::S;
+    const int lim = pre ? ktiles + C::S : ktiles;  // slabs (from this tile's first) fetched here
+
+    // One slab: wait for slab kt+1 and the reads of slab kt, barrier (slab kt's buffer is
+    // then free for slab kt+S), then the MFMAs of slab kt interleaved with the fragment reads
+    // of slab kt+1 and the direct-to-LDS loads of slab kt+S.  A single wave can issue only
+    // about a dozen other instructions in the shadow of one 32x32x64 MFMA, so the
+    // steady-state step (every slab involved complete, in range and in this tile) carries
+    // no run-time conditions and no vector address arithmetic; the generic step handles the
+    // last slabs, a ragged K and the fetches for the next tile.  The first step of a tile
+    // starts its accumulators from zero.
+    auto step = [&](auto steady, auto first_step, int kt, uint4 (&bc)[2 * C::TJ], uint4 (&bn)[2 * C::TJ]) {
+      constexpr bool kSteady = decltype(steady)::value;
+      constexpr bool kFirst = decltype(first_step)::value;
+      bool has_read = true;
+      int fetch = 1;  // 0: nothing, 1: slab kt+S of this tile, 2: slab kt+S-ktiles of the next
+      if constexpr (kSteady) {
+        if (loader) wait_vmcnt_lgkm0<(C::S - 2) * C::LOADS>();
+        else wait_lgkm0();
+      } else {
+        if (loader) wait_slabs<C::LOADS, C::S - 2, true>(lim - kt - 2);  // slabs issued after kt+1
+        else wait_lgkm0();
+        has_read = kt + 1 < ktiles;
+        fetch = !loader ? 0 : kt + C::S < ktiles ? 1 : (pre ? 2 : 0);
+      }
+      __syncthreads();
+      const uint8_t* Sn = smem + ((rb + kt + 1) % C::S) * C::STAGE;
+      const uint32_t lds_dst = wave_lds((rb + kt) % C::S);
+      if (!kSteady && fetch == 2 && kt + C::S == ktiles) issue_scales(nxt, (j + 1) & 1);
+      int l = 0;
+#pragma unroll
+      for (int q = 0; q < kMfma; ++q) {
+        const int i = q / C::TJ, jj = q % C::TJ;
+        const v8i bf = as_v8(bc[2 * jj], bc[2 * jj + 1]);
+        const v8i af = as_v8(fa[2 * i], fa[2 * i + 1]);
+        if constexpr (kFirst)
+          acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, (v16f){}, 0, 0, 0, 0, 0, 0);
+        else
+          acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[i][jj], 0, 0, 0, 0, 0, 0);
+        if (kSteady || has_read) {
+          if (q < C::TJ) {
+            bn[2 * q] = read_b(Sn, 2 * q);
+            bn[2 * q + 1] = read_b(Sn, 2 * q + 1);
+          }
+          if (jj == C::TJ - 1) {
+            fa[2 * i] = read_a(Sn, 2 * i);
+            fa[2 * i + 1] = read_a(Sn, 2 * i + 1);
+          }
+        }
+        const int l_end = (q + 1) * C::LOADS / kMfma;
+        for (; l < l_end; ++l) {
+          if constexpr (kSteady) {
+            if (loader) issue_full(dc, kt + C::S, lds_dst, l);
+          } else if (fetch != 0) {
+            const bool nx = fetch == 2;
+            issue_one(TileDesc2{pick(nx, dn.a, dc.a), pick(nx, dn.b, dc.b)}, nx ? kt + C::S - ktiles : kt + C::S,
+                      lds_dst, l);
+          }
+        }
+      }
+      interleave_mfma_reads<0, kMfma, C::TJ>();
+    };
+
+    if (C::S < full_slabs) step(True{}, True{}, 0, fb0, fb1);
+    else step(False{}, True{}, 0, fb0, fb1);
+    int kt = 1;
+    for (; kt + 1 + C::S < full_slabs; kt += 2) {  // kt and kt+1 steady: kt+1+S < full_slabs
+      step(True{}, False{}, kt, fb1, fb0);
+      step(True{}, False{}, kt + 1, fb0, fb1);
+    }
+    for (; kt + 1 < ktiles; kt += 2) {
+      step(False{}, False{}, kt, fb1, fb0);
+      step(False{}, False{}, kt + 1, fb0, fb1);
+    }
+    if (kt < ktiles) step(False{}, False{}, kt, fb1, fb0);
+    // Every wave is past this tile's last barrier and no fragment read is pending, so the
+    // ring is free unless `pre` already refilled it.
+    if (has_next && !pre) prologue(nxt, dn, (j + 1) & 1);
+
+    // ---- epilogue.  Lane: token row wm*WM + 32 i + (lane & 31); register group g of tile
+    // (i, jj): columns wn*WN + 32 jj + 8 g + 4 half + 0..3.  Outputs are scaled, rounded to
+    // FP16 and staged in an LDS strip, then read back as 16-byte chunks along the rows, so
+    // each store instruction writes whole 128-byte row segments.  Each loader/storer pair
+    // shares one 32-row strip; per 32-row block i the loader stages its rows, and after a
+    // barrier the storer stores them, stages its own rows in the same strip and stores
+    // those; a second barrier frees the strip for the loader's next block.
+    {
+      const float* sc = reinterpret_cast<const float*>(smem + C::SCALE_OFF + (j & 1) * C::SCALE_BYTES);
+      const int partner = loader ? wave : wave - C::LOADERS;
+      uint8_t* strip = smem + C::EPI_OFF + partner * C::STRIP;
+      constexpr int kCpr = C::WN / 8;   // 16-byte chunks per strip row
+      constexpr int kRpt = 64 / kCpr;   // strip rows covered by one 64-lane read
+      int el = lane;                    // opaque copy: addressing is redone per tile, not hoisted
+      asm volatile("" : "+v"(el));
+      const int lr = el / kCpr;         // this lane's strip row (plus kRpt t) and column
+      const int lc = 8 * (el % kCpr);
+      const int erow = el & 31, ehalf = el >> 5;  // MFMA output row and column half
+      const int rows = cur.row_end - cur.row_begin;
+      const bool col_ok = lc < N - cur.n0 - wn * C::WN;
+      const int pwm = partner / C::WGN, pwn = partner % C::WGN;
+      const bool pcol_ok = lc < N - cur.n0 - pwn * C::WN;
+      uint16_t* ytile = p.y + (int64_t)cur.row_begin * N + cur.n0 + lc;
+      // the wave's 32 rows of block i into the strip
+      auto stage = [&](int i) {
+        const float sa = sc[wm * C::WM + 32 * i + erow];
+#pragma unroll
+        for (int jj = 0; jj < C::TJ; ++jj) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int scol = 32 * jj + 8 * g + 4 * ehalf;
+            const v4f sb = *reinterpret_cast<const v4f*>(sc + C::BM + wn * C::WN + scol);
+            const v16f& a = acc[i][jj];
+            uint2 v;
+            v.x = pack_half2((a[4 * g] * sa) * sb[0], (a[4 * g + 1] * sa) * sb[1]);
+            v.y = pack_half2((a[4 * g + 2] * sa) * sb[2], (a[4 * g + 3] * sa) * sb[3]);
+            *reinterpret_cast<uint2*>(strip + erow * C::EPI_STRIDE + 2 * scol) = v;
+          }
+        }
+      };
+      // the strip's 32 rows to output rows row0 + r of wave-tile column block wcol
+      auto drain = [&](int row0, int wcol, bool cok) {
+#pragma unroll
+        for (int t = 0; t < 32 / kRpt; ++t) {
+          const int r = lr + kRpt * t;
+          const uint4 v = *reinterpret_cast<const uint4*>(strip + r * C::EPI_STRIDE + 2 * lc);
+          if (row0 + r < rows && cok) st_global_16(ytile + (int64_t)(row0 + r) * N + wcol, v);
+        }
+      };
+#pragma unroll
+      for (int i = 0; i < C::TI; ++i) {
+        if (loader) stage(i);
+        __syncthreads();
+        if (!loader) {
+          drain(pwm * C::WM + 32 * i, pwn * C::WN, pcol_ok);
+          stage(i);
+          drain(wm * C::WM + 32 * i, wn * C::WN, col_ok);
+        }
+        __syncthreads();
       }
     }
-    interleave_mfma_reads<0, kMfma, kReads, kReadMfmas>();
-  };
+    if (!has_next) break;
+    cur = nxt;
+    dc = dn;
+    rb = pre ? (rb + ktiles) % C::S : 0;
+    wait_read_first(rb);
+  }
+}
 
-  using Steady = std::integral_constant<bool, true>;
-  using Generic = std::integral_constant<bool, false>;
-  const int full_slabs = (int)(K / BK);
-  int kt = 0;
-  for (; kt + 1 + C::S < full_slabs; kt += 2) {  // kt and kt+1 steady: kt+1+S < full_slabs
-    step(Steady{}, kt, fr0, fr1);
-    step(Steady{}, kt + 1, fr1, fr0);
-  }
-  for (; kt + 1 < ktiles; kt += 2) {
-    step(Generic{}, kt, fr0, fr1);
-    step(Generic{}, kt + 1, fr1, fr0);
-  }
-  if (kt < ktiles) step(Generic{}, kt, fr0, fr1);
-  __syncthreads();
+// Workgroups of this kernel the device keeps resident at once (all CUs), cached per device.
+template <class C, bool GROUPED>
+int resident_workgroups() {
+  constexpr int kDevices = 64;
+  static int cache[kDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  const int slot = dev < kDevices ? dev : kDevices - 1;
+  if (cache[slot] > 0) return cache[slot];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_fp8_kernel<C, GROUPED>, C::NT, 0) != hipSuccess ||
+      per_cu <= 0)
+    per_cu = 1;
+  cache[slot] = cus * per_cu;
+  return cache[slot];
+}
 
-  // ---- epilogue: one 32-row strip of the wave tile at a time, staged through LDS.
-  // 32x32 MFMA output layout: lane holds column (lane & 31) and, for register r, row
-  // 8 (r / 4) + 4 (lane / 32) + r % 4.  Strip rows are EPI_STRIDE bytes apart (padded so
-  // the two lane halves hit different banks); read back as 16-byte chunks of 8 columns.
-  // The row and column scales, loaded into registers at kernel start, go to LDS first.
-  uint8_t* strip = smem + wave * C::EPI_BYTES;
-  float* s_sa = reinterpret_cast<float*>(smem + C::WAVES * C::EPI_BYTES);
-  float* s_sb = s_sa + C::BM;
-  if (tid < C::BM) s_sa[tid] = my_sa;
-  if (tid < C::BN) s_sb[tid] = my_sb;
-  __syncthreads();
-  float sbv[C::TJ];
-#pragma unroll
-  for (int j = 0; j < C::TJ; ++j) sbv[j] = s_sb[wn * C::WN + 32 * j + frow];
-  constexpr int kChunksPerRow = C::WN / 8;
-  constexpr int kChunks = 32 * kChunksPerRow;
-#pragma unroll
-  for (int i = 0; i < C::TI; ++i) {
-    const int64_t strip_row0 = t.row_begin + wm * C::WM + 32 * i;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int srow = 8 * (r >> 2) + 4 * half + (r & 3);
-      const float sa = s_sa[wm * C::WM + 32 * i + srow];
-      uint16_t* dst = reinterpret_cast<uint16_t*>(strip + srow * C::EPI_STRIDE) + frow;
-#pragma unroll
-      for (int j = 0; j < C::TJ; ++j) dst[32 * j] = (uint16_t)float_to_half_bits((acc[i][j][r] * sa) * sbv[j]);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int c = lane; c < kChunks; c += 64) {
-      const int srow = c / kChunksPerRow;
-      const int scol = (c % kChunksPerRow) * 8;
-      const int64_t row = strip_row0 + srow;
-      const int64_t col = n0 + wn * C::WN + scol;
-      const uint4 v = *reinterpret_cast<const uint4*>(strip + srow * C::EPI_STRIDE + 2 * scol);
-      if (row < t.row_end && col < N) st_global_16(p.y + row * N + col, v);
-    }
-    __syncthreads();
-  }
+// RQ_GEMM_GRID=n caps the number of persistent workgroups (tests use it to give small
+// problems many tiles per workgroup); unset or invalid: no cap.
+int64_t grid_cap_override() {
+  const char* e = std::getenv("RQ_GEMM_GRID");
+  if (e == nullptr) return 0;
+  const long v = std::strtol(e, nullptr, 10);
+  return v > 0 ? (int64_t)v : 0;
 }
 
 template <class C, bool GROUPED>
 hipError_t launch(const GemmArgs& g, int m_tiles, hipStream_t stream) {
   const int n_tiles = (int)((g.N + C::BN - 1) / C::BN);
-  gemm_fp8_kernel<C, GROUPED><<<dim3(m_tiles * n_tiles), dim3(C::NT), 0, stream>>>(g, m_tiles, n_tiles);
+  const int64_t tiles = (int64_t)m_tiles * n_tiles;  // grouped: the worst case
+  int64_t cap = resident_workgroups<C, GROUPED>();
+  const int64_t forced = grid_cap_override();
+  if (forced > 0 && forced < cap) cap = forced;
+  const int64_t want = (tiles + 7) / 8 * 8;
+  const int64_t grid = want < cap ? want : cap;
+  gemm_fp8_kernel<C, GROUPED><<<dim3((unsigned)grid), dim3(C::NT), 0, stream>>>(g, m_tiles, n_tiles);
   return hipGetLastError();
 }
 
@@ -436,8 +615,8 @@ hipError_t launch(const GemmArgs& g, int m_tiles, hipStream_t stream) {
 using Big = Cfg<256, 256, 4, 2, 4>;      // 128 KB ring, 128x64 per wavefront
 using Wide = Cfg<256, 128, 4, 4, 2>;     // 96 KB ring, 64x64 per wavefront
 using Small = Cfg<128, 128, 4, 2, 2>;    // 64 KB ring, two workgroups per CU
-using Thin = Cfg<64, 128, 4, 1, 4>;      // 48 KB ring, three workgroups per CU
-using ThinWide = Cfg<64, 256, 4, 1, 4>;  // 80 KB ring, two workgroups per CU
+using Thin = Cfg<64, 128, 3, 1, 4>;      // 36 KB ring, three workgroups per CU
+using ThinWide = Cfg<64, 256, 3, 1, 4>;  // 60 KB ring, two workgroups per CU
 
 struct TileDesc {
   const char* name;

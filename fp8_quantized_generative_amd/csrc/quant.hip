@@ -28,6 +28,9 @@
 // h = fl16(silu(g) * u) computed in FP32, so the SiLU, the FP16 rounding of h and the
 // quantization happen in one pass over HBM.
 //
+// MoE rows quantized once per token go straight to each of the token's permuted slots
+// (one copy per routed expert), so the grouped GEMM reads contiguous rows.
+//
 // Memory: each lane owns 16-byte chunks c = lane + 64 j of the row (8 FP16 values),
 // held in registers between the amax reduction and the cast, so the input is read from
 // HBM once; loads and stores are 16- and 8-byte vectors, contiguous across the wave.
@@ -96,7 +99,8 @@ template <int CPL, bool SILU>
 __global__ __launch_bounds__(256) void quant_rows_regs(const uint16_t* __restrict__ x, int64_t rows,
                                                        int K, uint8_t* __restrict__ q,
                                                        float* __restrict__ scale,
-                                                       uint16_t* __restrict__ h_out) {
+                                                       uint16_t* __restrict__ h_out,
+                                                       const int32_t* __restrict__ pos, int fanout) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -123,19 +127,27 @@ __global__ __launch_bounds__(256) void quant_rows_regs(const uint16_t* __restric
   float s, rcp;
   row_scale(amax, s, rcp);
 
-  uint8_t* qr = q + row * (int64_t)K;
+  uint2 out[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int c = lane + 64 * j;
     if (c < nchunk) {
-      uint2 out;
-      out.x = cast4(v[j].x, v[j].y, s, rcp);
-      out.y = cast4(v[j].z, v[j].w, s, rcp);
-      *reinterpret_cast<uint2*>(qr + 8 * c) = out;
+      out[j].x = cast4(v[j].x, v[j].y, s, rcp);
+      out[j].y = cast4(v[j].z, v[j].w, s, rcp);
       if (SILU && h_out != nullptr) st_global_16(h_out + row * (int64_t)K + 8 * c, v[j]);
     }
   }
-  if (lane == 0) scale[row] = s;
+  const int copies = pos != nullptr ? fanout : 1;
+  for (int d = 0; d < copies; ++d) {
+    const int64_t orow = pos != nullptr ? (int64_t)pos[row * fanout + d] : row;
+    uint8_t* qr = q + orow * (int64_t)K;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nchunk) *reinterpret_cast<uint2*>(qr + 8 * c) = out[j];
+    }
+    if (lane == 0) scale[orow] = s;
+  }
 }
 
 // Rows wider than 64 * 8 * 16 values: two passes, the second re-reading the row.
@@ -143,7 +155,8 @@ template <bool SILU>
 __global__ __launch_bounds__(256) void quant_rows_loop(const uint16_t* __restrict__ x, int64_t rows,
                                                        int64_t K, uint8_t* __restrict__ q,
                                                        float* __restrict__ scale,
-                                                       uint16_t* __restrict__ h_out) {
+                                                       uint16_t* __restrict__ h_out,
+                                                       const int32_t* __restrict__ pos, int fanout) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -159,47 +172,52 @@ __global__ __launch_bounds__(256) void quant_rows_loop(const uint16_t* __restric
   amax = wave_max_u32(amax);
   float s, rcp;
   row_scale(amax, s, rcp);
-  uint8_t* qr = q + row * K;
+  const int copies = pos != nullptr ? fanout : 1;
   for (int64_t c = lane; c < nchunk; c += 64) {
     uint4 v = chunk(c);
     uint2 out;
     out.x = cast4(v.x, v.y, s, rcp);
     out.y = cast4(v.z, v.w, s, rcp);
-    *reinterpret_cast<uint2*>(qr + 8 * c) = out;
+    for (int d = 0; d < copies; ++d) {
+      const int64_t orow = pos != nullptr ? (int64_t)pos[row * fanout + d] : row;
+      *reinterpret_cast<uint2*>(q + orow * K + 8 * c) = out;
+    }
     if (SILU && h_out != nullptr) st_global_16(h_out + row * K + 8 * c, v);
   }
-  if (lane == 0) scale[row] = s;
+  for (int d = 0; d < copies && lane == 0; ++d)
+    scale[pos != nullptr ? (int64_t)pos[row * fanout + d] : row] = s;
 }
 
 template <bool SILU>
 hipError_t launch_impl(const uint16_t* x, int64_t rows, int64_t K, uint8_t* q, float* scale,
-                       uint16_t* h, hipStream_t stream) {
+                       uint16_t* h, const int32_t* pos, int fanout, hipStream_t stream) {
   const int64_t nchunk = K / 8;
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
   const dim3 block(64 * kRowsPerBlock);
   const int k = (int)K;
   if (nchunk <= 64)
-    quant_rows_regs<1, SILU><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h);
+    quant_rows_regs<1, SILU><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h, pos, fanout);
   else if (nchunk <= 128)
-    quant_rows_regs<2, SILU><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h);
+    quant_rows_regs<2, SILU><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h, pos, fanout);
   else if (nchunk <= 256)
-    quant_rows_regs<4, SILU><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h);
+    quant_rows_regs<4, SILU><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h, pos, fanout);
   else if (nchunk <= 512)
-    quant_rows_regs<8, SILU><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h);
+    quant_rows_regs<8, SILU><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h, pos, fanout);
   else if (nchunk <= 1024)
-    quant_rows_regs<16, SILU><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h);
+    quant_rows_regs<16, SILU><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h, pos, fanout);
   else
-    quant_rows_loop<SILU><<<grid, block, 0, stream>>>(x, rows, K, q, scale, h);
+    quant_rows_loop<SILU><<<grid, block, 0, stream>>>(x, rows, K, q, scale, h, pos, fanout);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t K, int act, uint8_t* q,
-                             float* scale, uint16_t* h, hipStream_t stream) {
+                             float* scale, uint16_t* h, const int32_t* pos, int fanout,
+                             hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  if (act == 1) return launch_impl<true>(x, rows, K, q, scale, h, stream);
-  return launch_impl<false>(x, rows, K, q, scale, nullptr, stream);
+  if (act == 1) return launch_impl<true>(x, rows, K, q, scale, h, pos, fanout, stream);
+  return launch_impl<false>(x, rows, K, q, scale, nullptr, pos, fanout, stream);
 }
 
 }  // namespace rq

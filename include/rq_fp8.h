@@ -38,7 +38,7 @@
  * FP32 division, q_i = E4M3(fl32(x_i / s)) rounded to nearest even and saturated at
  * +/-448, the sign kept (-0 -> 0x80).
  *
- * Linear: y[m][n] = fl16(fl32(acc[m][n] * s_x[m]) * s_w[n]) with
+ * Linear: y[m][n] = fl16(fl32(fl32(acc[m][n] * s_x[m]) * s_w[n])) with
  * acc = sum_k decode(x_q[m][k]) * decode(w_q[n][k]) accumulated in FP32, rounded to
  * nearest even.  There is no bias.
  */
@@ -136,7 +136,10 @@ size_t rq_fp8_moe_workspace_size(int64_t T, int top_k, int64_t E, int64_t N, int
  * summed in FP32 in slot order, topk_w [T][top_k] FP16 required.
  * Experts with no rows read no weights.  A gate/up + SiLU + down expert FFN is two
  * calls: (TOKENS, NONE, PERMUTED) then (PERMUTED, SILU_MUL, COMBINED).
- * dbg->a_q / a_scale: T rows (TOKENS) or R rows (PERMUTED); dbg->h: R rows. */
+ * TOKENS rows are quantized once per token and the result is written to each of the
+ * token's top_k permuted rows, so the GEMM reads contiguous rows.
+ * dbg->a_q / a_scale: R rows in the permuted order (the GEMM operand, for either input
+ * layout); dbg->h: one row per input row (T for TOKENS, R for PERMUTED). */
 int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act,
                               const int32_t* topk_ids, const uint16_t* topk_w,
                               int64_t T, int top_k,

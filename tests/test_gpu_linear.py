@@ -155,3 +155,19 @@ def test_every_tile_shape(monkeypatch, tile, m, n, k):
     x = workloads.acts_channel_lognormal(rng, m, k)
     w = workloads.weights(rng, (n, k))
     _check(x, w)
+
+
+@pytest.mark.parametrize("grid", ["3", "8"])
+@pytest.mark.parametrize("tile", ["256x256", "256x128", "128x128", "64x128", "64x256"])
+@pytest.mark.parametrize("m,n,k", [(300, 400, 1040), (130, 272, 208), (257, 144, 128), (70, 528, 64)])
+def test_persistent_walk(monkeypatch, grid, tile, m, n, k):
+    """Few workgroups, many tiles each: the LDS ring and the scale areas carried from one
+    tile to the next (K of at least the ring depth), the per-tile restart (shorter K), odd
+    slab counts and ragged K; 3 workgroups walk tiles in plain order, 8 in XCD slices."""
+    case("linear walk grid=%s tile=%s m=%d n=%d k=%d" % (grid, tile, m, n, k))
+    monkeypatch.setenv("RQ_GEMM_TILE", tile)
+    monkeypatch.setenv("RQ_GEMM_GRID", grid)
+    rng = np.random.default_rng(m * 3 + n + k)
+    x = workloads.acts_student_t(rng, m, k)
+    w = workloads.weights(rng, (n, k))
+    _check(x, w)

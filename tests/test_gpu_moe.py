@@ -52,9 +52,11 @@ def _expert_ffn(d, t, k, f, e, top_k, sample=None):
     gu, dbg1 = rq.moe_grouped_linear(x, ids_d, wgu_q, wgu_s, "tokens", "none", "permuted", debug=True)
     gu_h, aq1, as1 = host(gu), host(dbg1["a_q"]), host(dbg1["a_scale"])
     xq, xs = quant.quantize_rows(d["x"])
-    assert np.array_equal(aq1, xq) and np.array_equal(as1.view(np.uint32), xs.view(np.uint32))
-
     counts, offsets, perm, pos = moe.plan(ids, e)
+    # the GEMM operand: permuted row r holds token perm[r] // top_k, quantized once per token
+    tok = perm // top_k
+    assert np.array_equal(aq1, xq[tok]) and np.array_equal(as1.view(np.uint32), xs[tok].view(np.uint32))
+
     rows = np.arange(t * top_k) if sample is None else np.asarray(sample)
     _check_rows_by_expert(gu_h, xq, xs, lambda r: perm[r] // top_k, rows, offsets, wgu_qh, wgu_sh)
 
@@ -129,11 +131,15 @@ def test_moe_full_size_sampled():
     _expert_ffn(d, 16384, 2048, 4096, 32, 2, sample=np.unique(np.array(sample)))
 
 
+@pytest.mark.parametrize("grid", [None, "5", "16"])
 @pytest.mark.parametrize("tile", ["256x256", "64x256", None])
-def test_grouped_tile_shapes(monkeypatch, tile):
-    # 600 tokens, top-2 of 4 experts: about 300 rows per expert (256-row tiles by default)
-    case("moe tile=%s" % tile)
+def test_grouped_tile_shapes(monkeypatch, tile, grid):
+    # 600 tokens, top-2 of 6 experts: about 200 rows per expert (256-row tiles by default);
+    # a capped grid makes each workgroup walk many expert tiles
+    case("moe tile=%s grid=%s" % (tile, grid))
     if tile is not None:
         monkeypatch.setenv("RQ_GEMM_TILE", tile)
-    d = workloads.make(4, t=600, k=128, f=144, e=4)
-    _expert_ffn(d, 600, 128, 144, 4, 2)
+    if grid is not None:
+        monkeypatch.setenv("RQ_GEMM_GRID", grid)
+    d = workloads.make(4, t=600, k=320, f=144, e=6)
+    _expert_ffn(d, 600, 320, 144, 6, 2)
