@@ -39,10 +39,11 @@
 //   walks groups of 8 M-tiles across all N-tiles, so tiles that share A rows or B columns
 //   run on the same XCD at the same time and hit its L2.
 // * Epilogue: each lane scales its four-column groups (FP32 row and column scales read from
-//   LDS) and rounds them to FP16; 32-row strips staged in LDS turn them into 16-byte stores
-//   that write whole 128-byte row segments.
-// * Wavefront roles: half the wavefronts issue every global load and never store, the
-//   other half issue every output store and never wait for loads to land (see the kernel).
+//   LDS) and rounds them to FP16; column groups are paired across the two 32-lane halves
+//   so each lane stores 16 bytes.
+// * Wavefront roles (the 256-row tiles): half the wavefronts issue every global load and
+//   never store, the other half issue every output store (the loaders' outputs reach them
+//   through LDS strips) and never wait for loads to land (see the kernel).
 //
 // Grouped (MoE) mode: the M-tiles are the concatenation over experts of
 // ceil(count_e / BM) tiles each, listed by the routing plan on the device in a table of
@@ -64,7 +65,7 @@ constexpr int kGroupM = 8;
 constexpr int BK = 64;          // K bytes per slab
 constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset that always reads zero
 
-template <int BM_, int BN_, int S_, int WGM_, int WGN_>
+template <int BM_, int BN_, int S_, int WGM_, int WGN_, bool SPLIT_>
 struct Cfg {
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
@@ -79,20 +80,22 @@ struct Cfg {
   static constexpr int TJ = WN / 32;             // ... N direction
   static constexpr int ROWS = BM + BN;           // A rows then B rows in one LDS slab
   static constexpr int STAGE = ROWS * BK;        // bytes per slab
-  // Wavefront roles: waves 0..LOADERS-1 issue every load, waves LOADERS.. every output
-  // store (see the kernel), so no wave ever waits for its stores to retire.
-  static constexpr int LOADERS = WAVES / 2;
+  // Wavefront roles (SPLIT): waves 0..LOADERS-1 issue every load, waves LOADERS.. every
+  // output store (see the kernel), so no wave ever waits for its stores to retire.
+  // Otherwise every wave loads and stores its own outputs.
+  static constexpr bool SPLIT = SPLIT_;
+  static constexpr int LOADERS = SPLIT ? WAVES / 2 : WAVES;
   static constexpr int LOADS = ROWS / 16 / LOADERS;  // direct-to-LDS loads per loader lane per slab
   static constexpr int A_LOADS = BM / 16 / LOADERS;  // the first A_LOADS of them fetch A rows
   static constexpr int SCALE_BYTES = 4 * ROWS;       // BM row scales, then BN column scales
   static constexpr int SCALE_LOADS = ROWS / 64;      // 4-byte-per-lane loads per tile
   static constexpr int EPI_STRIDE = 2 * WN + 16;     // padded FP16 row of an output strip
-  static constexpr int STRIP = 32 * EPI_STRIDE;     // one per loader/storer pair
+  static constexpr int STRIP = 32 * EPI_STRIDE;     // a loader's 32-row output block
   static constexpr int SCALE_OFF = S * STAGE;
   static constexpr int EPI_OFF = SCALE_OFF + 2 * SCALE_BYTES;
-  static constexpr int LDS = EPI_OFF + LOADERS * STRIP;
+  static constexpr int LDS = EPI_OFF + (SPLIT ? LOADERS * STRIP : 0);
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
-  static_assert(WAVES % 2 == 0 && (ROWS / 16) % LOADERS == 0, "whole 16-row load groups per loader");
+  static_assert((!SPLIT || WAVES % 2 == 0) && (ROWS / 16) % LOADERS == 0, "whole 16-row load groups per loader");
   static_assert((BM / 16) % LOADERS == 0, "each load fetches only A rows or only B rows");
   static_assert((16 * WN / 8) % 64 == 0, "whole strip reads per lane");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile of whole 32x32 MFMA tiles");
@@ -293,11 +296,14 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps addressing scalar
   // gfx9 counts loads and stores in one vmcnt per wave, so a wave that stored its outputs
   // would wait for those stores to retire at its next slab wait - with every CU writing its
-  // tile at once, several microseconds.  Loader waves therefore issue all loads and never
-  // store; storer waves issue all output stores (their own rows and their partner loader's,
-  // handed over in LDS) and never wait on vmcnt - the barrier after the loaders' waits
-  // tells them a slab has landed.
-  const bool loader = wave < C::LOADERS;
+  // tile at once, several microseconds.  With SPLIT, loader waves therefore issue all loads
+  // and never store; storer waves issue all output stores (their own rows and their partner
+  // loader's, handed over in LDS) and never wait on vmcnt - the barrier after the loaders'
+  // waits tells them a slab has landed.  Tiles with few MFMAs per slab keep every wave a
+  // loader: there a single wave could not issue a whole slab's loads in the time of its
+  // MFMAs.
+  const bool loader = wave < C::LOADERS;                  // every wave unless SPLIT
+  const bool storer = !C::SPLIT || wave >= C::LOADERS;    // every wave unless SPLIT
   const int K = p.K;
   const int N = p.N;
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
@@ -499,12 +505,12 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
     if (has_next && !pre) prologue(nxt, dn, (j + 1) & 1);
 
     // ---- epilogue.  Lane: token row wm*WM + 32 i + (lane & 31); register group g of tile
-    // (i, jj): columns wn*WN + 32 jj + 8 g + 4 half + 0..3.  Outputs are scaled, rounded to
-    // FP16 and staged in an LDS strip, then read back as 16-byte chunks along the rows, so
-    // each store instruction writes whole 128-byte row segments.  Each loader/storer pair
-    // shares one 32-row strip; per 32-row block i the loader stages its rows, and after a
-    // barrier the storer stores them, stages its own rows in the same strip and stores
-    // those; a second barrier frees the strip for the loader's next block.
+    // (i, jj): columns wn*WN + 32 jj + 8 g + 4 half + 0..3, scaled and rounded to FP16.
+    // Storers store their own blocks straight from registers: a 32-lane swap between column
+    // groups g and g+1 gives each lane 8 consecutive columns (16 bytes) of its row.  With
+    // SPLIT, loaders stage each 32-row block in an LDS strip shared with their storer; after
+    // a barrier the storer reads it back as 16-byte chunks along the rows (whole 128-byte
+    // row segments per store) and stores it; a second barrier frees the strip.
     {
       const float* sc = reinterpret_cast<const float*>(smem + C::SCALE_OFF + (j & 1) * C::SCALE_BYTES);
       const int partner = loader ? wave : wave - C::LOADERS;
@@ -517,46 +523,58 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
       const int lc = 8 * (el % kCpr);
       const int erow = el & 31, ehalf = el >> 5;  // MFMA output row and column half
       const int rows = cur.row_end - cur.row_begin;
-      const bool col_ok = lc < N - cur.n0 - wn * C::WN;
+      const int cols = N - cur.n0;
       const int pwm = partner / C::WGN, pwn = partner % C::WGN;
-      const bool pcol_ok = lc < N - cur.n0 - pwn * C::WN;
-      uint16_t* ytile = p.y + (int64_t)cur.row_begin * N + cur.n0 + lc;
-      // the wave's 32 rows of block i into the strip
-      auto stage = [&](int i) {
-        const float sa = sc[wm * C::WM + 32 * i + erow];
-#pragma unroll
-        for (int jj = 0; jj < C::TJ; ++jj) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int scol = 32 * jj + 8 * g + 4 * ehalf;
-            const v4f sb = *reinterpret_cast<const v4f*>(sc + C::BM + wn * C::WN + scol);
-            const v16f& a = acc[i][jj];
-            uint2 v;
-            v.x = pack_half2((a[4 * g] * sa) * sb[0], (a[4 * g + 1] * sa) * sb[1]);
-            v.y = pack_half2((a[4 * g + 2] * sa) * sb[2], (a[4 * g + 3] * sa) * sb[3]);
-            *reinterpret_cast<uint2*>(strip + erow * C::EPI_STRIDE + 2 * scol) = v;
-          }
-        }
-      };
-      // the strip's 32 rows to output rows row0 + r of wave-tile column block wcol
-      auto drain = [&](int row0, int wcol, bool cok) {
-#pragma unroll
-        for (int t = 0; t < 32 / kRpt; ++t) {
-          const int r = lr + kRpt * t;
-          const uint4 v = *reinterpret_cast<const uint4*>(strip + r * C::EPI_STRIDE + 2 * lc);
-          if (row0 + r < rows && cok) st_global_16(ytile + (int64_t)(row0 + r) * N + wcol, v);
-        }
+      const bool pcol_ok = lc < cols - pwn * C::WN;
+      uint16_t* ytile = p.y + (int64_t)cur.row_begin * N + cur.n0;
+      // FP16 of register group g of tile (i, jj): 4 columns
+      auto group = [&](int i, int jj, int g, float sa) -> uint2 {
+        const v4f sb = *reinterpret_cast<const v4f*>(sc + C::BM + wn * C::WN + 32 * jj + 8 * g + 4 * ehalf);
+        const v16f& a = acc[i][jj];
+        uint2 v;
+        v.x = pack_half2((a[4 * g] * sa) * sb[0], (a[4 * g + 1] * sa) * sb[1]);
+        v.y = pack_half2((a[4 * g + 2] * sa) * sb[2], (a[4 * g + 3] * sa) * sb[3]);
+        return v;
       };
 #pragma unroll
       for (int i = 0; i < C::TI; ++i) {
-        if (loader) stage(i);
-        __syncthreads();
-        if (!loader) {
-          drain(pwm * C::WM + 32 * i, pwn * C::WN, pcol_ok);
-          stage(i);
-          drain(wm * C::WM + 32 * i, wn * C::WN, col_ok);
+        const float sa = sc[wm * C::WM + 32 * i + erow];
+        if (!storer) {
+#pragma unroll
+          for (int jj = 0; jj < C::TJ; ++jj)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              *reinterpret_cast<uint2*>(strip + erow * C::EPI_STRIDE + 2 * (32 * jj + 8 * g + 4 * ehalf)) =
+                  group(i, jj, g, sa);
+        } else {
+          const int lrow = wm * C::WM + 32 * i + erow;
+          uint16_t* yrow = ytile + (int64_t)lrow * N + wn * C::WN + 8 * ehalf;
+#pragma unroll
+          for (int jj = 0; jj < C::TJ; ++jj) {
+#pragma unroll
+            for (int gp = 0; gp < 2; ++gp) {
+              const uint2 x = group(i, jj, 2 * gp, sa), y = group(i, jj, 2 * gp + 1, sa);
+              const auto s0 = __builtin_amdgcn_permlane32_swap(x.x, y.x, false, false);
+              const auto s1 = __builtin_amdgcn_permlane32_swap(x.y, y.y, false, false);
+              const int col = wn * C::WN + 32 * jj + 16 * gp + 8 * ehalf;
+              if (lrow < rows && col < cols)
+                st_global_16(yrow + 32 * jj + 16 * gp, make_uint4(s0[0], s1[0], s0[1], s1[1]));
+            }
+          }
         }
-        __syncthreads();
+        if constexpr (C::SPLIT) {
+          __syncthreads();
+          if (!loader) {
+#pragma unroll
+            for (int t = 0; t < 32 / kRpt; ++t) {
+              const int r = lr + kRpt * t;
+              const uint4 v = *reinterpret_cast<const uint4*>(strip + r * C::EPI_STRIDE + 2 * lc);
+              const int orow = pwm * C::WM + 32 * i + r;
+              if (orow < rows && pcol_ok) st_global_16(ytile + (int64_t)orow * N + pwn * C::WN + lc, v);
+            }
+          }
+          __syncthreads();
+        }
       }
     }
     if (!has_next) break;
@@ -612,11 +630,11 @@ hipError_t launch(const GemmArgs& g, int m_tiles, hipStream_t stream) {
 // Measured on MI355X: +8% (256x256) and +5% (256x128) over four wavefronts of twice the
 // tile each.  The 64-row tiles serve small M (the weight-streaming regime) and MoE experts
 // with few rows, where 256-row tiles would spend most MFMA work on padding.
-using Big = Cfg<256, 256, 4, 2, 4>;      // 128 KB ring, 128x64 per wavefront
-using Wide = Cfg<256, 128, 4, 4, 2>;     // 96 KB ring, 64x64 per wavefront
-using Small = Cfg<128, 128, 4, 2, 2>;    // 64 KB ring, two workgroups per CU
-using Thin = Cfg<64, 128, 3, 1, 4>;      // 36 KB ring, three workgroups per CU
-using ThinWide = Cfg<64, 256, 3, 1, 4>;  // 60 KB ring, two workgroups per CU
+using Big = Cfg<256, 256, 4, 2, 4, true>;       // 128 KB ring, 128x64 per wavefront
+using Wide = Cfg<256, 128, 4, 4, 2, true>;      // 96 KB ring, 64x64 per wavefront
+using Small = Cfg<128, 128, 4, 2, 2, false>;    // 64 KB ring, two workgroups per CU
+using Thin = Cfg<64, 128, 4, 1, 4, false>;      // 48 KB ring, three workgroups per CU
+using ThinWide = Cfg<64, 256, 4, 1, 4, false>;  // 80 KB ring, two workgroups per CU
 
 struct TileDesc {
   const char* name;
