@@ -49,7 +49,39 @@ def parse():
                          "(a *_results.db, a *_kernel_trace.csv, or a directory holding one) and exit")
     ap.add_argument("--only", default=None,
                     help="comma list of attention,ffn,moe,layer_small_m to restrict the step (profiling)")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0, metavar="MB",
+                    help="after the timed steps, one device-to-device copy of MB MiB (the known-size kernel "
+                         "that scales HBM byte counters)")
+    ap.add_argument("--traffic-summary", nargs=3, default=None, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
+                    help="from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of a bench command with "
+                         "--calibrate-copy-mb, write the dominant kernel's HBM traffic per launch to OUT (json)")
+    ap.add_argument("--steps-in-profile", type=int, default=None,
+                    help="with --rocprof-summary / --traffic-summary: steps (warmup + timed) the profiled "
+                         "command ran")
     return ap.parse_args()
+
+
+# Calls of one step, in launch order: (workload, call, kind).  "linear" launches the row
+# quantizer and the GEMM; "moe" the three routing-plan kernels, the quantizer and the
+# grouped GEMM; "moe_combined" also the weighted combine.
+STEP = [
+    ("attention", "qkv", "linear"), ("attention", "o", "linear"),
+    ("ffn", "gate_up", "linear"), ("ffn", "down", "linear"),
+    ("moe", "gate_up", "moe"), ("moe", "down", "moe_combined"),
+    ("layer_small_m", "qkv", "linear"), ("layer_small_m", "o", "linear"),
+    ("layer_small_m", "gate_up", "linear"), ("layer_small_m", "down", "linear"),
+    ("layer_small_m", "moe_gate_up", "moe"), ("layer_small_m", "moe_down", "moe_combined"),
+]
+DOMINANT = ("moe", "gate_up")
+KERNELS = {"linear": ["quant", "gemm"], "moe": ["plan_hist", "plan_scan", "plan_scatter", "quant", "gemm"],
+           "moe_combined": ["plan_hist", "plan_scan", "plan_scatter", "quant", "gemm", "combine"]}
+OUR_KERNELS = ("quant_rows", "gemm_fp8_kernel", "plan_hist", "plan_scan", "plan_scatter", "combine_kernel")
+
+
+def step_dispatches(only):
+    """(label, kind) of every kernel one step launches, in order."""
+    want = set(only.split(",")) if only else {w for w, _, _ in STEP}
+    return [("%s %s" % (w, c), k) for w, c, kind in STEP if w in want for k in KERNELS[kind]]
 
 
 class Hip:
@@ -235,19 +267,25 @@ def cpu_baseline(seconds_hint=15.0):
                       "float64 exact GEMMs; weights quantized beforehand (untimed)"}
 
 
-def _rocprof_rows(path):
-    """(kernel name, grid threads, workgroup threads, duration ns) for every dispatch."""
+def _find(path, patterns):
     import glob
-    import sqlite3
-    if os.path.isdir(path):
-        found = sorted(glob.glob(os.path.join(path, "**", "*_results.db"), recursive=True) +
-                       glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True))
-        if not found:
-            raise SystemExit("no rocprofv3 output under %s" % path)
-        path = found[0]
+    if not os.path.isdir(path):
+        return path
+    for pat in patterns:
+        found = sorted(glob.glob(os.path.join(path, "**", pat), recursive=True))
+        if found:
+            return found[0]
+    raise SystemExit("no rocprofv3 output (%s) under %s" % (", ".join(patterns), path))
+
+
+def _rocprof_rows(path):
+    """(kernel name, grid threads, workgroup threads, duration ns) of every dispatch, in launch order."""
+    path = _find(path, ["*_results.db", "*kernel_trace.csv"])
     if path.endswith(".db"):
+        import sqlite3
         db = sqlite3.connect(path)
-        q = "select name, grid_x * grid_y * grid_z, workgroup_x * workgroup_y * workgroup_z, duration from kernels"
+        q = ("select name, grid_x * grid_y * grid_z, workgroup_x * workgroup_y * workgroup_z, duration "
+             "from kernels order by start")
         return path, [(r[0], int(r[1]), int(r[2]), int(r[3])) for r in db.execute(q)]
     import csv
     rows = []
@@ -255,30 +293,158 @@ def _rocprof_rows(path):
         for r in csv.DictReader(f):
             grid = int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1)) * int(r.get("Grid_Size_Z", 1))
             wg = int(r["Workgroup_Size_X"]) * int(r.get("Workgroup_Size_Y", 1)) * int(r.get("Workgroup_Size_Z", 1))
-            rows.append((r["Kernel_Name"], grid, wg, int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
-    return path, rows
+            rows.append((int(r["Start_Timestamp"]), r["Kernel_Name"], grid, wg,
+                         int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    rows.sort()
+    return path, [r[1:] for r in rows]
 
 
-def rocprof_summary(path):
+_KIND_TOKEN = {"quant": "quant_rows", "gemm": "gemm_fp8_kernel", "plan_hist": "plan_hist",
+               "plan_scan": "plan_scan", "plan_scatter": "plan_scatter", "combine": "combine_kernel"}
+
+
+def _align_steps(names, only, steps):
+    """Indices (into names) of the dispatches of the last `steps` steps, with their labels.
+
+    names: kernel names in launch order.  Only this library's kernels are considered; the
+    step's kernel sequence is matched backwards from the last one (after the timed steps the
+    profiled command launches none of them)."""
+    seq = step_dispatches(only)
+    ours = [i for i, n in enumerate(names) if any(k in n for k in OUR_KERNELS)]
+    period = len(seq)
+    if steps is None:
+        steps = 0
+        while (steps + 1) * period <= len(ours):
+            block = ours[len(ours) - (steps + 1) * period:len(ours) - steps * period]
+            if not all(_KIND_TOKEN[seq[j][1]] in names[block[j]] for j in range(period)):
+                break
+            steps += 1
+    if steps <= 0 or steps * period > len(ours):
+        raise SystemExit("could not find the step's kernel sequence in the profile")
+    picked = ours[len(ours) - steps * period:]
+    out = []
+    for j, idx in enumerate(picked):
+        label, kind = seq[j % period]
+        if _KIND_TOKEN[kind] not in names[idx]:
+            raise SystemExit("dispatch %d (%s) does not match %s %s" % (idx, names[idx], label, kind))
+        out.append((idx, label, kind))
+    return out, steps
+
+
+def rocprof_summary(path, only=None, steps=None):
     src, rows = _rocprof_rows(path)
+    names = [r[0] for r in rows]
+    aligned, nsteps = _align_steps(names, only, steps)
     groups = {}
-    for name, grid, wg, dur in rows:
-        groups.setdefault((name, grid // max(wg, 1)), []).append(dur)
-    total = sum(d for v in groups.values() for d in v)
-    print("# rocprofv3 kernel trace: %s" % os.path.basename(src))
-    print("# %-72s %9s %6s %11s %11s %11s %6s" % ("kernel", "workgroups", "calls", "avg_us", "min_us", "max_us", "pct"))
-    for (name, nwg), durs in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
-        short = name.replace("rq::(anonymous namespace)::", "").replace("unsigned short", "u16")
-        short = short.split("(")[0] if len(short) > 72 else short
-        print("  %-72s %9d %6d %11.2f %11.2f %11.2f %5.1f%%" % (
-            short[:72], nwg, len(durs), np.mean(durs) / 1e3, min(durs) / 1e3, max(durs) / 1e3,
-            100.0 * sum(durs) / total))
+    for idx, label, kind in aligned:
+        groups.setdefault((label, kind), []).append(rows[idx][3])
+    step_ns = sum(sum(v) for v in groups.values()) / nsteps
+    print("# rocprofv3 kernel trace: %s (%d steps matched)" % (os.path.basename(src), nsteps))
+    print("# sum of kernel durations per step: %.1f us" % (step_ns / 1e3))
+    print("# %-28s %-13s %6s %10s %10s %10s %6s" % ("call", "kernel", "calls", "avg_us", "min_us", "max_us", "pct"))
+    for (label, kind), durs in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        print("  %-28s %-13s %6d %10.2f %10.2f %10.2f %5.1f%%" % (
+            label, kind, len(durs), np.mean(durs) / 1e3, min(durs) / 1e3, max(durs) / 1e3,
+            100.0 * sum(durs) / (step_ns * nsteps)))
+    dom = groups.get(("%s %s" % DOMINANT, "gemm"))
+    if dom:
+        print("# dominant launch (%s %s grouped GEMM): avg %.2f us over %d calls" % (
+            DOMINANT[0], DOMINANT[1], np.mean(dom) / 1e3, len(dom)))
+
+
+def _pmc_rows(path, counter):
+    """(kernel name, counter value summed over the dispatch's instances) per dispatch, in order."""
+    import csv
+    path = _find(path, ["*counter_collection.csv"])
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            name, v = per.get(d, (r["Kernel_Name"], 0.0))
+            per[d] = (name, v + float(r["Counter_Value"]))
+    return [per[d] for d in sorted(per)]
+
+
+def gemm_source_hash():
+    """Hash of the GEMM kernel's sources: stored traffic counters are valid only for this code."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h"):
+        with open(os.path.join(ROOT, "fp8_quantized_generative_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def dominant_algorithmic_bytes():
+    """Bytes the MoE gate/up grouped GEMM must move at least once: its FP8 A rows (one per
+    routed slot) and expert weights, the FP32 scales, and its FP16 output."""
+    t, k, f, e, top_k = 16384, 2048, 4096, 32, 2
+    r, n = t * top_k, 2 * f
+    return r * k + e * n * k + 4 * (r + e * n) + 2 * r * n
+
+
+def traffic_summary(fetch_dir, write_dir, out, only=None, steps=None):
+    result = {"kernel": "gemm_fp8_kernel (grouped, 256x256) for the %s %s call" % DOMINANT,
+              "source_sha256_16": gemm_source_hash()}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _pmc_rows(d, counter)
+        names = [r[0] for r in rows]
+        aligned, nsteps = _align_steps(names, only, steps)
+        dom = [rows[i][1] for i, label, kind in aligned if label == "%s %s" % DOMINANT and kind == "gemm"]
+        last = max(i for i, _, _ in aligned)
+        copies = [r for r in rows[last + 1:] if not any(k in r[0] for k in OUR_KERNELS)]
+        if not dom or not copies:
+            raise SystemExit("%s: dominant launch or calibration copy not found" % counter)
+        copy_kib = copies[-1][1]
+        result[counter.lower() + "_kib_per_launch"] = round(float(np.mean(dom)), 1)
+        result[counter.lower() + "_launches"] = len(dom)
+        result["copy_" + counter.lower() + "_kib"] = round(copy_kib, 1)
+        result["copy_kernel"] = copies[-1][0][:120]
+    return result
+
+
+def finish_traffic(result, copy_mib, out):
+    copy_bytes = copy_mib * 1024 * 1024
+    result["copy_mib"] = copy_mib
+    f_fac = result["copy_fetch_size_kib"] * 1024 / copy_bytes
+    w_fac = result["copy_write_size_kib"] * 1024 / copy_bytes
+    result["fetch_factor"] = round(f_fac, 4)
+    result["write_factor"] = round(w_fac, 4)
+    traffic = (result["fetch_size_kib_per_launch"] * 1024 / f_fac +
+               result["write_size_kib_per_launch"] * 1024 / w_fac)
+    result["traffic_bytes_per_launch"] = int(traffic)
+    result["algorithmic_bytes_per_launch"] = dominant_algorithmic_bytes()
+    result["traffic_over_algorithmic"] = round(traffic / dominant_algorithmic_bytes(), 3)
+    with open(out, "w") as f:
+        json.dump(result, f, indent=1)
+    print(json.dumps(result, indent=1))
+
+
+def stored_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter summary, or None
+    when it is missing or was taken on different GEMM sources."""
+    p = os.path.join(ROOT, "profiles", "gemm_fp8_grouped_moe_gate_up_traffic.json")
+    try:
+        with open(p) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256_16") != gemm_source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
 
 
 def main():
     args = parse()
     if args.rocprof_summary:
-        rocprof_summary(args.rocprof_summary)
+        rocprof_summary(args.rocprof_summary, args.only, args.steps_in_profile)
+        return
+    if args.traffic_summary:
+        fetch_dir, write_dir, out = args.traffic_summary
+        res = traffic_summary(fetch_dir, write_dir, out, args.only, args.steps_in_profile)
+        finish_traffic(res, args.calibrate_copy_mb or 512, out)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode (run with --gpus 1)",
@@ -314,7 +480,8 @@ def main():
     dom_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in evs]))
     achieved = dom[3] / (dom_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": stored_traffic(),
+                "algorithmic_bytes": dominant_algorithmic_bytes(),
                 "kernel": "gemm_fp8_kernel<grouped> (%s %s)" % (dom[0], dom[1]),
                 "flops_per_launch": dom[3], "avg_launch_us": round(dom_ms * 1e3, 2)}
 
@@ -329,6 +496,18 @@ def main():
                    **path.config, "gflop_per_step": round(path.flops / 1e9, 2)},
         "roofline": roofline,
     }
+    if args.calibrate_copy_mb:
+        # an elementwise kernel that reads and writes exactly n bytes (a plain copy, x * 1)
+        # an elementwise kernel that reads and writes exactly n bytes (a plain copy, x * 1); a
+        # 1 GiB write in between evicts the source from the 256 MB last-level cache first
+        n = args.calibrate_copy_mb * 1024 * 1024
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(2.0)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst, flush
     if not args.no_kernels:
         print("[bench] per-kernel breakdown", file=sys.stderr, flush=True)
         result["kernels"] = kernel_breakdown(path, hip)

@@ -1,0 +1,62 @@
+"""Host-side logic of bench.py: the step's dispatch table, matching a profile's kernel
+sequence to calls, the traffic scaling, and the one-GPU contract.  No GPU needed."""
+
+import json
+import subprocess
+import sys
+
+import pytest
+
+import bench
+
+
+def _names(only=None, steps=2, prefix=("quant_rows_regs<4, false>", "at::native::fill")):
+    tok = {"quant": "void rq::quant_rows_regs<8, false>(...)", "gemm": "void rq::gemm_fp8_kernel<Cfg>(...)",
+           "plan_hist": "rq::plan_hist(...)", "plan_scan": "rq::plan_scan(...)",
+           "plan_scatter": "rq::plan_scatter(...)", "combine": "rq::combine_kernel(...)"}
+    seq = [tok[k] for _, k in bench.step_dispatches(only)]
+    return list(prefix) + seq * steps + ["at::native::vectorized_elementwise_kernel (copy)"]
+
+
+def test_step_table_matches_workloads():
+    seq = bench.step_dispatches(None)
+    # 8 linears x 2 kernels, 2 uncombined MoE calls x 5, 2 combined x 6
+    assert len(seq) == 8 * 2 + 2 * 5 + 2 * 6
+    assert ("moe gate_up", "gemm") in seq
+    assert len(bench.step_dispatches("moe")) == 11
+
+
+def test_align_finds_every_step_and_labels():
+    names = _names(steps=3)
+    aligned, n = bench._align_steps(names, None, None)
+    assert n == 3
+    labels = [(label, kind) for _, label, kind in aligned]
+    assert labels == bench.step_dispatches(None) * 3
+    # the weight-quantization dispatch before the steps is not picked
+    assert min(i for i, _, _ in aligned) == 2
+
+
+def test_align_rejects_a_foreign_sequence():
+    names = ["rq::plan_scan(...)"] * 5
+    with pytest.raises(SystemExit):
+        bench._align_steps(names, None, None)
+
+
+def test_traffic_scaling(tmp_path):
+    res = {"fetch_size_kib_per_launch": 1000.0, "write_size_kib_per_launch": 300.0,
+           "copy_fetch_size_kib": 256.0 * 1024, "copy_write_size_kib": 512.0 * 1024}
+    out = tmp_path / "t.json"
+    bench.finish_traffic(res, 512, str(out))
+    t = json.loads(out.read_text())
+    assert t["fetch_factor"] == 0.5 and t["write_factor"] == 1.0
+    assert t["traffic_bytes_per_launch"] == int(1000 * 1024 / 0.5 + 300 * 1024)
+
+
+def test_algorithmic_bytes_of_the_dominant_call():
+    r, k, n, e = 32768, 2048, 8192, 32
+    assert bench.dominant_algorithmic_bytes() == r * k + e * n * k + 4 * (r + e * n) + 2 * r * n
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    p = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True)
+    assert p.returncode == 2 and "one GPU" in p.stderr
