@@ -328,10 +328,10 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
   auto wave_lds = [&](int buf) -> uint32_t {
     return (uint32_t)__builtin_amdgcn_readfirstlane((int)(smem_lds + buf * C::STAGE + wave * 16 * BK));
   };
-  // Full slab (all 64 K bytes in range): the K offset travels in the scalar soffset.
-  auto issue_full = [&](const TileDesc2& d, int slab, uint32_t lds, int i) {
-    load_lds_16(i < C::A_LOADS ? d.a : d.b, voff[i], (uint32_t)__builtin_amdgcn_readfirstlane(slab * BK), lds,
-                16 * BK * C::LOADERS * i);
+  // Full slab (all 64 K bytes in range): the K offset (soff = slab * 64) travels in the
+  // scalar soffset.
+  auto issue_full = [&](const TileDesc2& d, uint32_t soff, uint32_t lds, int i) {
+    load_lds_16(i < C::A_LOADS ? d.a : d.b, voff[i], soff, lds, 16 * BK * C::LOADERS * i);
   };
   // Any slab, including the ragged last one: granules past K read zero.
   auto issue_one = [&](const TileDesc2& d, int slab, uint32_t lds, int i) {
@@ -364,6 +364,7 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
   const int half = lane >> 5;
   const int f_off[2] = {frow * BK + 16 * swz(frow, 2 * half), frow * BK + 16 * swz(frow, 2 * half + 1)};
   constexpr int kMfma = C::TI * C::TJ;
+  constexpr int kDmaGroups = kMfma < 2 ? kMfma : 2;
   // Fragment r (= 2 f + h) of the A (or B) rows of a slab: half h of 32-row fragment f.
   auto read_a = [&](const uint8_t* S, int r) -> uint4 {
     return *reinterpret_cast<const uint4*>(S + (wm * C::WM + 32 * (r >> 1)) * BK + f_off[r & 1]);
@@ -436,13 +437,17 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
     // no run-time conditions and no vector address arithmetic; the generic step handles the
     // last slabs, a ragged K and the fetches for the next tile.  The first step of a tile
     // starts its accumulators from zero.
-    auto step = [&](auto steady, auto first_step, int kt, uint4 (&bc)[2 * C::TJ], uint4 (&bn)[2 * C::TJ]) {
+    // `role`: 0 decided at run time, 1 a loader, 2 not a loader.
+    auto step = [&](auto steady, auto first_step, auto role, int kt, uint4 (&bc)[2 * C::TJ],
+                    uint4 (&bn)[2 * C::TJ]) {
       constexpr bool kSteady = decltype(steady)::value;
       constexpr bool kFirst = decltype(first_step)::value;
+      constexpr int kRole = decltype(role)::value;
+      const bool loads = kRole == 1 || (kRole == 0 && loader);
       bool has_read = true;
       int fetch = 1;  // 0: nothing, 1: slab kt+S of this tile, 2: slab kt+S-ktiles of the next
       if constexpr (kSteady) {
-        if (loader) wait_vmcnt_lgkm0<(C::S - 2) * C::LOADS>();
+        if (loads) wait_vmcnt_lgkm0<(C::S - 2) * C::LOADS>();
         else wait_lgkm0();
       } else {
         if (loader) wait_slabs<C::LOADS, C::S - 2, true>(lim - kt - 2);  // slabs issued after kt+1
@@ -451,8 +456,10 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
         fetch = !loader ? 0 : kt + C::S < ktiles ? 1 : (pre ? 2 : 0);
       }
       __syncthreads();
-      const uint8_t* Sn = smem + ((rb + kt + 1) % C::S) * C::STAGE;
-      const uint32_t lds_dst = wave_lds((rb + kt) % C::S);
+      const unsigned slot = (unsigned)(rb + kt);  // ring buffer of slab kt
+      const uint8_t* Sn = smem + ((slot + 1) % C::S) * C::STAGE;
+      const uint32_t lds_dst = wave_lds(slot % C::S);
+      const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane((kt + C::S) * BK);
       if (!kSteady && fetch == 2 && kt + C::S == ktiles) issue_scales(nxt, (j + 1) & 1);
       int l = 0;
 #pragma unroll
@@ -474,10 +481,15 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
             fa[2 * i + 1] = read_a(Sn, 2 * i + 1);
           }
         }
-        const int l_end = (q + 1) * C::LOADS / kMfma;
+        // the slab's loads go out in kDmaGroups bursts after the first MFMAs (one role test
+        // per burst)
+        const int l_end = q < kDmaGroups ? (q + 1) * C::LOADS / kDmaGroups : C::LOADS;
+        if constexpr (kSteady) {
+          if (l < l_end && loads)
+            for (; l < l_end; ++l) issue_full(dc, soff, lds_dst, l);
+        }
         for (; l < l_end; ++l) {
           if constexpr (kSteady) {
-            if (loader) issue_full(dc, kt + C::S, lds_dst, l);
           } else if (fetch != 0) {
             const bool nx = fetch == 2;
             issue_one(TileDesc2{pick(nx, dn.a, dc.a), pick(nx, dn.b, dc.b)}, nx ? kt + C::S - ktiles : kt + C::S,
@@ -488,18 +500,19 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
       interleave_mfma_reads<0, kMfma, C::TJ>();
     };
 
-    if (C::S < full_slabs) step(True{}, True{}, 0, fb0, fb1);
-    else step(False{}, True{}, 0, fb0, fb1);
+    using Any = std::integral_constant<int, 0>;
+    if (C::S < full_slabs) step(True{}, True{}, Any{}, 0, fb0, fb1);
+    else step(False{}, True{}, Any{}, 0, fb0, fb1);
     int kt = 1;
     for (; kt + 1 + C::S < full_slabs; kt += 2) {  // kt and kt+1 steady: kt+1+S < full_slabs
-      step(True{}, False{}, kt, fb1, fb0);
-      step(True{}, False{}, kt + 1, fb0, fb1);
+      step(True{}, False{}, Any{}, kt, fb1, fb0);
+      step(True{}, False{}, Any{}, kt + 1, fb0, fb1);
     }
     for (; kt + 1 < ktiles; kt += 2) {
-      step(False{}, False{}, kt, fb1, fb0);
-      step(False{}, False{}, kt + 1, fb0, fb1);
+      step(False{}, False{}, Any{}, kt, fb1, fb0);
+      step(False{}, False{}, Any{}, kt + 1, fb0, fb1);
     }
-    if (kt < ktiles) step(False{}, False{}, kt, fb1, fb0);
+    if (kt < ktiles) step(False{}, False{}, Any{}, kt, fb1, fb0);
     // Every wave is past this tile's last barrier and no fragment read is pending, so the
     // ring is free unless `pre` already refilled it.
     if (has_next && !pre) prologue(nxt, dn, (j + 1) & 1);
