@@ -11,7 +11,8 @@
 //                    integer counts, so the result is deterministic);
 //   2. plan_scan:    one workgroup turns the block histograms into per-expert offsets,
 //                    per-(block, expert) base rows, the per-expert M-tile prefix sum and
-//                    the M-tile table {expert, first row, end row} the grouped GEMM reads;
+//                    the M-tile table {expert, first row, end row} the grouped GEMM reads,
+//                    with every thread busy (segment sums, LDS scans, one table entry each);
 //   3. plan_scatter: each slot's rank among equal experts inside its wavefront comes from
 //                    ballots over the bits of the expert id; ranks across the block's 16
 //                    wavefronts come from an LDS prefix; perm[row] = j and pos[j] = row.
@@ -71,43 +72,82 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_sums, int& 
   return wave_sums[wave] + incl - v;
 }
 
+// One workgroup turns the [nb][E] block histograms into per-expert offsets and M-tile
+// prefixes, the M-tile table, and per-(block, expert) base rows.  The blocks are split into
+// G contiguous segments (G groups of E threads, consecutive threads on consecutive experts
+// so every load is coalesced): each group sums its segment, the segment sums are scanned
+// per expert in LDS, and each group then rewrites its segment with running base rows.
 __global__ __launch_bounds__(kPlanThreads) void plan_scan(int32_t* __restrict__ block_hist, int nblocks, int E,
                                                           int tile_m, int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ tile_start,
                                                           int32_t* __restrict__ tile_table) {
   __shared__ int wave_sums[kPlanWaves + 1];
-  const int e = threadIdx.x;  // E <= 1024
-  int count = 0;
-  if (e < E)
-    for (int b = 0; b < nblocks; ++b) count += block_hist[(int64_t)b * E + e];
-  int total_rows, total_tiles;
-  const int off = block_exclusive_scan(e < E ? count : 0, wave_sums, total_rows);
+  __shared__ int seg[kPlanThreads];        // [G][E] segment sums, then their exclusive scans
+  __shared__ int s_tstart[kPlanThreads + 1];
+  __shared__ int s_off[kPlanThreads];
+  const int tid = threadIdx.x;
+  const int groups = kPlanThreads / E;     // E <= 1024
+  const int g = tid / E, e = tid % E;
+  const bool active = g < groups;
+  const int per = (nblocks + groups - 1) / groups;
+  const int b0 = active ? g * per : 0;
+  const int b1 = active ? min(nblocks, b0 + per) : 0;
+  int sum = 0;
+  for (int b = b0; b < b1; ++b) sum += block_hist[(int64_t)b * E + e];
+  if (active) seg[tid] = sum;
   __syncthreads();
-  const int tiles = e < E ? (count + tile_m - 1) / tile_m : 0;
-  const int tstart = block_exclusive_scan(tiles, wave_sums, total_tiles);
-  if (e < E) {
-    offsets[e] = off;
-    tile_start[e] = tstart;
-    // one {expert, first row, end row} entry per M-tile, so a GEMM workgroup finds its
-    // tile with a single load
-    for (int t = 0; t < tiles; ++t) {
-      int32_t* ent = tile_table + 4 * (int64_t)(tstart + t);
-      const int lo = off + t * tile_m;
-      ent[0] = e;
-      ent[1] = lo;
-      ent[2] = lo + tile_m < off + count ? lo + tile_m : off + count;
-      ent[3] = 0;
+  // per-expert totals and exclusive scan over the segments (thread e walks its column)
+  int count = 0;
+  if (tid < E) {
+    for (int gg = 0; gg < groups; ++gg) {
+      const int c = seg[gg * E + tid];
+      seg[gg * E + tid] = count;
+      count += c;
     }
-    int run = off;
-    for (int b = 0; b < nblocks; ++b) {
+  }
+  __syncthreads();
+  int total_rows, total_tiles;
+  const int off = block_exclusive_scan(tid < E ? count : 0, wave_sums, total_rows);
+  __syncthreads();
+  const int tiles = tid < E ? (count + tile_m - 1) / tile_m : 0;
+  const int tstart = block_exclusive_scan(tiles, wave_sums, total_tiles);
+  if (tid < E) {
+    offsets[tid] = off;
+    tile_start[tid] = tstart;
+    s_tstart[tid] = tstart;
+    s_off[tid] = off;
+  }
+  if (tid == 0) {
+    offsets[E] = total_rows;
+    tile_start[E] = total_tiles;
+    s_tstart[E] = total_tiles;
+  }
+  __syncthreads();
+  // base row of (block b, expert e) = offset of e + rows of e in earlier blocks
+  if (active) {
+    int run = s_off[e] + seg[tid];
+    for (int b = b0; b < b1; ++b) {
       const int c = block_hist[(int64_t)b * E + e];
-      block_hist[(int64_t)b * E + e] = run;  // becomes the base row of (block b, expert e)
+      block_hist[(int64_t)b * E + e] = run;
       run += c;
     }
   }
-  if (e == 0) {
-    offsets[E] = total_rows;
-    tile_start[E] = total_tiles;
+  // one {expert, first row, end row} entry per M-tile, so a GEMM tile finds its rows with
+  // one load; the expert of tile t is found by binary search over the tile prefix
+  for (int t = tid; t < total_tiles; t += kPlanThreads) {
+    int lo = 0, hi = E - 1;  // largest x with s_tstart[x] <= t
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_tstart[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int ex = lo;
+    const int first = s_off[ex] + (t - s_tstart[ex]) * tile_m;
+    const int end_e = ex + 1 < E ? s_off[ex + 1] : total_rows;
+    int32_t* ent = tile_table + 4 * (int64_t)t;
+    ent[0] = ex;
+    ent[1] = first;
+    ent[2] = first + tile_m < end_e ? first + tile_m : end_e;
+    ent[3] = 0;
   }
 }
 
