@@ -31,9 +31,10 @@
 // MoE rows quantized once per token go straight to each of the token's permuted slots
 // (one copy per routed expert), so the grouped GEMM reads contiguous rows.
 //
-// Memory: each lane owns 16-byte chunks c = lane + 64 j of the row (8 FP16 values),
-// held in registers between the amax reduction and the cast, so the input is read from
-// HBM once; loads and stores are 16- and 8-byte vectors, contiguous across the wave.
+// Memory: each lane owns 16-byte chunks of the row (8 FP16 values), held in registers
+// between the amax reduction and the cast, so the input is read from HBM once; loads and
+// stores are 16- and 8-byte vectors, contiguous across the wave.  A row is one wavefront's,
+// or is split over 2 or 4 wavefronts when there are few rows.
 // Rows wider than 8192 values fall back to a two-pass loop that re-reads the row.
 
 #include "common.h"
@@ -95,26 +96,36 @@ __device__ __forceinline__ void row_scale(uint32_t amax_bits, float& s, float& r
   rcp = __fdiv_rn(1.0f, s);
 }
 
-template <int CPL, bool SILU>
+// One row per SPLIT wavefronts (SPLIT = 1, 2 or 4; 4 wavefronts per workgroup): lane l of
+// wavefront part p owns chunks c = 64 p + l + 64 SPLIT j, j < CPL.  Splitting a long row over
+// several wavefronts keeps enough of them in flight when there are few rows; their partial
+// maxima meet in LDS.
+template <int CPL, bool SILU, int SPLIT>
 __global__ __launch_bounds__(256) void quant_rows_regs(const uint16_t* __restrict__ x, int64_t rows,
                                                        int K, uint8_t* __restrict__ q,
                                                        float* __restrict__ scale,
                                                        uint16_t* __restrict__ h_out,
                                                        const int32_t* __restrict__ pos, int fanout) {
+  static_assert(SPLIT == 1 || SPLIT == 2 || SPLIT == 4, "wavefronts per row");
+  __shared__ uint32_t part_max[kRowsPerBlock];
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  const int wave = threadIdx.x >> 6;
+  const int part = wave % SPLIT;
+  const int64_t row = (int64_t)blockIdx.x * (kRowsPerBlock / SPLIT) + wave / SPLIT;
+  const bool valid = row < rows;
+  if (SPLIT == 1 && !valid) return;
   const int nchunk = K >> 3;
   const int64_t in_stride = SILU ? 2 * (int64_t)K : (int64_t)K;
-  const uint16_t* xr = x + row * in_stride;
+  const uint16_t* xr = x + (valid ? row : 0) * in_stride;
+  const int c0 = 64 * part + lane;
 
   uint4 v[CPL];
   uint32_t amax = 0;
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
-    const int c = lane + 64 * j;
+    const int c = c0 + 64 * SPLIT * j;
     v[j] = make_uint4(0, 0, 0, 0);
-    if (c < nchunk) {
+    if (valid && c < nchunk) {
       if (SILU) {
         v[j] = silu_mul8(ld_global_16(xr + 8 * c), ld_global_16(xr + K + 8 * c));
       } else {
@@ -124,13 +135,21 @@ __global__ __launch_bounds__(256) void quant_rows_regs(const uint16_t* __restric
     }
   }
   amax = wave_max_u32(amax);
+  if (SPLIT > 1) {
+    if (lane == 0) part_max[wave] = amax;
+    __syncthreads();
+    const int first = wave - part;
+#pragma unroll
+    for (int p2 = 0; p2 < SPLIT; ++p2) amax = amax > part_max[first + p2] ? amax : part_max[first + p2];
+    if (!valid) return;
+  }
   float s, rcp;
   row_scale(amax, s, rcp);
 
   uint2 out[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
-    const int c = lane + 64 * j;
+    const int c = c0 + 64 * SPLIT * j;
     if (c < nchunk) {
       out[j].x = cast4(v[j].x, v[j].y, s, rcp);
       out[j].y = cast4(v[j].z, v[j].w, s, rcp);
@@ -143,10 +162,10 @@ __global__ __launch_bounds__(256) void quant_rows_regs(const uint16_t* __restric
     uint8_t* qr = q + orow * (int64_t)K;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-      const int c = lane + 64 * j;
+      const int c = c0 + 64 * SPLIT * j;
       if (c < nchunk) *reinterpret_cast<uint2*>(qr + 8 * c) = out[j];
     }
-    if (lane == 0) scale[orow] = s;
+    if (part == 0 && lane == 0) scale[orow] = s;
   }
 }
 
@@ -188,26 +207,41 @@ __global__ __launch_bounds__(256) void quant_rows_loop(const uint16_t* __restric
     scale[pos != nullptr ? (int64_t)pos[row * fanout + d] : row] = s;
 }
 
+template <int CPL, bool SILU>
+hipError_t launch_split(int split, const uint16_t* x, int64_t rows, int k, uint8_t* q, float* scale, uint16_t* h,
+                        const int32_t* pos, int fanout, hipStream_t stream) {
+  const dim3 block(64 * kRowsPerBlock);
+  const int per_block = kRowsPerBlock / split;
+  const dim3 grid((unsigned)((rows + per_block - 1) / per_block));
+  if (split == 4)
+    quant_rows_regs<CPL, SILU, 4><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h, pos, fanout);
+  else if (split == 2)
+    quant_rows_regs<CPL, SILU, 2><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h, pos, fanout);
+  else
+    quant_rows_regs<CPL, SILU, 1><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h, pos, fanout);
+  return hipGetLastError();
+}
+
 template <bool SILU>
 hipError_t launch_impl(const uint16_t* x, int64_t rows, int64_t K, uint8_t* q, float* scale,
                        uint16_t* h, const int32_t* pos, int fanout, hipStream_t stream) {
   const int64_t nchunk = K / 8;
-  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-  const dim3 block(64 * kRowsPerBlock);
   const int k = (int)K;
-  if (nchunk <= 64)
-    quant_rows_regs<1, SILU><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h, pos, fanout);
-  else if (nchunk <= 128)
-    quant_rows_regs<2, SILU><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h, pos, fanout);
-  else if (nchunk <= 256)
-    quant_rows_regs<4, SILU><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h, pos, fanout);
-  else if (nchunk <= 512)
-    quant_rows_regs<8, SILU><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h, pos, fanout);
-  else if (nchunk <= 1024)
-    quant_rows_regs<16, SILU><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h, pos, fanout);
-  else
-    quant_rows_loop<SILU><<<grid, block, 0, stream>>>(x, rows, K, q, scale, h, pos, fanout);
-  return hipGetLastError();
+  if (nchunk > 64 * 16) {
+    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+    quant_rows_loop<SILU><<<grid, dim3(64 * kRowsPerBlock), 0, stream>>>(x, rows, K, q, scale, h, pos, fanout);
+    return hipGetLastError();
+  }
+  // Wavefronts per row: split long rows while the launch would hold fewer than 8192
+  // wavefronts (32 per CU), keeping at least 4 chunks per lane.
+  int split = 1;
+  while (split < 4 && rows * split < 8192 && nchunk >= 64 * 4 * 2 * split) split *= 2;
+  const int64_t per_lane = (nchunk + 64 * split - 1) / (64 * split);
+  if (per_lane <= 1) return launch_split<1, SILU>(split, x, rows, k, q, scale, h, pos, fanout, stream);
+  if (per_lane <= 2) return launch_split<2, SILU>(split, x, rows, k, q, scale, h, pos, fanout, stream);
+  if (per_lane <= 4) return launch_split<4, SILU>(split, x, rows, k, q, scale, h, pos, fanout, stream);
+  if (per_lane <= 8) return launch_split<8, SILU>(split, x, rows, k, q, scale, h, pos, fanout, stream);
+  return launch_split<16, SILU>(split, x, rows, k, q, scale, h, pos, fanout, stream);
 }
 
 }  // namespace
