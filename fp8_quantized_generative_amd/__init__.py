@@ -15,10 +15,10 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (RQ_ACT_NONE, RQ_ACT_SILU_MUL, RQ_MOE_IN_PERMUTED, RQ_MOE_IN_TOKENS,  # noqa: F401
+from ._lib import (RQ_ACT_GATE_SILU, RQ_ACT_NONE, RQ_ACT_SILU_MUL, RQ_MOE_IN_PERMUTED, RQ_MOE_IN_TOKENS,  # noqa: F401
                    RQ_MOE_OUT_COMBINED, RQ_MOE_OUT_PERMUTED, DebugOut, RqError)
 
-ACTS = {"none": RQ_ACT_NONE, "silu_mul": RQ_ACT_SILU_MUL}
+ACTS = {"none": RQ_ACT_NONE, "silu_mul": RQ_ACT_SILU_MUL, "gate_silu": RQ_ACT_GATE_SILU}
 IN_LAYOUTS = {"tokens": RQ_MOE_IN_TOKENS, "permuted": RQ_MOE_IN_PERMUTED}
 OUT_LAYOUTS = {"permuted": RQ_MOE_OUT_PERMUTED, "combined": RQ_MOE_OUT_COMBINED}
 
@@ -43,6 +43,11 @@ def _dev(t, dtype, name):
     if not t.is_contiguous():
         raise TypeError("%s must be contiguous" % name)
     return t
+
+
+def _shape(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %r, got %r" % (name, tuple(shape), tuple(t.shape)))
 
 
 def _stream(t, stream):
@@ -94,7 +99,9 @@ def _debug(debug, q_rows, h_rows, k, act, device):
 
 
 def linear(x, w_q, w_scale, act="none", out=None, workspace=None, debug=False, stream=None):
-    """W8A8 FP8 linear: FP16 x [M, K] (or [M, 2K] for ``act='silu_mul'``) -> FP16 y [M, N].
+    """W8A8 FP8 linear: FP16 x [M, K] (or [M, 2K] for ``act='silu_mul'``) -> FP16 y [M, N]
+    (or h [M, N/2] for ``act='gate_silu'``, whose weight rows interleave 32 gate and 32 up
+    features; see ``interleave_gate_up``).
 
     With ``debug=True`` returns ``(y, {"a_q", "a_scale", "h"})``: the quantized GEMM input
     (and the SiLU*up rows).
@@ -109,9 +116,11 @@ def linear(x, w_q, w_scale, act="none", out=None, workspace=None, debug=False, s
     n, k = w_q.shape
     if x.shape[1] != (2 * k if a == RQ_ACT_SILU_MUL else k):
         raise ValueError("x width %d does not match K=%d for act=%r" % (x.shape[1], k, act))
+    n_out = n // 2 if a == RQ_ACT_GATE_SILU else n
     if out is None:
-        out = torch.empty((m, n), dtype=torch.float16, device=x.device)
+        out = torch.empty((m, n_out), dtype=torch.float16, device=x.device)
     _dev(out, torch.float16, "out")
+    _shape(out, (m, n_out), "out")
     lib = _lib.load()
     ws_bytes = lib.rq_fp8_linear_workspace_size(m, k, a)
     ws = _workspace(ws_bytes, x.device, workspace)
@@ -151,8 +160,10 @@ def moe_grouped_linear(x, topk_ids, w_q, w_scale, in_layout="tokens", act="none"
     if tuple(x.shape) != (rows, 2 * k if a == RQ_ACT_SILU_MUL else k):
         raise ValueError("x shape %r does not match the layout" % (tuple(x.shape),))
     if out is None:
-        out = torch.empty((t if ol == RQ_MOE_OUT_COMBINED else r, n), dtype=torch.float16, device=x.device)
+        out = torch.empty((t if ol == RQ_MOE_OUT_COMBINED else r, n // 2 if a == RQ_ACT_GATE_SILU else n),
+                          dtype=torch.float16, device=x.device)
     _dev(out, torch.float16, "out")
+    _shape(out, (t if ol == RQ_MOE_OUT_COMBINED else r, n // 2 if a == RQ_ACT_GATE_SILU else n), "out")
     lib = _lib.load()
     ws_bytes = lib.rq_fp8_moe_workspace_size(t, top_k, e, n, k, il, a, ol)
     ws = _workspace(ws_bytes, x.device, workspace)
@@ -163,3 +174,19 @@ def moe_grouped_linear(x, topk_ids, w_q, w_scale, in_layout="tokens", act="none"
         _stream(x, stream))
     _lib.check("rq_fp8_moe_grouped_linear", st)
     return (out, dbg) if debug else out
+
+
+def interleave_gate_up(w_gu, block=32):
+    """Reorder gate/up weight rows [gate (F) | up (F)] (any leading expert dims) into blocks of
+    `block` alternating gate and up rows, the layout ``act='gate_silu'`` expects.  Offline
+    weight preparation; works on any tensor (or array) with rows on the second-to-last axis
+    (FP16 weights before quantization, or E4M3 bytes with their scales as [..., 2F, 1])."""
+    f2 = w_gu.shape[-2]
+    if f2 % (2 * block) != 0:
+        raise ValueError("gate/up rows (%d) must be a multiple of %d" % (f2, 2 * block))
+    f = f2 // 2
+    lead = tuple(w_gu.shape[:-2])
+    g = w_gu[..., :f, :].reshape(lead + (f // block, 1, block, w_gu.shape[-1]))
+    u = w_gu[..., f:, :].reshape(lead + (f // block, 1, block, w_gu.shape[-1]))
+    cat = torch.cat if isinstance(w_gu, torch.Tensor) else __import__("numpy").concatenate
+    return cat([g, u], -3).reshape(w_gu.shape)

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "librq_fp8.so")
 
 RQ_OK = 0
-RQ_ACT_NONE, RQ_ACT_SILU_MUL = 0, 1
+RQ_ACT_NONE, RQ_ACT_SILU_MUL, RQ_ACT_GATE_SILU = 0, 1, 2
 RQ_MOE_IN_TOKENS, RQ_MOE_IN_PERMUTED = 0, 1
 RQ_MOE_OUT_PERMUTED, RQ_MOE_OUT_COMBINED = 0, 1
 RQ_KERNEL_QUANT, RQ_KERNEL_GEMM, RQ_KERNEL_COMBINE = 0, 1, 2

@@ -65,7 +65,7 @@ struct MoeLayout {
   size_t a_q, a_scale, offsets, tile_start, tile_table, perm, pos, block_hist, y_perm;
 };
 
-MoeLayout moe_layout(int64_t T, int top_k, int64_t E, int64_t N, int64_t K, int in_layout,
+MoeLayout moe_layout(int64_t T, int top_k, int64_t E, int64_t N, int64_t K, int in_layout, int act,
                      int out_layout) {
   (void)in_layout;
   const int64_t R = T * top_k;
@@ -78,7 +78,8 @@ MoeLayout moe_layout(int64_t T, int top_k, int64_t E, int64_t N, int64_t K, int 
   l.perm = (size_t)R * sizeof(int32_t);
   l.pos = (size_t)R * sizeof(int32_t);
   l.block_hist = (size_t)(rq::moe_plan_blocks(R) * E) * sizeof(int32_t);
-  l.y_perm = out_layout == RQ_MOE_OUT_COMBINED ? (size_t)(R * N) * sizeof(uint16_t) : 0;
+  const int64_t NO = act == RQ_ACT_GATE_SILU ? N / 2 : N;  // output row length
+  l.y_perm = out_layout == RQ_MOE_OUT_COMBINED ? (size_t)(R * NO) * sizeof(uint16_t) : 0;
   return l;
 }
 
@@ -147,9 +148,9 @@ size_t rq_fp8_linear_workspace_size(int64_t M, int64_t K, int act) {
 int rq_fp8_linear(const uint16_t* x, int64_t M, int64_t K, int act, const uint8_t* w_q,
                   const float* w_scale, int64_t N, uint16_t* y, void* workspace,
                   size_t workspace_bytes, const rq_debug_out* dbg, void* stream) {
-  if (act != RQ_ACT_NONE && act != RQ_ACT_SILU_MUL) return RQ_ERR_ARG;
+  if (act != RQ_ACT_NONE && act != RQ_ACT_SILU_MUL && act != RQ_ACT_GATE_SILU) return RQ_ERR_ARG;
   if (M < 0 || K <= 0 || N <= 0) return RQ_ERR_SHAPE;
-  if (K % 16 != 0 || N % 16 != 0) return RQ_ERR_ALIGN;
+  if (K % 16 != 0 || N % 16 != 0 || (act == RQ_ACT_GATE_SILU && N % 64 != 0)) return RQ_ERR_ALIGN;
   if (K > kMaxK || N > (int64_t)1 << 30 || M > (int64_t)1 << 31) return RQ_ERR_SHAPE;
   if (M * K > kMaxOperandBytes || N * K > kMaxOperandBytes) return RQ_ERR_SHAPE;
   if (!w_q || !w_scale) return RQ_ERR_NULL;
@@ -174,7 +175,8 @@ int rq_fp8_linear(const uint16_t* x, int64_t M, int64_t K, int act, const uint8_
   hipStream_t s = (hipStream_t)stream;
   {
     Hook hook(RQ_KERNEL_QUANT, s);
-    if (rq::launch_quant_rows(x, M, K, act, xq, sx, act == RQ_ACT_SILU_MUL ? dh : nullptr, nullptr, 0, s) !=
+    const int in_act = act == RQ_ACT_SILU_MUL ? RQ_ACT_SILU_MUL : RQ_ACT_NONE;
+    if (rq::launch_quant_rows(x, M, K, in_act, xq, sx, act == RQ_ACT_SILU_MUL ? dh : nullptr, nullptr, 0, s) !=
         hipSuccess)
       return RQ_ERR_HIP;
   }
@@ -189,15 +191,15 @@ int rq_fp8_linear(const uint16_t* x, int64_t M, int64_t K, int act, const uint8_
   g.N = (int32_t)N;
   g.K = (int32_t)K;
   g.E = 1;
+  g.gate = act == RQ_ACT_GATE_SILU ? 1 : 0;
   Hook hook(RQ_KERNEL_GEMM, s);
   return rq::launch_gemm_dense(g, s) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 
 size_t rq_fp8_moe_workspace_size(int64_t T, int top_k, int64_t E, int64_t N, int64_t K,
                                  int in_layout, int act, int out_layout) {
-  (void)act;
   if (T < 0 || top_k < 1 || E < 1 || N <= 0 || K <= 0) return 0;
-  const MoeLayout l = moe_layout(T, top_k, E, N, K, in_layout, out_layout);
+  const MoeLayout l = moe_layout(T, top_k, E, N, K, in_layout, act, out_layout);
   return align_up(l.a_q) + align_up(l.a_scale) + align_up(l.offsets) + align_up(l.tile_start) +
          align_up(l.tile_table) + align_up(l.perm) + align_up(l.pos) + align_up(l.block_hist) + align_up(l.y_perm);
 }
@@ -207,12 +209,12 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const i
                               const float* w_scale, int64_t E, int64_t N, int64_t K, uint16_t* y,
                               int out_layout, void* workspace, size_t workspace_bytes,
                               const rq_debug_out* dbg, void* stream) {
-  if (act != RQ_ACT_NONE && act != RQ_ACT_SILU_MUL) return RQ_ERR_ARG;
+  if (act != RQ_ACT_NONE && act != RQ_ACT_SILU_MUL && act != RQ_ACT_GATE_SILU) return RQ_ERR_ARG;
   if (in_layout != RQ_MOE_IN_TOKENS && in_layout != RQ_MOE_IN_PERMUTED) return RQ_ERR_ARG;
   if (out_layout != RQ_MOE_OUT_PERMUTED && out_layout != RQ_MOE_OUT_COMBINED) return RQ_ERR_ARG;
   if (T < 0 || K <= 0 || N <= 0 || E < 1 || E > kMaxExperts || top_k < 1 || top_k > E)
     return RQ_ERR_SHAPE;
-  if (K % 16 != 0 || N % 16 != 0) return RQ_ERR_ALIGN;
+  if (K % 16 != 0 || N % 16 != 0 || (act == RQ_ACT_GATE_SILU && N % 64 != 0)) return RQ_ERR_ALIGN;
   if (K > kMaxK || N > (int64_t)1 << 30 || T * top_k > ((int64_t)1 << 31) - 1)
     return RQ_ERR_SHAPE;
   if (T * top_k * K > kMaxOperandBytes || N * K > kMaxOperandBytes) return RQ_ERR_SHAPE;
@@ -234,7 +236,7 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const i
 
   const int64_t R = T * top_k;
   const int64_t rows = in_layout == RQ_MOE_IN_TOKENS ? T : R;
-  const MoeLayout l = moe_layout(T, top_k, E, N, K, in_layout, out_layout);
+  const MoeLayout l = moe_layout(T, top_k, E, N, K, in_layout, act, out_layout);
   Carve c{reinterpret_cast<uint8_t*>(workspace)};
   uint8_t* aq = c.take<uint8_t>(l.a_q);
   float* as = c.take<float>(l.a_scale);
@@ -257,7 +259,8 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const i
     Hook hook(RQ_KERNEL_QUANT, s);
     // per-token rows are written to each of the token's permuted slots
     const bool tokens = in_layout == RQ_MOE_IN_TOKENS;
-    if (rq::launch_quant_rows(x, rows, K, act, aq, as, act == RQ_ACT_SILU_MUL ? dh : nullptr,
+    const int in_act = act == RQ_ACT_SILU_MUL ? RQ_ACT_SILU_MUL : RQ_ACT_NONE;
+    if (rq::launch_quant_rows(x, rows, K, in_act, aq, as, act == RQ_ACT_SILU_MUL ? dh : nullptr,
                               tokens ? pos : nullptr, tokens ? top_k : 0, s) != hipSuccess)
       return RQ_ERR_HIP;
   }
@@ -274,13 +277,15 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const i
   g.tile_start = tile_start;
   g.tile_table = tile_table;
   g.E = (int32_t)E;
+  g.gate = act == RQ_ACT_GATE_SILU ? 1 : 0;
   {
     Hook hook(RQ_KERNEL_GEMM, s);
     if (rq::launch_gemm_grouped(g, kind, s) != hipSuccess) return RQ_ERR_HIP;
   }
   if (out_layout == RQ_MOE_OUT_COMBINED) {
     Hook hook(RQ_KERNEL_COMBINE, s);
-    if (rq::launch_moe_combine(y_perm, pos, topk_w, T, top_k, N, y, s) != hipSuccess) return RQ_ERR_HIP;
+    const int64_t NO = act == RQ_ACT_GATE_SILU ? N / 2 : N;  // output row length
+    if (rq::launch_moe_combine(y_perm, pos, topk_w, T, top_k, NO, y, s) != hipSuccess) return RQ_ERR_HIP;
   }
   return RQ_OK;
 }

@@ -21,6 +21,25 @@ __device__ __forceinline__ uint32_t float_to_half_bits(float f) {
   return (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)f);  // round to nearest even
 }
 
+// h = fl16(fl32(silu(g) * u)) for two packed FP16 pairs, computed in FP32 with
+// silu(g) = g / (1 + exp(-g)).  The quantizer's SiLU*up input transform and the GEMM's gated
+// output both use this one definition, so the two FFN formulations give identical h.
+__device__ __forceinline__ uint32_t silu_mul_pair(uint32_t g2, uint32_t u2) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    float g = half_bits_to_float((g2 >> (16 * i)) & 0xFFFFu);
+    float u = half_bits_to_float((u2 >> (16 * i)) & 0xFFFFu);
+    float silu = __fdividef(g, 1.0f + __expf(-g));
+    float p = silu * u;
+    // FP32 product, then FP16: the empty asm keeps the compiler from fusing the multiply
+    // into the conversion (a single rounding) in some contexts and not in others
+    asm("" : "+v"(p));
+    out |= float_to_half_bits(p) << (16 * i);
+  }
+  return out;
+}
+
 __device__ __forceinline__ uint4 ld_global_16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
@@ -61,6 +80,7 @@ struct GemmArgs {
   const int32_t* tile_start;  // [E+1] first m-tile of each expert (exclusive scan); [E] = total
   const int32_t* tile_table;  // [m-tiles][4] {expert, first row, end row, 0}
   int32_t E;
+  int32_t gate;               // 1: gated SiLU output (see rq_fp8.h, RQ_ACT_GATE_SILU), y is [rows][N/2]
 };
 
 // GEMM tile shapes (rows x columns of output per workgroup).

@@ -210,8 +210,11 @@ __device__ __forceinline__ void load_lds_4(const v4i& desc, uint32_t voffset, ui
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
-// Two FP32 values rounded to FP16 (nearest even), packed low then high.
+// Two FP32 values rounded to FP16 (nearest even), packed low then high.  The empty asm
+// makes the inputs plain FP32 values: without it the compiler may fuse the multiply that
+// produced them into a single-rounding multiply-to-FP16 in some contexts and not others.
 __device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
+  asm("" : "+v"(lo), "+v"(hi));
   const h2 v = {(_Float16)lo, (_Float16)hi};
   return __builtin_bit_cast(uint32_t, v);
 }
@@ -265,8 +268,9 @@ __device__ __forceinline__ TileDesc2 tile_descs(const GemmArgs& p, const TileInf
   return d;
 }
 
-template <class C, bool GROUPED>
+template <class C, bool GROUPED, bool GATE>
 __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles, int n_tiles) {
+  static_assert(!GATE || C::TJ % 2 == 0, "gated output pairs 32-column gate and up blocks in a wave");
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
 
   // ---- this workgroup's tiles: logical tiles first, first + stride, ... below last.
@@ -519,16 +523,23 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
 
     // ---- epilogue.  Lane: token row wm*WM + 32 i + (lane & 31); register group g of tile
     // (i, jj): columns wn*WN + 32 jj + 8 g + 4 half + 0..3, scaled and rounded to FP16.
+    // GATE: MFMA tiles jj = 2 o and 2 o + 1 are the gate and up columns of the same 32
+    // features, so output block o holds h = fl16(silu(g) * u) of those features (half the
+    // columns; the row stride of y is N / 2).
     // Storers store their own blocks straight from registers: a 32-lane swap between column
     // groups g and g+1 gives each lane 8 consecutive columns (16 bytes) of its row.  With
     // SPLIT, loaders stage each 32-row block in an LDS strip shared with their storer; after
     // a barrier the storer reads it back as 16-byte chunks along the rows (whole 128-byte
     // row segments per store) and stores it; a second barrier frees the strip.
     {
+      constexpr int kOutTJ = GATE ? C::TJ / 2 : C::TJ;  // 32-column output blocks per wave
+      constexpr int kOutWN = 32 * kOutTJ;               // output columns per wave
+      const int NO = GATE ? N / 2 : N;                   // output row length
+      const int n0o = GATE ? cur.n0 / 2 : cur.n0;
       const float* sc = reinterpret_cast<const float*>(smem + C::SCALE_OFF + (j & 1) * C::SCALE_BYTES);
       const int partner = loader ? wave : wave - C::LOADERS;
       uint8_t* strip = smem + C::EPI_OFF + partner * C::STRIP;
-      constexpr int kCpr = C::WN / 8;   // 16-byte chunks per strip row
+      constexpr int kCpr = kOutWN / 8;  // 16-byte chunks per strip row
       constexpr int kRpt = 64 / kCpr;   // strip rows covered by one 64-lane read
       int el = lane;                    // opaque copy: addressing is redone per tile, not hoisted
       asm volatile("" : "+v"(el));
@@ -536,10 +547,10 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
       const int lc = 8 * (el % kCpr);
       const int erow = el & 31, ehalf = el >> 5;  // MFMA output row and column half
       const int rows = cur.row_end - cur.row_begin;
-      const int cols = N - cur.n0;
+      const int cols = NO - n0o;
       const int pwm = partner / C::WGN, pwn = partner % C::WGN;
-      const bool pcol_ok = lc < cols - pwn * C::WN;
-      uint16_t* ytile = p.y + (int64_t)cur.row_begin * N + cur.n0;
+      const bool pcol_ok = lc < cols - pwn * kOutWN;
+      uint16_t* ytile = p.y + (int64_t)cur.row_begin * NO + n0o;
       // FP16 of register group g of tile (i, jj): 4 columns
       auto group = [&](int i, int jj, int g, float sa) -> uint2 {
         const v4f sb = *reinterpret_cast<const v4f*>(sc + C::BM + wn * C::WN + 32 * jj + 8 * g + 4 * ehalf);
@@ -549,29 +560,38 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
         v.y = pack_half2((a[4 * g + 2] * sa) * sb[2], (a[4 * g + 3] * sa) * sb[3]);
         return v;
       };
+      // the 4 output columns of register group g of output block o
+      auto out_group = [&](int i, int o, int g, float sa) -> uint2 {
+        if constexpr (GATE) {
+          const uint2 gt = group(i, 2 * o, g, sa), up = group(i, 2 * o + 1, g, sa);
+          return make_uint2(silu_mul_pair(gt.x, up.x), silu_mul_pair(gt.y, up.y));
+        } else {
+          return group(i, o, g, sa);
+        }
+      };
 #pragma unroll
       for (int i = 0; i < C::TI; ++i) {
         const float sa = sc[wm * C::WM + 32 * i + erow];
         if (!storer) {
 #pragma unroll
-          for (int jj = 0; jj < C::TJ; ++jj)
+          for (int o = 0; o < kOutTJ; ++o)
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-              *reinterpret_cast<uint2*>(strip + erow * C::EPI_STRIDE + 2 * (32 * jj + 8 * g + 4 * ehalf)) =
-                  group(i, jj, g, sa);
+              *reinterpret_cast<uint2*>(strip + erow * C::EPI_STRIDE + 2 * (32 * o + 8 * g + 4 * ehalf)) =
+                  out_group(i, o, g, sa);
         } else {
           const int lrow = wm * C::WM + 32 * i + erow;
-          uint16_t* yrow = ytile + (int64_t)lrow * N + wn * C::WN + 8 * ehalf;
+          uint16_t* yrow = ytile + (int64_t)lrow * NO + wn * kOutWN + 8 * ehalf;
 #pragma unroll
-          for (int jj = 0; jj < C::TJ; ++jj) {
+          for (int o = 0; o < kOutTJ; ++o) {
 #pragma unroll
             for (int gp = 0; gp < 2; ++gp) {
-              const uint2 x = group(i, jj, 2 * gp, sa), y = group(i, jj, 2 * gp + 1, sa);
+              const uint2 x = out_group(i, o, 2 * gp, sa), y = out_group(i, o, 2 * gp + 1, sa);
               const auto s0 = __builtin_amdgcn_permlane32_swap(x.x, y.x, false, false);
               const auto s1 = __builtin_amdgcn_permlane32_swap(x.y, y.y, false, false);
-              const int col = wn * C::WN + 32 * jj + 16 * gp + 8 * ehalf;
+              const int col = wn * kOutWN + 32 * o + 16 * gp + 8 * ehalf;
               if (lrow < rows && col < cols)
-                st_global_16(yrow + 32 * jj + 16 * gp, make_uint4(s0[0], s1[0], s0[1], s1[1]));
+                st_global_16(yrow + 32 * o + 16 * gp, make_uint4(s0[0], s1[0], s0[1], s1[1]));
             }
           }
         }
@@ -583,7 +603,7 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
               const int r = lr + kRpt * t;
               const uint4 v = *reinterpret_cast<const uint4*>(strip + r * C::EPI_STRIDE + 2 * lc);
               const int orow = pwm * C::WM + 32 * i + r;
-              if (orow < rows && pcol_ok) st_global_16(ytile + (int64_t)orow * N + pwn * C::WN + lc, v);
+              if (orow < rows && pcol_ok) st_global_16(ytile + (int64_t)orow * NO + pwn * kOutWN + lc, v);
             }
           }
           __syncthreads();
@@ -599,7 +619,7 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
 }
 
 // Workgroups of this kernel the device keeps resident at once (all CUs), cached per device.
-template <class C, bool GROUPED>
+template <class C, bool GROUPED, bool GATE>
 int resident_workgroups() {
   constexpr int kDevices = 64;
   static int cache[kDevices] = {};
@@ -609,7 +629,8 @@ int resident_workgroups() {
   if (cache[slot] > 0) return cache[slot];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_fp8_kernel<C, GROUPED>, C::NT, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_fp8_kernel<C, GROUPED, GATE>, C::NT, 0) !=
+          hipSuccess ||
       per_cu <= 0)
     per_cu = 1;
   cache[slot] = cus * per_cu;
@@ -625,17 +646,27 @@ int64_t grid_cap_override() {
   return v > 0 ? (int64_t)v : 0;
 }
 
-template <class C, bool GROUPED>
-hipError_t launch(const GemmArgs& g, int m_tiles, hipStream_t stream) {
+template <class C, bool GROUPED, bool GATE>
+hipError_t launch_one(const GemmArgs& g, int m_tiles, hipStream_t stream) {
   const int n_tiles = (int)((g.N + C::BN - 1) / C::BN);
   const int64_t tiles = (int64_t)m_tiles * n_tiles;  // grouped: the worst case
-  int64_t cap = resident_workgroups<C, GROUPED>();
+  int64_t cap = resident_workgroups<C, GROUPED, GATE>();
   const int64_t forced = grid_cap_override();
   if (forced > 0 && forced < cap) cap = forced;
   const int64_t want = (tiles + 7) / 8 * 8;
   const int64_t grid = want < cap ? want : cap;
-  gemm_fp8_kernel<C, GROUPED><<<dim3((unsigned)grid), dim3(C::NT), 0, stream>>>(g, m_tiles, n_tiles);
+  gemm_fp8_kernel<C, GROUPED, GATE><<<dim3((unsigned)grid), dim3(C::NT), 0, stream>>>(g, m_tiles, n_tiles);
   return hipGetLastError();
+}
+
+template <class C, bool GROUPED>
+hipError_t launch(const GemmArgs& g, int m_tiles, hipStream_t stream) {
+  if constexpr (C::TJ % 2 == 0) {
+    if (g.gate) return launch_one<C, GROUPED, true>(g, m_tiles, stream);
+  } else {
+    if (g.gate) return hipErrorInvalidValue;  // tile shapes with one 32-column block per wave
+  }
+  return launch_one<C, GROUPED, false>(g, m_tiles, stream);
 }
 
 // Eight wavefronts (two per SIMD) for the large tiles: while one wavefront of a SIMD waits
@@ -669,16 +700,17 @@ int tile_override() {
 // loaded) that still yields enough workgroups to occupy the 256 CUs, else the thinnest.
 // On MI355X this rule picks the fastest shape for every linear of the workloads (measured
 // over all five shapes at M = 512 and M = 4096).
-int pick_dense(int64_t M, int64_t N) {
+int pick_dense(int64_t M, int64_t N, bool gate) {
   const int forced = tile_override();
-  if (forced >= 0) return forced;
+  if (forced >= 0 && !(gate && forced == kTileThin)) return forced;
   const int order[] = {kTileBig, kTileWide, kTileSmall, kTileThin};
   for (int o : order) {
     const TileDesc& d = kTiles[o];
     const int64_t tiles = ((M + d.bm - 1) / d.bm) * ((N + d.bn - 1) / d.bn);
-    if (tiles >= 192) return o;
+    if (tiles >= 192) return gate && o == kTileThin ? kTileThinWide : o;
   }
-  return kTileThin;
+  // a gated output needs both 32-column blocks of a feature group in one wavefront
+  return gate ? kTileThinWide : kTileThin;
 }
 
 template <class C>
@@ -701,7 +733,7 @@ int64_t grouped_max_mtiles(int64_t R, int64_t E, int tile_m) { return (R + tile_
 
 hipError_t launch_gemm_dense(const GemmArgs& g, hipStream_t stream) {
   if (g.M <= 0) return hipSuccess;
-  switch (pick_dense(g.M, g.N)) {
+  switch (pick_dense(g.M, g.N, g.gate != 0)) {
     case kTileBig: return launch_dense<Big>(g, stream);
     case kTileWide: return launch_dense<Wide>(g, stream);
     case kTileSmall: return launch_dense<Small>(g, stream);

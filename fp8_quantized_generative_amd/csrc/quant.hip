@@ -56,18 +56,6 @@ __device__ __forceinline__ uint32_t absmax_packed(uint4 v, uint32_t m) {
   return m;
 }
 
-__device__ __forceinline__ uint32_t silu_mul_pair(uint32_t g2, uint32_t u2) {
-  uint32_t out = 0;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    float g = half_bits_to_float((g2 >> (16 * i)) & 0xFFFFu);
-    float u = half_bits_to_float((u2 >> (16 * i)) & 0xFFFFu);
-    float silu = __fdividef(g, 1.0f + __expf(-g));
-    out |= float_to_half_bits(silu * u) << (16 * i);
-  }
-  return out;
-}
-
 __device__ __forceinline__ uint4 silu_mul8(uint4 g, uint4 u) {
   return make_uint4(silu_mul_pair(g.x, u.x), silu_mul_pair(g.y, u.y),
                     silu_mul_pair(g.z, u.z), silu_mul_pair(g.w, u.w));

@@ -67,7 +67,17 @@ typedef enum {
  * RQ_ACT_SILU_MUL: each input row has 2K values [g (K) | u (K)] and the quantized row is
  * h = fl16(silu(g) * u), silu(g) = g / (1 + exp(-g)) evaluated in FP32.  This is the FFN
  * intermediate between the gate/up and down linears. */
-enum { RQ_ACT_NONE = 0, RQ_ACT_SILU_MUL = 1 };
+enum { RQ_ACT_NONE = 0, RQ_ACT_SILU_MUL = 1, RQ_ACT_GATE_SILU = 2 };
+
+/* RQ_ACT_GATE_SILU is applied to the OUTPUT instead (the input rows are plain [K] rows): the
+ * linear's N output columns come in blocks of 32 alternating gate and up features - output
+ * columns [64b, 64b + 32) are the gate values of features [32b, 32b + 32) and columns
+ * [64b + 32, 64b + 64) their up values (so the weight rows are interleaved the same way) -
+ * and the call writes h [rows][N / 2], h[m][32b + i] = fl16(silu(g) * u) of the FP16 linear
+ * outputs g = y[m][64b + i], u = y[m][64b + 32 + i], computed in FP32 exactly as
+ * RQ_ACT_SILU_MUL computes it.  The FFN intermediate then never exists at full width in
+ * memory: its gate/up GEMM writes h, and the down linear takes h with RQ_ACT_NONE.
+ * N must be a multiple of 64 (RQ_ERR_ALIGN otherwise). */
 
 /* MoE input rows: one per token (quantized once, before dispatch) or one per routed
  * slot in the canonical permuted order (see rq_fp8_moe_grouped_linear). */
@@ -106,6 +116,7 @@ size_t rq_fp8_linear_workspace_size(int64_t M, int64_t K, int act);
  * x [M][K] FP16 (or [M][2K] with RQ_ACT_SILU_MUL) is quantized per token into the
  * workspace (or dbg->a_q / dbg->a_scale), multiplied with w_q [N][K] E4M3 and
  * dequantized with w_scale [N] into y [M][N] FP16.
+ * With RQ_ACT_GATE_SILU, y is [M][N / 2] (see above).
  * Two kernels on `stream`: the row quantizer, then the FP8 MFMA GEMM with the
  * scale/FP16 epilogue.  dbg may be NULL. */
 int rq_fp8_linear(const uint16_t* x, int64_t M, int64_t K, int act,
@@ -134,8 +145,11 @@ size_t rq_fp8_moe_workspace_size(int64_t T, int top_k, int64_t E, int64_t N, int
  * Output: RQ_MOE_OUT_PERMUTED: y [R][N] FP16 in canonical order;
  * RQ_MOE_OUT_COMBINED: y [T][N] = fl16(sum_k fl32(topk_w[t][k] * y_perm[pos(t,k)])),
  * summed in FP32 in slot order, topk_w [T][top_k] FP16 required.
+ * With RQ_ACT_GATE_SILU the output rows are N / 2 wide (see above).
  * Experts with no rows read no weights.  A gate/up + SiLU + down expert FFN is two
- * calls: (TOKENS, NONE, PERMUTED) then (PERMUTED, SILU_MUL, COMBINED).
+ * calls: (TOKENS, NONE, PERMUTED) then (PERMUTED, SILU_MUL, COMBINED), or, with gate/up
+ * weight rows interleaved in blocks of 32, (TOKENS, GATE_SILU, PERMUTED) then
+ * (PERMUTED, NONE, COMBINED).
  * TOKENS rows are quantized once per token and the result is written to each of the
  * token's top_k permuted rows, so the GEMM reads contiguous rows.
  * dbg->a_q / a_scale: R rows in the permuted order (the GEMM operand, for either input

@@ -25,3 +25,33 @@ def silu_mul(gu, f):
     with np.errstate(over="ignore"):
         h = g * u / (1.0 + np.exp(-g))
         return h.astype(np.float16)
+
+
+# Gated layout: the gate/up linear's output columns come in blocks of 32 alternating gate
+# and up features (columns [64b, 64b+32) gate of features [32b, 32b+32), [64b+32, 64b+64)
+# their up values), so a kernel producing a 64-column block holds both operands of 32
+# features.  The weight rows of W_gu are reordered the same way; since a linear computes
+# each output column from its own weight row, reordering rows reorders output columns.
+GATE_BLOCK = 32
+
+
+def gate_up_order(f):
+    """Row (or column) order of the gated layout: index i of the gated layout holds row
+    ``order[i]`` of ``[gate (f) | up (f)]``."""
+    if f % GATE_BLOCK != 0:
+        raise ValueError("f must be a multiple of %d" % GATE_BLOCK)
+    order = []
+    for b in range(f // GATE_BLOCK):
+        order.extend(range(b * GATE_BLOCK, (b + 1) * GATE_BLOCK))          # gate rows
+        order.extend(range(f + b * GATE_BLOCK, f + (b + 1) * GATE_BLOCK))  # up rows
+    return np.array(order, dtype=np.int64)
+
+
+def gate_silu(y16):
+    """``h`` of an FP16 gate/up output in the gated layout: put the columns back in
+    ``[gate | up]`` order and apply ``silu_mul``."""
+    y16 = np.asarray(y16)
+    f = y16.shape[1] // 2
+    gu = np.empty_like(y16)
+    gu[:, gate_up_order(f)] = y16
+    return silu_mul(gu, f)

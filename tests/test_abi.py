@@ -64,7 +64,8 @@ def _linear(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(act=2), RQ_ERR_ARG),
+    (dict(act=3), RQ_ERR_ARG),
+    (dict(act=2, N=96), RQ_ERR_ALIGN),
     (dict(M=-1), RQ_ERR_SHAPE),
     (dict(K=0), RQ_ERR_SHAPE),
     (dict(N=-16), RQ_ERR_SHAPE),
@@ -110,6 +111,8 @@ def _moe(**kw):
     (dict(il=2), RQ_ERR_ARG),
     (dict(ol=5), RQ_ERR_ARG),
     (dict(act=-1), RQ_ERR_ARG),
+    (dict(act=3), RQ_ERR_ARG),
+    (dict(act=2, N=96), RQ_ERR_ALIGN),
     (dict(T=-1), RQ_ERR_SHAPE),
     (dict(E=0), RQ_ERR_SHAPE),
     (dict(E=1025), RQ_ERR_SHAPE),

@@ -171,3 +171,37 @@ def test_persistent_walk(monkeypatch, grid, tile, m, n, k):
     x = workloads.acts_student_t(rng, m, k)
     w = workloads.weights(rng, (n, k))
     _check(x, w)
+
+
+@pytest.mark.parametrize("tile", [None, "256x256", "256x128", "128x128", "64x256"])
+@pytest.mark.parametrize("m,f,k", [(130, 64, 272), (300, 320, 528), (64, 2048, 512)])
+def test_gated_silu_output(monkeypatch, tile, m, f, k):
+    """act='gate_silu' on interleaved gate/up weights writes exactly the h that the unfused
+    path (plain gate/up linear, then the SiLU*up input transform of the down linear) makes."""
+    rq = require_gpu()
+    case("gated linear tile=%s m=%d f=%d k=%d" % (tile, m, f, k))
+    if tile is not None:
+        monkeypatch.setenv("RQ_GEMM_TILE", tile)
+    rng = np.random.default_rng(m + f + k)
+    x = workloads.acts_channel_lognormal(rng, m, k)
+    w = workloads.weights(rng, (2 * f, k))
+    wq, ws = rq.quant_weights(dev(w))
+    order = torch.from_numpy(ffn.gate_up_order(f)).cuda()
+    xd = dev(x)
+    h = host(rq.linear(xd, wq[order].contiguous(), ws[order].contiguous(), act="gate_silu"))
+    assert h.shape == (m, f)
+    gu = rq.linear(xd, wq, ws)
+    w_dn_q = torch.zeros((16, f), dtype=torch.uint8, device="cuda")
+    _, dbg = rq.linear(gu, w_dn_q, torch.ones(16, device="cuda"), act="silu_mul", debug=True)
+    assert np.array_equal(h.view(np.uint16), host(dbg["h"]).view(np.uint16))
+    # and against the oracle's SiLU of the GPU's own gate/up output
+    assert ulp_diff16(h, ffn.silu_mul(host(gu), f)).max() <= 1
+
+
+def test_gated_needs_64_column_blocks():
+    rq = require_gpu()
+    case("gated linear: N % 64 != 0 is refused")
+    wq = torch.zeros((96, 64), dtype=torch.uint8, device="cuda")
+    with pytest.raises(rq.RqError):
+        rq.linear(torch.zeros((4, 64), dtype=torch.float16, device="cuda"), wq,
+                  torch.ones(96, device="cuda"), act="gate_silu")

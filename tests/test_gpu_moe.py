@@ -143,3 +143,29 @@ def test_grouped_tile_shapes(monkeypatch, tile, grid):
         monkeypatch.setenv("RQ_GEMM_GRID", grid)
     d = workloads.make(4, t=600, k=320, f=144, e=6)
     _expert_ffn(d, 600, 320, 144, 6, 2)
+
+
+@pytest.mark.parametrize("tile", [None, "256x256", "64x256"])
+@pytest.mark.parametrize("t,k,f,e", [(300, 128, 64, 6), (600, 320, 160, 4)])
+def test_gated_expert_ffn(monkeypatch, tile, t, k, f, e):
+    """(TOKENS, GATE_SILU, PERMUTED) on interleaved expert weights writes exactly the h of the
+    plain (TOKENS, NONE, PERMUTED) call followed by the down call's SiLU*up transform, and
+    the down call on it (PERMUTED, NONE, COMBINED) matches the unfused FFN bit for bit."""
+    rq = require_gpu()
+    case("moe gated tile=%s t=%d k=%d f=%d e=%d" % (tile, t, k, f, e))
+    if tile is not None:
+        monkeypatch.setenv("RQ_GEMM_TILE", tile)
+    d = workloads.make(4, t=t, k=k, f=f, e=e)
+    ids, tw, x = dev(d["ids"].astype(np.int32)), dev(d["topk_w"]), dev(d["x"])
+    wgu_q, wgu_s = rq.quant_weights(dev(d["w_gu"]))
+    wdn_q, wdn_s = rq.quant_weights(dev(d["w_dn"]))
+    order = torch.from_numpy(ffn.gate_up_order(f)).cuda()
+    wgi_q, wgi_s = wgu_q[:, order].contiguous(), wgu_s[:, order].contiguous()
+    h = rq.moe_grouped_linear(x, ids, wgi_q, wgi_s, "tokens", "gate_silu", "permuted")
+    assert tuple(h.shape) == (2 * t, f)
+    gu = rq.moe_grouped_linear(x, ids, wgu_q, wgu_s, "tokens", "none", "permuted")
+    out_plain, dbg = rq.moe_grouped_linear(gu, ids, wdn_q, wdn_s, "permuted", "silu_mul", "combined",
+                                           topk_w=tw, debug=True)
+    assert np.array_equal(host(h).view(np.uint16), host(dbg["h"]).view(np.uint16))
+    out = rq.moe_grouped_linear(h, ids, wdn_q, wdn_s, "permuted", "none", "combined", topk_w=tw)
+    assert np.array_equal(host(out).view(np.uint16), host(out_plain).view(np.uint16))

@@ -162,3 +162,32 @@ def test_zipf_routing_recipe():
     assert np.all(ids[:, 0] != ids[:, 1])
     assert counts.max() > 4 * np.median(counts[counts > 0])
     assert np.allclose(data["topk_w"].astype(np.float64).sum(axis=1), 1.0, atol=2e-3)
+
+
+def test_gate_up_order_is_a_block_permutation():
+    o = ffn.gate_up_order(96)
+    assert sorted(o.tolist()) == list(range(192))
+    # blocks of 32: gate features 0..31, up features 0..31, gate 32..63, ...
+    assert o[:32].tolist() == list(range(32)) and o[32:64].tolist() == list(range(96, 128))
+    assert o[64:96].tolist() == list(range(32, 64)) and o[-32:].tolist() == list(range(160, 192))
+    with pytest.raises(ValueError):
+        ffn.gate_up_order(48)
+
+
+def test_gate_silu_of_reordered_weights_equals_silu_mul():
+    # reordering W_gu's rows reorders the linear's output columns, so the gated output of the
+    # reordered weights is silu_mul of the plain layout, bit for bit
+    rng = np.random.default_rng(11)
+    f, k = 64, 48
+    x = workloads.acts_outliers(rng, 9, k)
+    w = workloads.weights(rng, (2 * f, k))
+    xq, xs = quant.quantize_rows(x)
+    wq, ws = quant.quantize_rows(w)
+    plain = linear.linear(xq, xs, wq, ws)
+    o = ffn.gate_up_order(f)
+    gated = linear.linear(xq, xs, wq[o], ws[o])
+    assert np.array_equal(gated.view(np.uint16), plain[:, o].view(np.uint16))
+    h = ffn.gate_silu(gated)
+    assert np.array_equal(h.view(np.uint16), ffn.silu_mul(plain, f).view(np.uint16))
+    # a plain-layout output fed to gate_silu is a different function (the layouts are not mixed up)
+    assert not np.array_equal(ffn.gate_silu(plain).view(np.uint16), h.view(np.uint16))
