@@ -5,9 +5,10 @@ A step is one pass of the whole path over one batch of each synthetic workload, 
 size, with inputs and quantized weights resident in HBM:
 
 * attention projections: 4096 tokens x hidden 2048, merged QKV (N = 6144) and O (2048);
-* dense FFN: 4096 tokens, gate/up (N = 16384), SiLU*up re-quantization, down (K = 8192);
-* sparse MoE: 16384 tokens, top-2 of 32 Zipf-loaded experts, grouped gate/up (8192),
-  SiLU*up, grouped down (K = 4096) and the weighted combine;
+* dense FFN: 4096 tokens, gate/up (N = 16384) writing h = SiLU(g)*up from its epilogue
+  (gate/up weight rows interleaved offline), h re-quantization, down (K = 8192);
+* sparse MoE: 16384 tokens, top-2 of 32 Zipf-loaded experts, grouped gate/up (8192) writing
+  h, grouped down (K = 4096) and the weighted combine;
 * small-M layer: 512 rows through QKV, O, the dense FFN and the MoE expert FFN.
 
 Each linear runs per-token activation quantization, the FP8 MFMA GEMM with FP32
@@ -117,14 +118,19 @@ class Path:
             wq, ws = rq.quant_weights(dev(w16))
             return wq, ws
 
+        def qw_gated(w16):
+            # gate/up rows interleaved in blocks of 32 (offline, untimed): the gate/up GEMM
+            # then writes h = silu(g) * u directly
+            return qw(rq.interleave_gate_up(w16))
+
         def add_linear(work, label, x, wq, ws, act="none"):
             m = x.shape[0]
             n, k = wq.shape
-            out = torch.empty((m, n), dtype=torch.float16, device="cuda")
+            out = torch.empty((m, n // 2 if act == "gate_silu" else n), dtype=torch.float16, device="cuda")
             ws_t = torch.empty(max(rq.linear_workspace_size(m, k, act), 1), dtype=torch.uint8, device="cuda")
             fl = 2 * m * n * k
             # bytes that must cross HBM at least once: activations in, weights, output
-            by = x.numel() * 2 + wq.numel() + m * n * 2
+            by = x.numel() * 2 + wq.numel() + out.numel() * 2
             self.calls.append((work, label, "linear", fl, by,
                                lambda: rq.linear(x, wq, ws, act=act, out=out, workspace=ws_t)))
             self.flops += fl
@@ -134,11 +140,12 @@ class Path:
             t, top_k = ids.shape
             e, n, k = wq.shape
             r = t * top_k
-            out = torch.empty((t if ol == "combined" else r, n), dtype=torch.float16, device="cuda")
+            n_out = n // 2 if act == "gate_silu" else n
+            out = torch.empty((t if ol == "combined" else r, n_out), dtype=torch.float16, device="cuda")
             ws_t = torch.empty(rq.moe_workspace_size(t, top_k, e, n, k, il, act, ol), dtype=torch.uint8,
                                device="cuda")
             fl = 2 * r * n * k
-            by = x.numel() * 2 + wq.numel() + r * n * 2
+            by = x.numel() * 2 + wq.numel() + r * n_out * 2
             self.calls.append((work, label, "moe", fl, by,
                                lambda: rq.moe_grouped_linear(x, ids, wq, ws, il, act, ol, topk_w=topk_w,
                                                              out=out, workspace=ws_t)))
@@ -155,18 +162,18 @@ class Path:
             self.config["attention"] = "4096 tokens x 2048; QKV 6144, O 2048"
         if "ffn" in want:
             d = workloads.make(3)
-            wgu, wdn = qw(d["w_gu"]), qw(d["w_dn"])
-            gu = add_linear("ffn", "gate_up", dev(d["x"]), *wgu)
-            add_linear("ffn", "down", gu, *wdn, act="silu_mul")
+            wgu, wdn = qw_gated(d["w_gu"]), qw(d["w_dn"])
+            h = add_linear("ffn", "gate_up", dev(d["x"]), *wgu, act="gate_silu")
+            add_linear("ffn", "down", h, *wdn)
             self.config["ffn"] = "4096 tokens x 2048; gate/up 2x8192, down K=8192"
         if "moe" in want:
             d = workloads.make(4)
-            wgu, wdn = qw(d["w_gu"]), qw(d["w_dn"])
+            wgu, wdn = qw_gated(d["w_gu"]), qw(d["w_dn"])
             ids, tw = dev(d["ids"].astype(np.int32)), dev(d["topk_w"])
             counts = np.bincount(d["ids"].reshape(-1), minlength=32)
-            gu = add_moe("moe", "gate_up", dev(d["x"]), ids, *wgu, "tokens", "none", "permuted")
+            h = add_moe("moe", "gate_up", dev(d["x"]), ids, *wgu, "tokens", "gate_silu", "permuted")
             self.dominant = len(self.calls) - 1
-            add_moe("moe", "down", gu, ids, *wdn, "permuted", "silu_mul", "combined", topk_w=tw)
+            add_moe("moe", "down", h, ids, *wdn, "permuted", "none", "combined", topk_w=tw)
             self.config["moe"] = ("16384 tokens x 2048; top-2 of 32 experts (Zipf 1.1; max %d, min nonzero %d, "
                                   "%d empty rows of 32768); gate/up 2x4096, down K=4096"
                                   % (counts.max(), counts[counts > 0].min(), int((counts == 0).sum())))
@@ -175,12 +182,12 @@ class Path:
             d = workloads.make(5)
             add_linear("layer_small_m", "qkv", dev(d["x_qkv"]), *qw(d["w_qkv"]))
             add_linear("layer_small_m", "o", dev(d["x_o"]), *qw(d["w_o"]))
-            gu = add_linear("layer_small_m", "gate_up", dev(d["x_ffn"]), *qw(d["w_gu"]))
-            add_linear("layer_small_m", "down", gu, *qw(d["w_dn"]), act="silu_mul")
+            h = add_linear("layer_small_m", "gate_up", dev(d["x_ffn"]), *qw_gated(d["w_gu"]), act="gate_silu")
+            add_linear("layer_small_m", "down", h, *qw(d["w_dn"]))
             ids, tw = dev(d["ids"].astype(np.int32)), dev(d["topk_w"])
-            g2 = add_moe("layer_small_m", "moe_gate_up", dev(d["x_moe"]), ids, *qw(d["w_gu_moe"]),
-                         "tokens", "none", "permuted")
-            add_moe("layer_small_m", "moe_down", g2, ids, *qw(d["w_dn_moe"]), "permuted", "silu_mul",
+            h2 = add_moe("layer_small_m", "moe_gate_up", dev(d["x_moe"]), ids, *qw_gated(d["w_gu_moe"]),
+                         "tokens", "gate_silu", "permuted")
+            add_moe("layer_small_m", "moe_down", h2, ids, *qw(d["w_dn_moe"]), "permuted", "none",
                     "combined", topk_w=tw)
             self.config["layer_small_m"] = "512 rows (32 requests x 16 beams); one layer: QKV, O, FFN 8192, MoE 4096"
             del d
@@ -379,10 +386,11 @@ def gemm_source_hash():
 
 def dominant_algorithmic_bytes():
     """Bytes the MoE gate/up grouped GEMM must move at least once: its FP8 A rows (one per
-    routed slot) and expert weights, the FP32 scales, and its FP16 output."""
+    routed slot) and expert weights, the FP32 scales, and its FP16 output h = silu(g) * u
+    (F columns per routed slot; the gated layout never writes g and u)."""
     t, k, f, e, top_k = 16384, 2048, 4096, 32, 2
     r, n = t * top_k, 2 * f
-    return r * k + e * n * k + 4 * (r + e * n) + 2 * r * n
+    return r * k + e * n * k + 4 * (r + e * n) + 2 * r * f
 
 
 def traffic_summary(fetch_dir, write_dir, out, only=None, steps=None):

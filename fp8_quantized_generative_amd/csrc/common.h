@@ -22,7 +22,7 @@ __device__ __forceinline__ uint32_t float_to_half_bits(float f) {
 }
 
 // h = fl16(fl32(silu(g) * u)) for two packed FP16 pairs, computed in FP32 with
-// silu(g) = g / (1 + exp(-g)).  The quantizer's SiLU*up input transform and the GEMM's gated
+// silu(g) = g * rcp(1 + exp(-g)) (hardware exp2 and reciprocal).  The quantizer's SiLU*up input transform and the GEMM's gated
 // output both use this one definition, so the two FFN formulations give identical h.
 __device__ __forceinline__ uint32_t silu_mul_pair(uint32_t g2, uint32_t u2) {
   uint32_t out = 0;
@@ -30,7 +30,9 @@ __device__ __forceinline__ uint32_t silu_mul_pair(uint32_t g2, uint32_t u2) {
   for (int i = 0; i < 2; ++i) {
     float g = half_bits_to_float((g2 >> (16 * i)) & 0xFFFFu);
     float u = half_bits_to_float((u2 >> (16 * i)) & 0xFFFFu);
-    float silu = __fdividef(g, 1.0f + __expf(-g));
+    // exp through the hardware exp2 and the quotient through the hardware reciprocal (about
+    // one FP32 ulp each): the correctly rounded division would cost ten instructions per value
+    float silu = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
     float p = silu * u;
     // FP32 product, then FP16: the empty asm keeps the compiler from fusing the multiply
     // into the conversion (a single rounding) in some contexts and not in others

@@ -54,7 +54,7 @@ def test_traffic_scaling(tmp_path):
 
 def test_algorithmic_bytes_of_the_dominant_call():
     r, k, n, e = 32768, 2048, 8192, 32
-    assert bench.dominant_algorithmic_bytes() == r * k + e * n * k + 4 * (r + e * n) + 2 * r * n
+    assert bench.dominant_algorithmic_bytes() == r * k + e * n * k + 4 * (r + e * n) + 2 * r * (n // 2)
 
 
 def test_more_than_one_gpu_exits_with_a_message():
