@@ -235,7 +235,7 @@ def cpu_baseline(seconds_hint=15.0):
     except Exception:  # noqa: BLE001
         blas_threads = None
     cores = len(os.sched_getaffinity(0))
-    rows = 64
+    rows = 320  # about 10 s of float64 work on 16 host cores
     d2 = workloads.make(2, m=rows)
     d3 = workloads.make(3, m=rows)
     d4 = workloads.make(4, t=rows, e=4)
@@ -268,10 +268,10 @@ def cpu_baseline(seconds_hint=15.0):
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "blas_threads": blas_threads, "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "64 token rows through each linear of the step: attention QKV and O, dense FFN "
-                      "gate/up + SiLU + down, and the MoE expert FFN (F = 4096) over 64 tokens, top-2 of 4 "
+            "sample": "%d token rows through each linear of the step: attention QKV and O, dense FFN "
+                      "gate/up + SiLU + down, and the MoE expert FFN (F = 4096) over %d tokens, top-2 of 4 "
                       "full-size experts; "
-                      "float64 exact GEMMs; weights quantized beforehand (untimed)"}
+                      "float64 exact GEMMs; weights quantized beforehand (untimed)" % (rows, rows)}
 
 
 def _find(path, patterns):
