@@ -251,7 +251,7 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const i
   if (ds) as = ds;
 
   hipStream_t s = (hipStream_t)stream;
-  const int kind = rq::pick_grouped(R, E);
+  const int kind = rq::pick_grouped(R, E, N);
   if (rq::launch_moe_plan(topk_ids, T, top_k, E, rq::tile_rows(kind), offsets, tile_start, tile_table,
                           perm, pos, block_hist, s) != hipSuccess)
     return RQ_ERR_HIP;

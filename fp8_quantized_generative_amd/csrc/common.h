@@ -91,7 +91,7 @@ constexpr int kMinTileRows = 64;  // fewest rows of any tile shape (sizes the Mo
 
 hipError_t launch_gemm_dense(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemm_grouped(const GemmArgs& g, int kind, hipStream_t stream);
-int pick_grouped(int64_t R, int64_t E);        // tile shape for R routed rows over E experts
+int pick_grouped(int64_t R, int64_t E, int64_t N);  // tile shape for R routed rows over E experts
 int tile_rows(int kind);                       // M rows of a tile shape
 int64_t grouped_max_mtiles(int64_t R, int64_t E, int tile_m);
 

@@ -720,11 +720,20 @@ hipError_t launch_dense(const GemmArgs& g, hipStream_t stream) {
 
 }  // namespace
 
-int pick_grouped(int64_t R, int64_t E) {
+int pick_grouped(int64_t R, int64_t E, int64_t N) {
   const int forced = tile_override();
   if (forced == kTileBig || forced == kTileThinWide) return forced;
-  // experts average R / E rows: 64-row tiles once 256-row tiles would be mostly padding
-  return R >= 192 * E ? kTileBig : kTileThinWide;
+  // Rounds of resident workgroups (256 CUs; one 256x256 or two 64x256 workgroups per CU)
+  // each shape needs, counting each expert's last M-tile as half full.  A tile's K loop
+  // costs about the same in both shapes (measured), so fewer rounds win; ties go to the
+  // 256-row tiles, which read each expert's weights fewer times.
+  const int64_t nonempty = E < R ? E : R;
+  auto rounds = [&](int bm, int bn, int per_cu) {
+    const int64_t tiles = ((R + bm - 1) / bm + nonempty / 2) * ((N + bn - 1) / bn);
+    const int64_t cap = 256 * per_cu;
+    return (tiles + cap - 1) / cap;
+  };
+  return rounds(256, 256, 1) <= rounds(64, 256, 2) ? kTileBig : kTileThinWide;
 }
 
 int tile_rows(int kind) { return kTiles[kind].bm; }
