@@ -111,6 +111,7 @@ class Path:
         self.rq, self.torch = rq, torch
         dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
         self.calls = []     # (workload, label, kind, flops, bytes_moved, fn)
+        self.qbytes = []    # per call: bytes the row quantizer must move
         self.flops = 0
         want = set(only.split(",")) if only else {"attention", "ffn", "moe", "layer_small_m"}
 
@@ -133,6 +134,8 @@ class Path:
             by = x.numel() * 2 + wq.numel() + out.numel() * 2
             self.calls.append((work, label, "linear", fl, by,
                                lambda: rq.linear(x, wq, ws, act=act, out=out, workspace=ws_t)))
+            # the row quantizer: FP16 rows in, E4M3 rows and FP32 scales out
+            self.qbytes.append(x.numel() * 2 + m * k + 4 * m)
             self.flops += fl
             return out
 
@@ -149,6 +152,9 @@ class Path:
             self.calls.append((work, label, "moe", fl, by,
                                lambda: rq.moe_grouped_linear(x, ids, wq, ws, il, act, ol, topk_w=topk_w,
                                                              out=out, workspace=ws_t)))
+            # the row quantizer reads each input row once and writes one E4M3 row and scale per
+            # routed slot
+            self.qbytes.append(x.numel() * 2 + r * k + 4 * r)
             self.flops += fl
             return out
 
@@ -193,12 +199,14 @@ class Path:
             del d
         if not hasattr(self, "dominant"):
             self.dominant = max(range(len(self.calls)), key=lambda i: self.calls[i][3])
+        self.quant_dominant = max(range(len(self.calls)), key=lambda i: self.qbytes[i])
         torch.cuda.synchronize()
 
-    def step(self, hook=None):
+    def step(self, hooks=()):
         for i, c in enumerate(self.calls):
-            if hook is not None and i == hook[0]:
-                self.rq._lib.load().rq_time_next_kernel(hook[1], hook[2], hook[3])
+            for h in hooks:
+                if i == h[0]:
+                    self.rq._lib.load().rq_time_next_kernel(h[1], h[2], h[3])
             c[5]()
 
 
@@ -217,15 +225,17 @@ def kernel_breakdown(path, hip, reps=5):
                 fn()
                 ts.append(hip.elapsed_ms(a, b))
             res[kname] = float(np.median(ts))
+        qgbs = path.qbytes[i] / (res["quant"] * 1e-3) / 1e9
         rows.append({"workload": work, "call": label, "gemm_us": round(res["gemm"] * 1e3, 2),
                      "gemm_tflops": round(fl / (res["gemm"] * 1e-3) / 1e12, 1),
                      "gemm_frac_fp8_peak": round(fl / (res["gemm"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
                      "gemm_min_hbm_gbs": round(by / (res["gemm"] * 1e-3) / 1e9, 1),
-                     "quant_us": round(res["quant"] * 1e3, 2)})
+                     "quant_us": round(res["quant"] * 1e3, 2), "quant_gbs": round(qgbs, 1),
+                     "quant_frac_hbm": round(qgbs / HBM_PEAK_GBS, 4)})
     return rows
 
 
-def cpu_baseline(seconds_hint=15.0):
+def cpu_baseline(target_s=12.0):
     """The CPU oracle on a bounded sample of the same workloads (rows sampled per linear)."""
     import workloads
     from oracle import ffn, linear, moe, quant
@@ -235,43 +245,57 @@ def cpu_baseline(seconds_hint=15.0):
     except Exception:  # noqa: BLE001
         blas_threads = None
     cores = len(os.sched_getaffinity(0))
-    rows = 320  # about 10 s of float64 work on 16 host cores
-    d2 = workloads.make(2, m=rows)
-    d3 = workloads.make(3, m=rows)
-    d4 = workloads.make(4, t=rows, e=4)
-    # offline weight quantization (untimed); one expert's weights for the MoE sample
-    wqkv = quant.quantize_rows(d2["w_qkv"])
-    wo = quant.quantize_rows(d2["w_o"])
-    wgu = quant.quantize_rows(d3["w_gu"])
-    wdn = quant.quantize_rows(d3["w_dn"])
-    egu = [quant.quantize_rows(d4["w_gu"][e]) for e in range(4)]
-    edn = [quant.quantize_rows(d4["w_dn"][e]) for e in range(4)]
+    # offline weight quantization (untimed); the weights do not depend on the row count.
+    # Four full-size experts serve the MoE sample.
+    w2, w3, w4 = workloads.make(2, m=64), workloads.make(3, m=64), workloads.make(4, t=64, e=4)
+    wqkv = quant.quantize_rows(w2["w_qkv"])
+    wo = quant.quantize_rows(w2["w_o"])
+    wgu = quant.quantize_rows(w3["w_gu"])
+    wdn = quant.quantize_rows(w3["w_dn"])
+    egu = [quant.quantize_rows(w4["w_gu"][e]) for e in range(4)]
+    edn = [quant.quantize_rows(w4["w_dn"][e]) for e in range(4)]
     egu_q = np.stack([q for q, _ in egu]); egu_s = np.stack([s for _, s in egu])
     edn_q = np.stack([q for q, _ in edn]); edn_s = np.stack([s for _, s in edn])
-    flops = 0
-    t0 = time.perf_counter()
-    xq, xs = quant.quantize_rows(d2["x"])
-    linear.linear(xq, xs, *wqkv)
-    flops += 2 * rows * 6144 * 2048
-    aq, as_ = quant.quantize_rows(d2["attn_out"])
-    linear.linear(aq, as_, *wo)
-    flops += 2 * rows * 2048 * 2048
-    xq, xs = quant.quantize_rows(d3["x"])
-    gu = linear.linear(xq, xs, *wgu)
-    hq, hs = quant.quantize_rows(ffn.silu_mul(gu, 8192))
-    linear.linear(hq, hs, *wdn)
-    flops += 2 * rows * 16384 * 2048 + 2 * rows * 2048 * 8192
-    r1 = moe.grouped_linear(d4["x"], moe.IN_TOKENS, moe.ACT_NONE, d4["ids"], egu_q, egu_s)
-    moe.grouped_linear(r1["y"], moe.IN_PERMUTED, moe.ACT_SILU_MUL, d4["ids"], edn_q, edn_s,
-                       moe.OUT_COMBINED, d4["topk_w"])
-    flops += 2 * rows * 2 * 8192 * 2048 + 2 * rows * 2 * 2048 * 4096
-    dt = time.perf_counter() - t0
+    del w2, w3, w4
+
+    def sample(rows):
+        d2 = workloads.make(2, m=rows)
+        d3 = workloads.make(3, m=rows)
+        d4 = workloads.make(4, t=rows, e=4)
+        flops = 0
+        t0 = time.perf_counter()
+        xq, xs = quant.quantize_rows(d2["x"])
+        linear.linear(xq, xs, *wqkv)
+        flops += 2 * rows * 6144 * 2048
+        aq, as_ = quant.quantize_rows(d2["attn_out"])
+        linear.linear(aq, as_, *wo)
+        flops += 2 * rows * 2048 * 2048
+        xq, xs = quant.quantize_rows(d3["x"])
+        gu = linear.linear(xq, xs, *wgu)
+        hq, hs = quant.quantize_rows(ffn.silu_mul(gu, 8192))
+        linear.linear(hq, hs, *wdn)
+        flops += 2 * rows * 16384 * 2048 + 2 * rows * 2048 * 8192
+        r1 = moe.grouped_linear(d4["x"], moe.IN_TOKENS, moe.ACT_NONE, d4["ids"], egu_q, egu_s)
+        moe.grouped_linear(r1["y"], moe.IN_PERMUTED, moe.ACT_SILU_MUL, d4["ids"], edn_q, edn_s,
+                           moe.OUT_COMBINED, d4["topk_w"])
+        flops += 2 * rows * 2 * 8192 * 2048 + 2 * rows * 2 * 2048 * 4096
+        return flops, time.perf_counter() - t0
+
+    # The oracle's cost is a fixed part (decoding each weight matrix) plus a part per row:
+    # two short passes fit both, and the sample gets the rows that make it about target_s
+    # seconds on this host.
+    _, t_a = sample(64)
+    _, t_b = sample(256)
+    per_row = max((t_b - t_a) / 192, 1e-6)
+    fixed = max(t_a - 64 * per_row, 0.0)
+    rows = int(max(64, min(8192, (target_s - fixed) / per_row)) // 64 * 64)
+    flops, dt = sample(rows)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "blas_threads": blas_threads, "kind": "oracle", "seconds": round(dt, 2),
             "sample": "%d token rows through each linear of the step: attention QKV and O, dense FFN "
                       "gate/up + SiLU + down, and the MoE expert FFN (F = 4096) over %d tokens, top-2 of 4 "
-                      "full-size experts; "
-                      "float64 exact GEMMs; weights quantized beforehand (untimed)" % (rows, rows)}
+                      "full-size experts; float64 exact GEMMs; weights quantized beforehand (untimed); "
+                      "rows sized from 64- and 256-row passes to about %.0f s" % (rows, rows, target_s)}
 
 
 def _find(path, patterns):
@@ -473,10 +497,12 @@ def main():
     torch.cuda.synchronize()
 
     evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    qevs = [(hip.event(), hip.event()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        path.step(hook=(path.dominant, _lib.RQ_KERNEL_GEMM, evs[s][0], evs[s][1]))
+        path.step(hooks=((path.dominant, _lib.RQ_KERNEL_GEMM, evs[s][0], evs[s][1]),
+                         (path.quant_dominant, _lib.RQ_KERNEL_QUANT, qevs[s][0], qevs[s][1])))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
@@ -493,6 +519,14 @@ def main():
                 "kernel": "gemm_fp8_kernel<grouped> (%s %s)" % (dom[0], dom[1]),
                 "flops_per_launch": dom[3], "avg_launch_us": round(dom_ms * 1e3, 2)}
 
+    qcall = path.calls[path.quant_dominant]
+    q_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in qevs]))
+    q_gbs = path.qbytes[path.quant_dominant] / (q_ms * 1e-3) / 1e9
+    quant_roofline = {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(q_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                      "kernel": "quant_rows (%s %s)" % (qcall[0], qcall[1]),
+                      "bytes_per_launch": path.qbytes[path.quant_dominant], "avg_launch_us": round(q_ms * 1e3, 2)}
+
     result = {
         "metric": "FP8 linear TFLOP/s (dense + MoE grouped) and % of MI355X FP8 MFMA peak",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -503,6 +537,7 @@ def main():
         "config": {"workload": "+".join(path.config) + " (full-size W8A8 FP8 linears, one step each)",
                    **path.config, "gflop_per_step": round(path.flops / 1e9, 2)},
         "roofline": roofline,
+        "quant_roofline": quant_roofline,
     }
     if args.calibrate_copy_mb:
         # an elementwise kernel that reads and writes exactly n bytes (a plain copy, x * 1)
