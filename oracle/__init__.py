@@ -25,6 +25,8 @@ Arithmetic is float64 and integers.  Every rounding is explicit.  Modules:
                the parity tolerance.
 * ``ffn``    - the SiLU(gate) * up intermediate of the dense and expert FFNs.
 * ``moe``    - the MoE routing plan, grouped linear over experts and the weighted combine.
+* ``wscale`` - weight scales per tensor and per 128 x 128 block (page "FP8量化在生成式推荐
+               系统OneRec-V2中的优化实践", §2.1 / §2.2) and the linear that uses them.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py`` against
 values fixed independently of this code (the OCP format definition, closed forms,
@@ -32,6 +34,6 @@ brute force over exact rationals, PyTorch's own float8_e4m3fn conversion and SiL
 No function is "parity unpinned".
 """
 
-from . import e4m3, quant, linear, ffn, moe  # noqa: F401
+from . import e4m3, quant, linear, ffn, moe, wscale  # noqa: F401
 
-__all__ = ["e4m3", "quant", "linear", "ffn", "moe"]
+__all__ = ["e4m3", "quant", "linear", "ffn", "moe", "wscale"]

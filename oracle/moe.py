@@ -26,7 +26,7 @@ summed in float64 and rounded once.
 
 import numpy as np
 
-from . import ffn, linear, quant
+from . import ffn, linear, quant, wscale
 
 IN_TOKENS, IN_PERMUTED = 0, 1
 OUT_PERMUTED, OUT_COMBINED = 0, 1
@@ -54,11 +54,13 @@ def plan(ids, num_experts):
     return counts, offsets, perm, pos
 
 
-def grouped_linear(x, in_layout, act, ids, w_q, s_w, out_layout=OUT_PERMUTED, topk_w=None):
+def grouped_linear(x, in_layout, act, ids, w_q, s_w, out_layout=OUT_PERMUTED, topk_w=None,
+                   gran=wscale.CHANNEL):
     """Oracle of one grouped call.
 
     ``x`` FP16 [T or R, K or 2K]; ``ids`` int [T, top_k]; ``w_q`` uint8 [E, N, K];
-    ``s_w`` float32 [E, N]; ``topk_w`` FP16 [T, top_k] for the combined output.
+    ``s_w`` float32 [E, N] (or per expert the layout of ``gran``, see ``oracle.wscale``);
+    ``topk_w`` FP16 [T, top_k] for the combined output.
 
     Returns a dict with ``y`` (FP16 [R, N] permuted or [T, N] combined), ``y_perm``
     (FP16 [R, N]), ``a_q``/``a_scale`` (the quantized GEMM input: T rows for TOKENS, R
@@ -87,7 +89,10 @@ def grouped_linear(x, in_layout, act, ids, w_q, s_w, out_layout=OUT_PERMUTED, to
             continue
         r = np.arange(lo, hi)
         src = perm[r] // top_k if in_layout == IN_TOKENS else r
-        y_perm[r] = linear.linear(a_q[src], a_scale[src], w_q[e], s_w[e])
+        if gran == wscale.CHANNEL:
+            y_perm[r] = linear.linear(a_q[src], a_scale[src], w_q[e], s_w[e])
+        else:
+            y_perm[r] = wscale.linear(a_q[src], a_scale[src], w_q[e], s_w[e], gran)
 
     out = {"y_perm": y_perm, "a_q": a_q, "a_scale": a_scale, "h": h,
            "counts": counts, "offsets": offsets, "perm": perm, "pos": pos}
@@ -109,7 +114,7 @@ def combine(y_perm, pos, topk_w):
     return acc.astype(np.float16)
 
 
-def grouped_linear_check(y_gpu_perm, a_q, a_scale, in_layout, ids, w_q, s_w):
+def grouped_linear_check(y_gpu_perm, a_q, a_scale, in_layout, ids, w_q, s_w, gran=wscale.CHANNEL):
     """Stage check of a GPU permuted GEMM output against the GPU's own quantized input.
 
     Returns ``(ok, worst |d|/tol)`` over all permuted rows.
@@ -123,7 +128,10 @@ def grouped_linear_check(y_gpu_perm, a_q, a_scale, in_layout, ids, w_q, s_w):
             continue
         r = np.arange(lo, hi)
         src = perm[r] // top_k if in_layout == IN_TOKENS else r
-        good, ratio, _ = linear.check(y_gpu_perm[r], a_q[src], a_scale[src], w_q[e], s_w[e])
+        if gran == wscale.CHANNEL:
+            good, ratio, _ = linear.check(y_gpu_perm[r], a_q[src], a_scale[src], w_q[e], s_w[e])
+        else:
+            good, ratio, _ = wscale.check(y_gpu_perm[r], a_q[src], a_scale[src], w_q[e], s_w[e], gran)
         ok &= good
         worst = max(worst, ratio)
     return ok, worst
