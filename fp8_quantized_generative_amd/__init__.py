@@ -4,7 +4,8 @@ Python face of the C ABI in ``include/rq_fp8.h`` (``librq_fp8.so``).  Every step
 computation runs in the library's HIP kernels; this module only marshals arguments.
 PyTorch provides device memory and the current stream.
 
-* ``quant_weights(w)``                         offline per-output-channel E4M3 quantization
+* ``quant_weights(w, wscale=...)``            offline E4M3 weight quantization (scales per
+                                               output channel, per tensor or per 128x128 block)
 * ``linear(x, w_q, w_scale, act=...)``         per-token quantization + FP8 GEMM + FP16 epilogue
 * ``moe_grouped_linear(x, ids, w_q, w_scale, ...)``  routing plan + grouped GEMM (+ combine)
 * ``linear_workspace_size`` / ``moe_workspace_size``  scratch sizes for caller-held workspaces
@@ -16,11 +17,23 @@ import torch
 
 from . import _lib
 from ._lib import (RQ_ACT_GATE_SILU, RQ_ACT_NONE, RQ_ACT_SILU_MUL, RQ_MOE_IN_PERMUTED, RQ_MOE_IN_TOKENS,  # noqa: F401
-                   RQ_MOE_OUT_COMBINED, RQ_MOE_OUT_PERMUTED, DebugOut, RqError)
+                   RQ_MOE_OUT_COMBINED, RQ_MOE_OUT_PERMUTED, RQ_WSCALE_BLOCK128, RQ_WSCALE_CHANNEL,
+                   RQ_WSCALE_TENSOR, DebugOut, RqError)
 
 ACTS = {"none": RQ_ACT_NONE, "silu_mul": RQ_ACT_SILU_MUL, "gate_silu": RQ_ACT_GATE_SILU}
 IN_LAYOUTS = {"tokens": RQ_MOE_IN_TOKENS, "permuted": RQ_MOE_IN_PERMUTED}
 OUT_LAYOUTS = {"permuted": RQ_MOE_OUT_PERMUTED, "combined": RQ_MOE_OUT_COMBINED}
+WSCALES = {"channel": RQ_WSCALE_CHANNEL, "tensor": RQ_WSCALE_TENSOR, "block128": RQ_WSCALE_BLOCK128}
+
+
+def scale_shape(lead, n, k, wscale):
+    """Shape of the FP32 weight scales of ``lead`` matrices [N, K] at granularity ``wscale``."""
+    g = _code(WSCALES, wscale, "wscale")
+    if g == RQ_WSCALE_TENSOR:
+        return tuple(lead) if lead else (1,)
+    if g == RQ_WSCALE_BLOCK128:
+        return tuple(lead) + (n // 128, k // 128)
+    return tuple(lead) + (n,)
 
 
 def _code(table, v, what):
@@ -61,20 +74,27 @@ def _workspace(nbytes, device, workspace):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
-def quant_weights(w, w_q=None, w_scale=None, stream=None):
-    """FP16 [N, K] or [B, N, K] -> (E4M3 bytes of the same shape, FP32 scales [N] / [B, N])."""
+def quant_weights(w, w_q=None, w_scale=None, stream=None, wscale="channel"):
+    """FP16 [N, K] or [B, N, K] -> (E4M3 bytes of the same shape, FP32 scales).
+
+    Scales per ``wscale``: "channel" [N] / [B, N]; "tensor" [1] / [B]; "block128"
+    [N/128, K/128] / [B, N/128, K/128]."""
+    g = _code(WSCALES, wscale, "wscale")
     _dev(w, torch.float16, "w")
     if w.dim() not in (2, 3):
         raise ValueError("w must be [N, K] or [B, N, K]")
     b, n, k = (1,) + tuple(w.shape) if w.dim() == 2 else tuple(w.shape)
+    lead = tuple(w.shape[:-2])
     if w_q is None:
         w_q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
     if w_scale is None:
-        w_scale = torch.empty(w.shape[:-1], dtype=torch.float32, device=w.device)
+        w_scale = torch.empty(scale_shape(lead, n, k, g), dtype=torch.float32, device=w.device)
     _dev(w_q, torch.uint8, "w_q")
     _dev(w_scale, torch.float32, "w_scale")
-    st = _lib.load().rq_fp8_quant_weights(_ptr(w), b, n, k, _ptr(w_q), _ptr(w_scale), _stream(w, stream))
-    _lib.check("rq_fp8_quant_weights", st)
+    _shape(w_q, w.shape, "w_q")
+    _shape(w_scale, scale_shape(lead, n, k, g), "w_scale")
+    st = _lib.load().rq_fp8_quant_weights_ex(_ptr(w), b, n, k, g, _ptr(w_q), _ptr(w_scale), _stream(w, stream))
+    _lib.check("rq_fp8_quant_weights_ex", st)
     return w_q, w_scale
 
 
@@ -98,15 +118,17 @@ def _debug(debug, q_rows, h_rows, k, act, device):
     return d, s
 
 
-def linear(x, w_q, w_scale, act="none", out=None, workspace=None, debug=False, stream=None):
+def linear(x, w_q, w_scale, act="none", out=None, workspace=None, debug=False, stream=None, wscale="channel"):
     """W8A8 FP8 linear: FP16 x [M, K] (or [M, 2K] for ``act='silu_mul'``) -> FP16 y [M, N]
     (or h [M, N/2] for ``act='gate_silu'``, whose weight rows interleave 32 gate and 32 up
     features; see ``interleave_gate_up``).
 
     With ``debug=True`` returns ``(y, {"a_q", "a_scale", "h"})``: the quantized GEMM input
-    (and the SiLU*up rows).
+    (and the SiLU*up rows).  ``wscale`` names the granularity of ``w_scale`` (see
+    ``quant_weights``).
     """
     a = _code(ACTS, act, "act")
+    g = _code(WSCALES, wscale, "wscale")
     _dev(x, torch.float16, "x")
     _dev(w_q, torch.uint8, "w_q")
     _dev(w_scale, torch.float32, "w_scale")
@@ -125,20 +147,22 @@ def linear(x, w_q, w_scale, act="none", out=None, workspace=None, debug=False, s
     ws_bytes = lib.rq_fp8_linear_workspace_size(m, k, a)
     ws = _workspace(ws_bytes, x.device, workspace)
     dbg, dbg_s = _debug(debug, m, m, k, a, x.device)
-    st = lib.rq_fp8_linear(_ptr(x), m, k, a, _ptr(w_q), _ptr(w_scale), n, _ptr(out), _ptr(ws),
-                           ws.numel(), ctypes.byref(dbg_s) if dbg_s is not None else None,
-                           _stream(x, stream))
-    _lib.check("rq_fp8_linear", st)
+    _shape(w_scale, scale_shape((), n, k, g), "w_scale")
+    st = lib.rq_fp8_linear_ex(_ptr(x), m, k, a, _ptr(w_q), _ptr(w_scale), g, n, _ptr(out), _ptr(ws),
+                              ws.numel(), ctypes.byref(dbg_s) if dbg_s is not None else None,
+                              _stream(x, stream))
+    _lib.check("rq_fp8_linear_ex", st)
     return (out, dbg) if debug else out
 
 
 def moe_grouped_linear(x, topk_ids, w_q, w_scale, in_layout="tokens", act="none",
                        out_layout="permuted", topk_w=None, out=None, workspace=None,
-                       debug=False, stream=None):
+                       debug=False, stream=None, wscale="channel"):
     """Expert grouped W8A8 linear.
 
     ``x``: FP16 [T, K*] (tokens) or [T*top_k, K*] (permuted), K* = 2K for ``silu_mul``;
-    ``topk_ids``: int32 [T, top_k]; ``w_q``: uint8 [E, N, K]; ``w_scale``: FP32 [E, N];
+    ``topk_ids``: int32 [T, top_k]; ``w_q``: uint8 [E, N, K]; ``w_scale``: FP32 [E, N] (or the
+    ``wscale`` layout with E matrices, see ``quant_weights``);
     ``topk_w``: FP16 [T, top_k] for ``out_layout='combined'``.
     Returns FP16 [T*top_k, N] (permuted) or [T, N] (combined), plus the debug dict when
     ``debug=True``: ``a_q`` / ``a_scale`` hold the GEMM operand, one row per routed slot in
@@ -147,6 +171,7 @@ def moe_grouped_linear(x, topk_ids, w_q, w_scale, in_layout="tokens", act="none"
     il = _code(IN_LAYOUTS, in_layout, "in_layout")
     a = _code(ACTS, act, "act")
     ol = _code(OUT_LAYOUTS, out_layout, "out_layout")
+    g = _code(WSCALES, wscale, "wscale")
     _dev(x, torch.float16, "x")
     _dev(topk_ids, torch.int32, "topk_ids")
     _dev(w_q, torch.uint8, "w_q")
@@ -168,11 +193,12 @@ def moe_grouped_linear(x, topk_ids, w_q, w_scale, in_layout="tokens", act="none"
     ws_bytes = lib.rq_fp8_moe_workspace_size(t, top_k, e, n, k, il, a, ol)
     ws = _workspace(ws_bytes, x.device, workspace)
     dbg, dbg_s = _debug(debug, r, rows, k, a, x.device)
-    st = lib.rq_fp8_moe_grouped_linear(
-        _ptr(x), il, a, _ptr(topk_ids), _ptr(topk_w), t, top_k, _ptr(w_q), _ptr(w_scale), e, n, k,
+    _shape(w_scale, scale_shape((e,), n, k, g), "w_scale")
+    st = lib.rq_fp8_moe_grouped_linear_ex(
+        _ptr(x), il, a, _ptr(topk_ids), _ptr(topk_w), t, top_k, _ptr(w_q), _ptr(w_scale), g, e, n, k,
         _ptr(out), ol, _ptr(ws), ws.numel(), ctypes.byref(dbg_s) if dbg_s is not None else None,
         _stream(x, stream))
-    _lib.check("rq_fp8_moe_grouped_linear", st)
+    _lib.check("rq_fp8_moe_grouped_linear_ex", st)
     return (out, dbg) if debug else out
 
 

@@ -122,10 +122,12 @@ int rq_device_supported(int device) {
   return ok ? 1 : 0;
 }
 
-int rq_fp8_quant_weights(const uint16_t* w, int64_t B, int64_t N, int64_t K, uint8_t* w_q,
-                         float* w_scale, void* stream) {
+int rq_fp8_quant_weights_ex(const uint16_t* w, int64_t B, int64_t N, int64_t K, int w_gran, uint8_t* w_q,
+                            float* w_scale, void* stream) {
+  if (w_gran != RQ_WSCALE_CHANNEL && w_gran != RQ_WSCALE_TENSOR && w_gran != RQ_WSCALE_BLOCK128) return RQ_ERR_ARG;
   if (B < 0 || N < 0 || K <= 0) return RQ_ERR_SHAPE;
   if (K % 16 != 0) return RQ_ERR_ALIGN;
+  if (w_gran == RQ_WSCALE_BLOCK128 && (N % rq::kScaleBlock != 0 || K % rq::kScaleBlock != 0)) return RQ_ERR_ALIGN;
   if (B > 0 && N > 0 && B > INT64_MAX / N) return RQ_ERR_SHAPE;
   const int64_t rows = B * N;
   if (rows == 0) return RQ_OK;
@@ -134,9 +136,19 @@ int rq_fp8_quant_weights(const uint16_t* w, int64_t B, int64_t N, int64_t K, uin
   const int dev = check_device();
   if (dev != RQ_OK) return dev;
   Hook hook(RQ_KERNEL_QUANT, (hipStream_t)stream);
-  hipError_t e = rq::launch_quant_rows(w, rows, K, RQ_ACT_NONE, w_q, w_scale, nullptr, nullptr, 0,
-                                       (hipStream_t)stream);
+  hipError_t e;
+  if (w_gran == RQ_WSCALE_TENSOR)
+    e = rq::launch_quant_tensor(w, B, N, K, w_q, w_scale, (hipStream_t)stream);
+  else if (w_gran == RQ_WSCALE_BLOCK128)
+    e = rq::launch_quant_blocks(w, B, N, K, w_q, w_scale, (hipStream_t)stream);
+  else
+    e = rq::launch_quant_rows(w, rows, K, RQ_ACT_NONE, w_q, w_scale, nullptr, nullptr, 0, (hipStream_t)stream);
   return e == hipSuccess ? RQ_OK : RQ_ERR_HIP;
+}
+
+int rq_fp8_quant_weights(const uint16_t* w, int64_t B, int64_t N, int64_t K, uint8_t* w_q,
+                         float* w_scale, void* stream) {
+  return rq_fp8_quant_weights_ex(w, B, N, K, RQ_WSCALE_CHANNEL, w_q, w_scale, stream);
 }
 
 size_t rq_fp8_linear_workspace_size(int64_t M, int64_t K, int act) {
@@ -145,12 +157,14 @@ size_t rq_fp8_linear_workspace_size(int64_t M, int64_t K, int act) {
   return align_up((size_t)(M * K)) + align_up((size_t)M * sizeof(float));
 }
 
-int rq_fp8_linear(const uint16_t* x, int64_t M, int64_t K, int act, const uint8_t* w_q,
-                  const float* w_scale, int64_t N, uint16_t* y, void* workspace,
-                  size_t workspace_bytes, const rq_debug_out* dbg, void* stream) {
+int rq_fp8_linear_ex(const uint16_t* x, int64_t M, int64_t K, int act, const uint8_t* w_q,
+                     const float* w_scale, int w_gran, int64_t N, uint16_t* y, void* workspace,
+                     size_t workspace_bytes, const rq_debug_out* dbg, void* stream) {
   if (act != RQ_ACT_NONE && act != RQ_ACT_SILU_MUL && act != RQ_ACT_GATE_SILU) return RQ_ERR_ARG;
+  if (w_gran != RQ_WSCALE_CHANNEL && w_gran != RQ_WSCALE_TENSOR && w_gran != RQ_WSCALE_BLOCK128) return RQ_ERR_ARG;
   if (M < 0 || K <= 0 || N <= 0) return RQ_ERR_SHAPE;
   if (K % 16 != 0 || N % 16 != 0 || (act == RQ_ACT_GATE_SILU && N % 64 != 0)) return RQ_ERR_ALIGN;
+  if (w_gran == RQ_WSCALE_BLOCK128 && (N % rq::kScaleBlock != 0 || K % rq::kScaleBlock != 0)) return RQ_ERR_ALIGN;
   if (K > kMaxK || N > (int64_t)1 << 30 || M > (int64_t)1 << 31) return RQ_ERR_SHAPE;
   if (M * K > kMaxOperandBytes || N * K > kMaxOperandBytes) return RQ_ERR_SHAPE;
   if (!w_q || !w_scale) return RQ_ERR_NULL;
@@ -192,8 +206,16 @@ int rq_fp8_linear(const uint16_t* x, int64_t M, int64_t K, int act, const uint8_
   g.K = (int32_t)K;
   g.E = 1;
   g.gate = act == RQ_ACT_GATE_SILU ? 1 : 0;
+  g.b_gran = w_gran;
   Hook hook(RQ_KERNEL_GEMM, s);
   return rq::launch_gemm_dense(g, s) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
+}
+
+int rq_fp8_linear(const uint16_t* x, int64_t M, int64_t K, int act, const uint8_t* w_q,
+                  const float* w_scale, int64_t N, uint16_t* y, void* workspace,
+                  size_t workspace_bytes, const rq_debug_out* dbg, void* stream) {
+  return rq_fp8_linear_ex(x, M, K, act, w_q, w_scale, RQ_WSCALE_CHANNEL, N, y, workspace, workspace_bytes, dbg,
+                          stream);
 }
 
 size_t rq_fp8_moe_workspace_size(int64_t T, int top_k, int64_t E, int64_t N, int64_t K,
@@ -204,17 +226,19 @@ size_t rq_fp8_moe_workspace_size(int64_t T, int top_k, int64_t E, int64_t N, int
          align_up(l.tile_table) + align_up(l.perm) + align_up(l.pos) + align_up(l.block_hist) + align_up(l.y_perm);
 }
 
-int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const int32_t* topk_ids,
-                              const uint16_t* topk_w, int64_t T, int top_k, const uint8_t* w_q,
-                              const float* w_scale, int64_t E, int64_t N, int64_t K, uint16_t* y,
-                              int out_layout, void* workspace, size_t workspace_bytes,
-                              const rq_debug_out* dbg, void* stream) {
+int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act, const int32_t* topk_ids,
+                                 const uint16_t* topk_w, int64_t T, int top_k, const uint8_t* w_q,
+                                 const float* w_scale, int w_gran, int64_t E, int64_t N, int64_t K, uint16_t* y,
+                                 int out_layout, void* workspace, size_t workspace_bytes,
+                                 const rq_debug_out* dbg, void* stream) {
   if (act != RQ_ACT_NONE && act != RQ_ACT_SILU_MUL && act != RQ_ACT_GATE_SILU) return RQ_ERR_ARG;
+  if (w_gran != RQ_WSCALE_CHANNEL && w_gran != RQ_WSCALE_TENSOR && w_gran != RQ_WSCALE_BLOCK128) return RQ_ERR_ARG;
   if (in_layout != RQ_MOE_IN_TOKENS && in_layout != RQ_MOE_IN_PERMUTED) return RQ_ERR_ARG;
   if (out_layout != RQ_MOE_OUT_PERMUTED && out_layout != RQ_MOE_OUT_COMBINED) return RQ_ERR_ARG;
   if (T < 0 || K <= 0 || N <= 0 || E < 1 || E > kMaxExperts || top_k < 1 || top_k > E)
     return RQ_ERR_SHAPE;
   if (K % 16 != 0 || N % 16 != 0 || (act == RQ_ACT_GATE_SILU && N % 64 != 0)) return RQ_ERR_ALIGN;
+  if (w_gran == RQ_WSCALE_BLOCK128 && (N % rq::kScaleBlock != 0 || K % rq::kScaleBlock != 0)) return RQ_ERR_ALIGN;
   if (K > kMaxK || N > (int64_t)1 << 30 || T * top_k > ((int64_t)1 << 31) - 1)
     return RQ_ERR_SHAPE;
   if (T * top_k * K > kMaxOperandBytes || N * K > kMaxOperandBytes) return RQ_ERR_SHAPE;
@@ -278,6 +302,7 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const i
   g.tile_table = tile_table;
   g.E = (int32_t)E;
   g.gate = act == RQ_ACT_GATE_SILU ? 1 : 0;
+  g.b_gran = w_gran;
   {
     Hook hook(RQ_KERNEL_GEMM, s);
     if (rq::launch_gemm_grouped(g, kind, s) != hipSuccess) return RQ_ERR_HIP;
@@ -288,6 +313,16 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const i
     if (rq::launch_moe_combine(y_perm, pos, topk_w, T, top_k, NO, y, s) != hipSuccess) return RQ_ERR_HIP;
   }
   return RQ_OK;
+}
+
+int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const int32_t* topk_ids,
+                              const uint16_t* topk_w, int64_t T, int top_k, const uint8_t* w_q,
+                              const float* w_scale, int64_t E, int64_t N, int64_t K, uint16_t* y,
+                              int out_layout, void* workspace, size_t workspace_bytes,
+                              const rq_debug_out* dbg, void* stream) {
+  return rq_fp8_moe_grouped_linear_ex(x, in_layout, act, topk_ids, topk_w, T, top_k, w_q, w_scale,
+                                      RQ_WSCALE_CHANNEL, E, N, K, y, out_layout, workspace, workspace_bytes, dbg,
+                                      stream);
 }
 
 }  // extern "C"

@@ -68,6 +68,18 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t K, int act
                              uint8_t* q, float* scale, uint16_t* h, const int32_t* pos, int fanout,
                              hipStream_t stream);
 
+// Weight-scale granularities (the values of the C ABI's RQ_WSCALE_*): one FP32 scale per
+// output channel ([E][N]), per tensor ([E]) or per 128 x 128 block ([E][N/128][K/128]).
+enum { kScaleChannel = 0, kScaleTensor = 1, kScaleBlock128 = 2 };
+constexpr int kScaleBlock = 128;
+
+// Offline weight quantization at tensor or block granularity: B matrices [N][K] -> E4M3
+// bytes and B scales (tensor) or B * N/128 * K/128 scales (block; N, K multiples of 128).
+hipError_t launch_quant_tensor(const uint16_t* w, int64_t B, int64_t N, int64_t K, uint8_t* q, float* scale,
+                               hipStream_t stream);
+hipError_t launch_quant_blocks(const uint16_t* w, int64_t B, int64_t N, int64_t K, uint8_t* q, float* scale,
+                               hipStream_t stream);
+
 struct GemmArgs {
   const uint8_t* a;       // [a_rows][K] E4M3 (token rows, or permuted rows in grouped mode)
   const float* a_scale;   // [a_rows]
@@ -83,6 +95,7 @@ struct GemmArgs {
   const int32_t* tile_table;  // [m-tiles][4] {expert, first row, end row, 0}
   int32_t E;
   int32_t gate;               // 1: gated SiLU output (see rq_fp8.h, RQ_ACT_GATE_SILU), y is [rows][N/2]
+  int32_t b_gran;             // kScaleChannel, kScaleTensor or kScaleBlock128 (layout of b_scale)
 };
 
 // GEMM tile shapes (rows x columns of output per workgroup).

@@ -161,6 +161,9 @@ __device__ __forceinline__ void wait_slabs(int n) {
 __device__ __forceinline__ int load_uniform(const int32_t* p) {
   return *(const __attribute__((address_space(4))) int32_t*)(p);
 }
+__device__ __forceinline__ float load_uniform_f(const float* p) {
+  return *(const __attribute__((address_space(4))) float*)(p);
+}
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -268,8 +271,10 @@ __device__ __forceinline__ TileDesc2 tile_descs(const GemmArgs& p, const TileInf
   return d;
 }
 
-template <class C, bool GROUPED, bool GATE>
+template <class C, bool GROUPED, bool GATE, bool BLK>
 __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles, int n_tiles) {
+  static_assert(!BLK || (C::WN <= kScaleBlock && kScaleBlock % C::WN == 0),
+                "a wave's columns lie in one 128-column scale block");
   static_assert(!GATE || C::TJ % 2 == 0, "gated output pairs 32-column gate and up blocks in a wave");
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
 
@@ -354,8 +359,20 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
         const v4i d = make_desc(p.a_scale + t.row_begin, (uint32_t)(4 * (t.row_end - t.row_begin)));
         load_lds_4(d, (uint32_t)(4 * (64 * q + lane)), dst);
       } else {
-        const v4i d = make_desc(p.b_scale + (int64_t)t.expert * N + t.n0, (uint32_t)(4 * min(C::BN, N - t.n0)));
-        load_lds_4(d, (uint32_t)(4 * (64 * (q - C::BM / 64) + lane)), dst);
+        // column scales: the channel's own, the tensor's one scale, or (block scales) the
+        // scale of the channel's last K block, the one the accumulator is kept relative to
+        const int col = 64 * (q - C::BM / 64) + lane;
+        if (p.b_gran == kScaleTensor) {
+          load_lds_4(make_desc(p.b_scale + t.expert, 4u), 0u, dst);
+        } else if (BLK) {
+          const int kb = K / kScaleBlock, per_expert = (N / kScaleBlock) * kb;
+          const v4i d = make_desc(p.b_scale + (int64_t)t.expert * per_expert, (uint32_t)(4 * per_expert));
+          const int n = t.n0 + col;
+          load_lds_4(d, n < N ? (uint32_t)(4 * ((n / kScaleBlock) * kb + kb - 1)) : kOutOfRange, dst);
+        } else {
+          const v4i d = make_desc(p.b_scale + (int64_t)t.expert * N + t.n0, (uint32_t)(4 * min(C::BN, N - t.n0)));
+          load_lds_4(d, (uint32_t)(4 * col), dst);
+        }
       }
     }
   };
@@ -433,6 +450,20 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
     const bool pre = has_next && ktiles >= C::S;
     const int lim = pre ? ktiles + C::S : ktiles;  // slabs (from this tile's first) fetched here
 
+    // Block scales (BLK): the wave's columns share one 128-column block, so its K-block scales
+    // S[0..] form one row.  The accumulator is kept relative to the scale of the K block
+    // being summed: at the start of K block b >= 1 it is multiplied by S[b-1] / S[b], so
+    // after the last block it holds sum_b S[b] P_b / S[last], and the epilogue's column
+    // scale is S[last].  Each S[b] is loaded one slab before its block starts.
+    const float* srow = nullptr;
+    float s_prev = 1.0f, s_next = 1.0f;
+    if constexpr (BLK) {
+      const int kb = K / kScaleBlock, nbk = N / kScaleBlock;
+      const int nb = min((cur.n0 + wn * C::WN) / kScaleBlock, nbk - 1);  // waves past N: any row
+      srow = p.b_scale + ((int64_t)cur.expert * nbk + nb) * kb;
+      s_prev = load_uniform_f(srow);
+    }
+
     // One slab: wait for slab kt+1 and the reads of slab kt, barrier (slab kt's buffer is
     // then free for slab kt+S), then the MFMAs of slab kt interleaved with the fragment reads
     // of slab kt+1 and the direct-to-LDS loads of slab kt+S.  A single wave can issue only
@@ -442,11 +473,22 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
     // last slabs, a ragged K and the fetches for the next tile.  The first step of a tile
     // starts its accumulators from zero.
     // `role`: 0 decided at run time, 1 a loader, 2 not a loader.
-    auto step = [&](auto steady, auto first_step, auto role, int kt, uint4 (&bc)[2 * C::TJ],
+    // `resc`: 0 the slab starts no K block, 1 it starts one (block scales), 2 decided at run time.
+    auto step = [&](auto steady, auto first_step, auto role, auto resc, int kt, uint4 (&bc)[2 * C::TJ],
                     uint4 (&bn)[2 * C::TJ]) {
       constexpr bool kSteady = decltype(steady)::value;
       constexpr bool kFirst = decltype(first_step)::value;
       constexpr int kRole = decltype(role)::value;
+      constexpr int kResc = BLK ? decltype(resc)::value : 0;
+      // K blocks are two slabs: even slabs kt >= 2 start one; odd slabs fetch the next scale
+      const bool rescale = kResc == 1 || (kResc == 2 && kt > 0 && (kt & 1) == 0);
+      const bool fetch_scale = BLK && (kResc == 0 ? kSteady : kResc == 2) && (kt & 1) == 1 && kt + 1 < ktiles;
+      float ratio = 1.0f;
+      if (BLK && rescale) {
+        ratio = __fdiv_rn(s_prev, s_next);
+        s_prev = s_next;
+      }
+      if (BLK && fetch_scale) s_next = load_uniform_f(srow + ((kt + 1) >> 1));
       const bool loads = kRole == 1 || (kRole == 0 && loader);
       bool has_read = true;
       int fetch = 1;  // 0: nothing, 1: slab kt+S of this tile, 2: slab kt+S-ktiles of the next
@@ -471,6 +513,9 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
         const int i = q / C::TJ, jj = q % C::TJ;
         const v8i bf = as_v8(bc[2 * jj], bc[2 * jj + 1]);
         const v8i af = as_v8(fa[2 * i], fa[2 * i + 1]);
+        if constexpr (BLK && !kFirst) {
+          if (rescale) acc[i][jj] *= ratio;
+        }
         if constexpr (kFirst)
           acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, (v16f){}, 0, 0, 0, 0, 0, 0);
         else
@@ -505,18 +550,21 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
     };
 
     using Any = std::integral_constant<int, 0>;
-    if (C::S < full_slabs) step(True{}, True{}, Any{}, 0, fb0, fb1);
-    else step(False{}, True{}, Any{}, 0, fb0, fb1);
+    using NoK = std::integral_constant<int, 0>;   // no K-block start
+    using NewK = std::integral_constant<int, 1>;  // a K-block start (kt even, kt >= 2)
+    using RtK = std::integral_constant<int, 2>;   // decided at run time
+    if (C::S < full_slabs) step(True{}, True{}, Any{}, NoK{}, 0, fb0, fb1);
+    else step(False{}, True{}, Any{}, NoK{}, 0, fb0, fb1);
     int kt = 1;
     for (; kt + 1 + C::S < full_slabs; kt += 2) {  // kt and kt+1 steady: kt+1+S < full_slabs
-      step(True{}, False{}, Any{}, kt, fb1, fb0);
-      step(True{}, False{}, Any{}, kt + 1, fb0, fb1);
+      step(True{}, False{}, Any{}, NoK{}, kt, fb1, fb0);
+      step(True{}, False{}, Any{}, NewK{}, kt + 1, fb0, fb1);
     }
     for (; kt + 1 < ktiles; kt += 2) {
-      step(False{}, False{}, Any{}, kt, fb1, fb0);
-      step(False{}, False{}, Any{}, kt + 1, fb0, fb1);
+      step(False{}, False{}, Any{}, RtK{}, kt, fb1, fb0);
+      step(False{}, False{}, Any{}, RtK{}, kt + 1, fb0, fb1);
     }
-    if (kt < ktiles) step(False{}, False{}, Any{}, kt, fb1, fb0);
+    if (kt < ktiles) step(False{}, False{}, Any{}, RtK{}, kt, fb1, fb0);
     // Every wave is past this tile's last barrier and no fragment read is pending, so the
     // ring is free unless `pre` already refilled it.
     if (has_next && !pre) prologue(nxt, dn, (j + 1) & 1);
@@ -619,7 +667,7 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
 }
 
 // Workgroups of this kernel the device keeps resident at once (all CUs), cached per device.
-template <class C, bool GROUPED, bool GATE>
+template <class C, bool GROUPED, bool GATE, bool BLK>
 int resident_workgroups() {
   constexpr int kDevices = 64;
   static int cache[kDevices] = {};
@@ -629,7 +677,7 @@ int resident_workgroups() {
   if (cache[slot] > 0) return cache[slot];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_fp8_kernel<C, GROUPED, GATE>, C::NT, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_fp8_kernel<C, GROUPED, GATE, BLK>, C::NT, 0) !=
           hipSuccess ||
       per_cu <= 0)
     per_cu = 1;
@@ -646,27 +694,33 @@ int64_t grid_cap_override() {
   return v > 0 ? (int64_t)v : 0;
 }
 
-template <class C, bool GROUPED, bool GATE>
+template <class C, bool GROUPED, bool GATE, bool BLK>
 hipError_t launch_one(const GemmArgs& g, int m_tiles, hipStream_t stream) {
   const int n_tiles = (int)((g.N + C::BN - 1) / C::BN);
   const int64_t tiles = (int64_t)m_tiles * n_tiles;  // grouped: the worst case
-  int64_t cap = resident_workgroups<C, GROUPED, GATE>();
+  int64_t cap = resident_workgroups<C, GROUPED, GATE, BLK>();
   const int64_t forced = grid_cap_override();
   if (forced > 0 && forced < cap) cap = forced;
   const int64_t want = (tiles + 7) / 8 * 8;
   const int64_t grid = want < cap ? want : cap;
-  gemm_fp8_kernel<C, GROUPED, GATE><<<dim3((unsigned)grid), dim3(C::NT), 0, stream>>>(g, m_tiles, n_tiles);
+  gemm_fp8_kernel<C, GROUPED, GATE, BLK><<<dim3((unsigned)grid), dim3(C::NT), 0, stream>>>(g, m_tiles, n_tiles);
   return hipGetLastError();
+}
+
+template <class C, bool GROUPED, bool BLK>
+hipError_t launch_gate(const GemmArgs& g, int m_tiles, hipStream_t stream) {
+  if constexpr (C::TJ % 2 == 0) {
+    if (g.gate) return launch_one<C, GROUPED, true, BLK>(g, m_tiles, stream);
+  } else {
+    if (g.gate) return hipErrorInvalidValue;  // tile shapes with one 32-column block per wave
+  }
+  return launch_one<C, GROUPED, false, BLK>(g, m_tiles, stream);
 }
 
 template <class C, bool GROUPED>
 hipError_t launch(const GemmArgs& g, int m_tiles, hipStream_t stream) {
-  if constexpr (C::TJ % 2 == 0) {
-    if (g.gate) return launch_one<C, GROUPED, true>(g, m_tiles, stream);
-  } else {
-    if (g.gate) return hipErrorInvalidValue;  // tile shapes with one 32-column block per wave
-  }
-  return launch_one<C, GROUPED, false>(g, m_tiles, stream);
+  if (g.b_gran == kScaleBlock128) return launch_gate<C, GROUPED, true>(g, m_tiles, stream);
+  return launch_gate<C, GROUPED, false>(g, m_tiles, stream);
 }
 
 // Eight wavefronts (two per SIMD) for the large tiles: while one wavefront of a SIMD waits

@@ -245,7 +245,116 @@ hipError_t launch_impl(const uint16_t* x, int64_t rows, int64_t K, uint8_t* q, f
   return launch_split<16, SILU>(split, x, rows, k, q, scale, h, pos, fanout, stream);
 }
 
+// ---- weight scales per 128 x 128 block and per tensor (page "FP8量化在生成式推荐系统
+// OneRec-V2中的优化实践", §2.1 / §2.2: MoE expert weights block-wise, dense FFN weights per
+// tensor).  The row formula above applies to the set of values that shares a scale; the
+// quotient is the same Markstein one, valid because every |x| in the set is at most the
+// set's FP16 amax.
+
+// One 128 x 128 block per workgroup of 256 lanes: lane t reads 64 consecutive values (eight
+// 16-byte chunks) of block row t / 2, holds them in registers across the block's amax
+// reduction, then casts and stores them.  Scales are written in [B][N/128][K/128] order,
+// which is the workgroup order.
+__global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __restrict__ w, int64_t N, int64_t K,
+                                                           uint8_t* __restrict__ q, float* __restrict__ scale) {
+  __shared__ uint32_t part_max[4];
+  const int64_t nb = N / kScaleBlock, kb = K / kScaleBlock;
+  const int64_t blk = blockIdx.x;
+  const int64_t mat = blk / (nb * kb), in_mat = blk % (nb * kb);
+  const int64_t bi = in_mat / kb, bj = in_mat % kb;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t row = mat * N + bi * kScaleBlock + (t >> 1);
+  const int64_t col = bj * kScaleBlock + (t & 1) * 64;
+  const uint16_t* src = w + row * K + col;
+  uint4 v[8];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    v[j] = ld_global_16(src + 8 * j);
+    amax = absmax_packed(v[j], amax);
+  }
+  amax = wave_max_u32(amax);
+  if (lane == 0) part_max[wave] = amax;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) amax = amax > part_max[i] ? amax : part_max[i];
+  float s, rcp;
+  row_scale(amax, s, rcp);
+  uint8_t* dst = q + row * K + col;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    *reinterpret_cast<uint2*>(dst + 8 * j) = make_uint2(cast4(v[j].x, v[j].y, s, rcp), cast4(v[j].z, v[j].w, s, rcp));
+  if (t == 0) scale[blk] = s;
+}
+
+// Per-tensor scales in three steps on the stream: clear each matrix's amax word, fold every
+// row's FP16 magnitude maximum into it (an integer maximum, so the order of the atomic
+// updates does not matter), then quantize every row with its matrix's scale and finally
+// replace each amax word by the FP32 scale.  The amax words live in the scale array itself.
+__global__ __launch_bounds__(256) void clear_words(uint32_t* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+__global__ __launch_bounds__(256) void tensor_amax_kernel(const uint16_t* __restrict__ w, int64_t rows, int64_t N,
+                                                          int64_t K, uint32_t* __restrict__ amax_word) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const uint16_t* xr = w + row * K;
+  uint32_t amax = 0;
+  for (int64_t c = lane; c < K / 8; c += 64) amax = absmax_packed(ld_stream_16(xr + 8 * c), amax);
+  amax = wave_max_u32(amax);
+  if (lane == 0) atomicMax(amax_word + row / N, amax);
+}
+
+__global__ __launch_bounds__(256) void tensor_cast_kernel(const uint16_t* __restrict__ w, int64_t rows, int64_t N,
+                                                          int64_t K, const uint32_t* __restrict__ amax_word,
+                                                          uint8_t* __restrict__ q) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  float s, rcp;
+  row_scale(amax_word[row / N], s, rcp);
+  const uint16_t* xr = w + row * K;
+  uint8_t* qr = q + row * K;
+  for (int64_t c = lane; c < K / 8; c += 64) {
+    const uint4 v = ld_stream_16(xr + 8 * c);
+    *reinterpret_cast<uint2*>(qr + 8 * c) = make_uint2(cast4(v.x, v.y, s, rcp), cast4(v.z, v.w, s, rcp));
+  }
+}
+
+__global__ __launch_bounds__(256) void tensor_scale_kernel(float* __restrict__ scale, int64_t B) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= B) return;
+  float s, rcp;
+  row_scale(__builtin_bit_cast(uint32_t, scale[b]), s, rcp);
+  scale[b] = s;
+}
+
 }  // namespace
+
+hipError_t launch_quant_blocks(const uint16_t* w, int64_t B, int64_t N, int64_t K, uint8_t* q, float* scale,
+                               hipStream_t stream) {
+  const int64_t blocks = B * (N / kScaleBlock) * (K / kScaleBlock);
+  if (blocks <= 0) return hipSuccess;
+  quant_blocks_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(w, N, K, q, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_tensor(const uint16_t* w, int64_t B, int64_t N, int64_t K, uint8_t* q, float* scale,
+                               hipStream_t stream) {
+  const int64_t rows = B * N;
+  if (rows <= 0) return hipSuccess;
+  uint32_t* word = reinterpret_cast<uint32_t*>(scale);
+  const unsigned row_blocks = (unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock);
+  const unsigned b_blocks = (unsigned)((B + 255) / 256);
+  clear_words<<<dim3(b_blocks), dim3(256), 0, stream>>>(word, B);
+  tensor_amax_kernel<<<dim3(row_blocks), dim3(64 * kRowsPerBlock), 0, stream>>>(w, rows, N, K, word);
+  tensor_cast_kernel<<<dim3(row_blocks), dim3(64 * kRowsPerBlock), 0, stream>>>(w, rows, N, K, word, q);
+  tensor_scale_kernel<<<dim3(b_blocks), dim3(256), 0, stream>>>(scale, B);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t K, int act, uint8_t* q,
                              float* scale, uint16_t* h, const int32_t* pos, int fanout,

@@ -60,7 +60,7 @@ typedef enum {
   RQ_ERR_WORKSPACE = 4,   /* workspace smaller than the *_workspace_size result */
   RQ_ERR_UNSUPPORTED = 5, /* the current device is not gfx950 */
   RQ_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed */
-  RQ_ERR_ARG = 7          /* an unknown act / layout value, or a missing topk_w */
+  RQ_ERR_ARG = 7          /* an unknown act / layout / w_gran value, or a missing topk_w */
 } rq_status;
 
 /* Activation applied to the FP16 input rows before they are quantized.
@@ -162,6 +162,47 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act,
                               uint16_t* y, int out_layout,
                               void* workspace, size_t workspace_bytes,
                               const rq_debug_out* dbg, void* stream);
+
+/* Weight-scale granularity (page "FP8量化在生成式推荐系统OneRec-V2中的优化实践", §2.1 and
+ * §2.2, which quantizes the attention projections per output channel, the dense FFN
+ * weights per tensor and the MoE expert weights in 128 x 128 blocks).  Every granularity
+ * uses the row formula above over the set of values that shares one scale.  Scale
+ * layouts for B (or E) weight matrices [N][K]:
+ *   RQ_WSCALE_CHANNEL  [B][N]              one scale per output channel (the default)
+ *   RQ_WSCALE_TENSOR   [B]                 one scale per matrix
+ *   RQ_WSCALE_BLOCK128 [B][N/128][K/128]   one scale per block of 128 output x 128 input
+ *                                          channels; N and K must be multiples of 128
+ *                                          (RQ_ERR_ALIGN otherwise)
+ * With block scales the linear is y[m][n] = fl16(s_x[m] * sum_j S[n/128][j] * P_j[m][n]),
+ * P_j the FP32-accumulated product over K block j: the accumulator is kept relative to the
+ * current block's scale (multiplied by S[j-1] / S[j] as block j starts), then scaled by
+ * s_x[m] and the last block's scale, each in FP32, and rounded to FP16. */
+enum { RQ_WSCALE_CHANNEL = 0, RQ_WSCALE_TENSOR = 1, RQ_WSCALE_BLOCK128 = 2 };
+
+/* rq_fp8_quant_weights with the weight-scale granularity w_gran (layouts above).
+ * RQ_ERR_ARG for an unknown w_gran.  Per-tensor scales take four short kernels (amax words
+ * are kept in w_scale until the last one writes the scales). */
+int rq_fp8_quant_weights_ex(const uint16_t* w, int64_t B, int64_t N, int64_t K, int w_gran,
+                            uint8_t* w_q, float* w_scale, void* stream);
+
+/* rq_fp8_linear with weights quantized at granularity w_gran; w_scale has that layout
+ * (B = 1).  rq_fp8_linear is this call with RQ_WSCALE_CHANNEL. */
+int rq_fp8_linear_ex(const uint16_t* x, int64_t M, int64_t K, int act,
+                     const uint8_t* w_q, const float* w_scale, int w_gran, int64_t N,
+                     uint16_t* y, void* workspace, size_t workspace_bytes,
+                     const rq_debug_out* dbg, void* stream);
+
+/* rq_fp8_moe_grouped_linear with expert weights quantized at granularity w_gran; w_scale
+ * has that layout with B = E.  rq_fp8_moe_grouped_linear is this call with
+ * RQ_WSCALE_CHANNEL.  The workspace size does not depend on w_gran. */
+int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act,
+                                 const int32_t* topk_ids, const uint16_t* topk_w,
+                                 int64_t T, int top_k,
+                                 const uint8_t* w_q, const float* w_scale, int w_gran,
+                                 int64_t E, int64_t N, int64_t K,
+                                 uint16_t* y, int out_layout,
+                                 void* workspace, size_t workspace_bytes,
+                                 const rq_debug_out* dbg, void* stream);
 
 /* Kernel-level timing for benchmarks and profilers.  After this call, the next kernel
  * of the given kind that the calling thread enqueues (through any entry point above) is
