@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel breakdown")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the weight-scale variants (per-tensor FFN, 128x128-block MoE weights)")
     ap.add_argument("--rocprof-summary", default=None, metavar="PATH",
                     help="print per-(kernel, grid) dispatch statistics of a rocprofv3 output "
                          "(a *_results.db, a *_kernel_trace.csv, or a directory holding one) and exit")
@@ -106,12 +108,15 @@ class Hip:
 class Path:
     """Device-resident inputs, quantized weights, outputs and workspaces of one step."""
 
-    def __init__(self, rq, torch, only=None):
+    def __init__(self, rq, torch, only=None, variants=True):
         import workloads
         self.rq, self.torch = rq, torch
         dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
         self.calls = []     # (workload, label, kind, flops, bytes_moved, fn)
         self.qbytes = []    # per call: bytes the row quantizer must move
+        # weight-scale variants, timed apart from the step: (workload, call, wscale, flops,
+        # index of the per-channel call of the same shape, fn)
+        self.variants = []
         self.flops = 0
         want = set(only.split(",")) if only else {"attention", "ffn", "moe", "layer_small_m"}
 
@@ -171,6 +176,22 @@ class Path:
             wgu, wdn = qw_gated(d["w_gu"]), qw(d["w_dn"])
             h = add_linear("ffn", "gate_up", dev(d["x"]), *wgu, act="gate_silu")
             add_linear("ffn", "down", h, *wdn)
+            if variants:
+                # the dense FFN with one scale per weight tensor
+                x3 = dev(d["x"])
+                tgu = rq.quant_weights(dev(rq.interleave_gate_up(d["w_gu"])), wscale="tensor")
+                tdn = rq.quant_weights(dev(d["w_dn"]), wscale="tensor")
+                h_t = torch.empty_like(h)
+                y_t = torch.empty((4096, 2048), dtype=torch.float16, device="cuda")
+                ws_gu = torch.empty(rq.linear_workspace_size(4096, 2048), dtype=torch.uint8, device="cuda")
+                ws_dn = torch.empty(rq.linear_workspace_size(4096, 8192), dtype=torch.uint8, device="cuda")
+                n0 = len(self.calls)
+                self.variants.append(("ffn", "gate_up", "tensor", self.calls[n0 - 2][3], n0 - 2,
+                                      lambda x3=x3, tgu=tgu, h_t=h_t, ws_gu=ws_gu: rq.linear(
+                                          x3, *tgu, act="gate_silu", out=h_t, workspace=ws_gu, wscale="tensor")))
+                self.variants.append(("ffn", "down", "tensor", self.calls[n0 - 1][3], n0 - 1,
+                                      lambda h_t=h_t, tdn=tdn, y_t=y_t, ws_dn=ws_dn: rq.linear(
+                                          h_t, *tdn, out=y_t, workspace=ws_dn, wscale="tensor")))
             self.config["ffn"] = "4096 tokens x 2048; gate/up 2x8192, down K=8192"
         if "moe" in want:
             d = workloads.make(4)
@@ -180,6 +201,26 @@ class Path:
             h = add_moe("moe", "gate_up", dev(d["x"]), ids, *wgu, "tokens", "gate_silu", "permuted")
             self.dominant = len(self.calls) - 1
             add_moe("moe", "down", h, ids, *wdn, "permuted", "none", "combined", topk_w=tw)
+            if variants:
+                # expert weights with one scale per 128 x 128 block
+                x4 = dev(d["x"])
+                bgu = rq.quant_weights(dev(rq.interleave_gate_up(d["w_gu"])), wscale="block128")
+                bdn = rq.quant_weights(dev(d["w_dn"]), wscale="block128")
+                h_b = torch.empty_like(h)
+                y_b = torch.empty((16384, 2048), dtype=torch.float16, device="cuda")
+                ws_gu = torch.empty(rq.moe_workspace_size(16384, 2, 32, 8192, 2048, "tokens", "gate_silu", "permuted"),
+                                    dtype=torch.uint8, device="cuda")
+                ws_dn = torch.empty(rq.moe_workspace_size(16384, 2, 32, 2048, 4096, "permuted", "none", "combined"),
+                                    dtype=torch.uint8, device="cuda")
+                n0 = len(self.calls)
+                self.variants.append(("moe", "gate_up", "block128", self.calls[n0 - 2][3], n0 - 2,
+                                      lambda x4=x4, ids=ids, bgu=bgu, h_b=h_b, ws_gu=ws_gu: rq.moe_grouped_linear(
+                                          x4, ids, *bgu, "tokens", "gate_silu", "permuted", out=h_b, workspace=ws_gu,
+                                          wscale="block128")))
+                self.variants.append(("moe", "down", "block128", self.calls[n0 - 1][3], n0 - 1,
+                                      lambda h_b=h_b, ids=ids, bdn=bdn, tw=tw, y_b=y_b, ws_dn=ws_dn:
+                                      rq.moe_grouped_linear(h_b, ids, *bdn, "permuted", "none", "combined", topk_w=tw,
+                                                            out=y_b, workspace=ws_dn, wscale="block128")))
             self.config["moe"] = ("16384 tokens x 2048; top-2 of 32 experts (Zipf 1.1; max %d, min nonzero %d, "
                                   "%d empty rows of 32768); gate/up 2x4096, down K=4096"
                                   % (counts.max(), counts[counts > 0].min(), int((counts == 0).sum())))
@@ -232,6 +273,31 @@ def kernel_breakdown(path, hip, reps=5):
                      "gemm_min_hbm_gbs": round(by / (res["gemm"] * 1e-3) / 1e9, 1),
                      "quant_us": round(res["quant"] * 1e3, 2), "quant_gbs": round(qgbs, 1),
                      "quant_frac_hbm": round(qgbs / HBM_PEAK_GBS, 4)})
+    return rows
+
+
+def variant_breakdown(path, hip, reps=5):
+    """GEMM time of each weight-scale variant next to the per-channel call of the same shape."""
+    from fp8_quantized_generative_amd import _lib
+    lib = _lib.load()
+
+    def gemm_ms(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            a, b = hip.event(), hip.event()
+            lib.rq_time_next_kernel(_lib.RQ_KERNEL_GEMM, a, b)
+            fn()
+            ts.append(hip.elapsed_ms(a, b))
+        return float(np.median(ts))
+
+    rows = []
+    for work, label, wscale, fl, ref, fn in path.variants:
+        ms, ref_ms = gemm_ms(fn), gemm_ms(path.calls[ref][5])
+        rows.append({"workload": work, "call": label, "wscale": wscale, "gemm_us": round(ms * 1e3, 2),
+                     "gemm_tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                     "gemm_frac_fp8_peak": round(fl / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                     "channel_gemm_us": round(ref_ms * 1e3, 2)})
     return rows
 
 
@@ -489,7 +555,7 @@ def main():
     torch.cuda.set_device(0)
     hip = Hip()
     print("[bench] building inputs", file=sys.stderr, flush=True)
-    path = Path(rq, torch, args.only)
+    path = Path(rq, torch, args.only, variants=not args.no_variants)
     print("[bench] %d calls per step, %.1f GFLOP" % (len(path.calls), path.flops / 1e9), file=sys.stderr, flush=True)
 
     for _ in range(args.warmup):
@@ -554,6 +620,9 @@ def main():
     if not args.no_kernels:
         print("[bench] per-kernel breakdown", file=sys.stderr, flush=True)
         result["kernels"] = kernel_breakdown(path, hip)
+    if path.variants:
+        print("[bench] weight-scale variants", file=sys.stderr, flush=True)
+        result["wscale_variants"] = variant_breakdown(path, hip)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         del path

@@ -129,13 +129,19 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (
 // Scheduling pattern of one slab (M MFMAs over TI x TJ tiles, i-major): each MFMA followed
 // by the fragment reads it frees or that are due - two B reads after each of the first TJ
 // MFMAs, and A fragment i's two reads after the last MFMA that uses it.
-template <int Q, int M, int TJ>
+// RESC (block scales, see the kernel): 1 in the last slab of a K block, where the 16
+// multiplies rescaling MFMA tile q - 1's accumulator follow MFMA q (that tile's MFMA has
+// finished by then, and the multiplies run in the shadow of MFMA q); 2 in the first slab of
+// the next block, where the last tile's rescale follows MFMA 0.
+template <int Q, int M, int TJ, int RESC = 0>
 __device__ __forceinline__ void interleave_mfma_reads() {
   if constexpr (Q < M) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    if constexpr ((RESC == 1 && Q >= 1) || (RESC == 2 && Q == 0))
+      __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // a tile's 16 rescale multiplies
     constexpr int reads = (Q < TJ ? 2 : 0) + (Q % TJ == TJ - 1 ? 2 : 0);
     if constexpr (reads > 0) __builtin_amdgcn_sched_group_barrier(0x100, reads, 0);  // DS reads
-    interleave_mfma_reads<Q + 1, M, TJ>();
+    interleave_mfma_reads<Q + 1, M, TJ, RESC>();
   }
 }
 
@@ -452,16 +458,21 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
 
     // Block scales (BLK): the wave's columns share one 128-column block, so its K-block scales
     // S[0..] form one row.  The accumulator is kept relative to the scale of the K block
-    // being summed: at the start of K block b >= 1 it is multiplied by S[b-1] / S[b], so
-    // after the last block it holds sum_b S[b] P_b / S[last], and the epilogue's column
-    // scale is S[last].  Each S[b] is loaded one slab before its block starts.
+    // being summed: between K blocks b - 1 and b (b >= 1) each MFMA tile's accumulator is
+    // multiplied by S[b-1] / S[b], so after the last block it holds sum_b S[b] P_b / S[last]
+    // and the epilogue's column scale is S[last].  A K block is two slabs: tile q's multiply
+    // follows MFMA q + 1 of the block's last slab (the last tile's, MFMA 0 of the next
+    // block's first slab), always after the tile's last MFMA of block b - 1 and before its
+    // first of block b.  S[b + 1] is loaded in the first slab of block b, a slab before the
+    // ratio needs it.
     const float* srow = nullptr;
-    float s_prev = 1.0f, s_next = 1.0f;
+    float s_prev = 1.0f, s_next = 1.0f, ratio = 1.0f;
     if constexpr (BLK) {
       const int kb = K / kScaleBlock, nbk = N / kScaleBlock;
       const int nb = min((cur.n0 + wn * C::WN) / kScaleBlock, nbk - 1);  // waves past N: any row
       srow = p.b_scale + ((int64_t)cur.expert * nbk + nb) * kb;
       s_prev = load_uniform_f(srow);
+      if (kb > 1) s_next = load_uniform_f(srow + 1);
     }
 
     // One slab: wait for slab kt+1 and the reads of slab kt, barrier (slab kt's buffer is
@@ -473,22 +484,21 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
     // last slabs, a ragged K and the fetches for the next tile.  The first step of a tile
     // starts its accumulators from zero.
     // `role`: 0 decided at run time, 1 a loader, 2 not a loader.
-    // `resc`: 0 the slab starts no K block, 1 it starts one (block scales), 2 decided at run time.
+    // `resc` (block scales): 0 no rescale, 1 the last slab of a K block that another follows,
+    // 2 the first slab of a K block after the first, 3 decided at run time.
     auto step = [&](auto steady, auto first_step, auto role, auto resc, int kt, uint4 (&bc)[2 * C::TJ],
                     uint4 (&bn)[2 * C::TJ]) {
       constexpr bool kSteady = decltype(steady)::value;
       constexpr bool kFirst = decltype(first_step)::value;
       constexpr int kRole = decltype(role)::value;
       constexpr int kResc = BLK ? decltype(resc)::value : 0;
-      // K blocks are two slabs: even slabs kt >= 2 start one; odd slabs fetch the next scale
-      const bool rescale = kResc == 1 || (kResc == 2 && kt > 0 && (kt & 1) == 0);
-      const bool fetch_scale = BLK && (kResc == 0 ? kSteady : kResc == 2) && (kt & 1) == 1 && kt + 1 < ktiles;
-      float ratio = 1.0f;
-      if (BLK && rescale) {
+      const bool resc_last = kResc == 1 || (kResc == 3 && (kt & 1) == 1 && kt + 1 < ktiles);
+      const bool resc_first = kResc == 2 || (kResc == 3 && (kt & 1) == 0 && kt >= 2);
+      if (BLK && resc_last) {
         ratio = __fdiv_rn(s_prev, s_next);
         s_prev = s_next;
       }
-      if (BLK && fetch_scale) s_next = load_uniform_f(srow + ((kt + 1) >> 1));
+      if (BLK && resc_first && kt + 2 < ktiles) s_next = load_uniform_f(srow + (kt >> 1) + 1);
       const bool loads = kRole == 1 || (kRole == 0 && loader);
       bool has_read = true;
       int fetch = 1;  // 0: nothing, 1: slab kt+S of this tile, 2: slab kt+S-ktiles of the next
@@ -513,13 +523,14 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
         const int i = q / C::TJ, jj = q % C::TJ;
         const v8i bf = as_v8(bc[2 * jj], bc[2 * jj + 1]);
         const v8i af = as_v8(fa[2 * i], fa[2 * i + 1]);
-        if constexpr (BLK && !kFirst) {
-          if (rescale) acc[i][jj] *= ratio;
-        }
         if constexpr (kFirst)
           acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, (v16f){}, 0, 0, 0, 0, 0, 0);
         else
           acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[i][jj], 0, 0, 0, 0, 0, 0);
+        if constexpr (BLK) {
+          if (resc_last && q >= 1) acc[(q - 1) / C::TJ][(q - 1) % C::TJ] *= ratio;
+          if (resc_first && q == 0) acc[C::TI - 1][C::TJ - 1] *= ratio;
+        }
         if (kSteady || has_read) {
           if (q < C::TJ) {
             bn[2 * q] = read_b(Sn, 2 * q);
@@ -546,18 +557,19 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
           }
         }
       }
-      interleave_mfma_reads<0, kMfma, C::TJ>();
+      interleave_mfma_reads<0, kMfma, C::TJ, (kResc == 1 || kResc == 2) ? kResc : 0>();
     };
 
     using Any = std::integral_constant<int, 0>;
-    using NoK = std::integral_constant<int, 0>;   // no K-block start
-    using NewK = std::integral_constant<int, 1>;  // a K-block start (kt even, kt >= 2)
-    using RtK = std::integral_constant<int, 2>;   // decided at run time
+    using NoK = std::integral_constant<int, 0>;    // no rescale
+    using LastK = std::integral_constant<int, 1>;  // last slab of a K block (kt odd)
+    using NewK = std::integral_constant<int, 2>;   // first slab of a K block (kt even, kt >= 2)
+    using RtK = std::integral_constant<int, 3>;    // decided at run time
     if (C::S < full_slabs) step(True{}, True{}, Any{}, NoK{}, 0, fb0, fb1);
     else step(False{}, True{}, Any{}, NoK{}, 0, fb0, fb1);
     int kt = 1;
     for (; kt + 1 + C::S < full_slabs; kt += 2) {  // kt and kt+1 steady: kt+1+S < full_slabs
-      step(True{}, False{}, Any{}, NoK{}, kt, fb1, fb0);
+      step(True{}, False{}, Any{}, LastK{}, kt, fb1, fb0);
       step(True{}, False{}, Any{}, NewK{}, kt + 1, fb0, fb1);
     }
     for (; kt + 1 < ktiles; kt += 2) {
