@@ -464,14 +464,23 @@ def _pmc_rows(path, counter):
     return [per[d] for d in sorted(per)]
 
 
-def gemm_source_hash():
-    """Hash of the GEMM kernel's sources: stored traffic counters are valid only for this code."""
+def source_hash(files):
+    """Hash of a kernel's sources: stored traffic counters are valid only for this code."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.h"):
+    for f in files:
         with open(os.path.join(ROOT, "fp8_quantized_generative_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+GEMM_SOURCES = ("gemm.hip", "common.h")
+QUANT_SOURCES = ("quant.hip", "common.h")
+QUANT_CALL = ("moe", "down")   # the largest row-quantizer call: 32768 permuted rows x 4096
+
+
+def gemm_source_hash():
+    return source_hash(GEMM_SOURCES)
 
 
 def dominant_algorithmic_bytes():
@@ -483,27 +492,37 @@ def dominant_algorithmic_bytes():
     return r * k + e * n * k + 4 * (r + e * n) + 2 * r * f
 
 
+def quant_algorithmic_bytes():
+    """The row quantizer of the MoE down call: FP16 rows in, E4M3 rows and FP32 scales out."""
+    r, k = 16384 * 2, 4096
+    return 2 * r * k + r * k + 4 * r
+
+
 def traffic_summary(fetch_dir, write_dir, out, only=None, steps=None):
-    result = {"kernel": "gemm_fp8_kernel (grouped, 256x256) for the %s %s call" % DOMINANT,
-              "source_sha256_16": gemm_source_hash()}
+    """Per-launch counter values of the dominant GEMM and of the largest quantizer call, and
+    of the calibration copy that follows the profiled steps."""
+    gemm = {"kernel": "gemm_fp8_kernel (grouped, 256x256) for the %s %s call" % DOMINANT,
+            "source_sha256_16": source_hash(GEMM_SOURCES)}
+    qnt = {"kernel": "quant_rows for the %s %s call (32768 x 4096 FP16 rows)" % QUANT_CALL,
+           "source_sha256_16": source_hash(QUANT_SOURCES)}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _pmc_rows(d, counter)
         names = [r[0] for r in rows]
         aligned, nsteps = _align_steps(names, only, steps)
-        dom = [rows[i][1] for i, label, kind in aligned if label == "%s %s" % DOMINANT and kind == "gemm"]
         last = max(i for i, _, _ in aligned)
         copies = [r for r in rows[last + 1:] if not any(k in r[0] for k in OUR_KERNELS)]
-        if not dom or not copies:
-            raise SystemExit("%s: dominant launch or calibration copy not found" % counter)
-        copy_kib = copies[-1][1]
-        result[counter.lower() + "_kib_per_launch"] = round(float(np.mean(dom)), 1)
-        result[counter.lower() + "_launches"] = len(dom)
-        result["copy_" + counter.lower() + "_kib"] = round(copy_kib, 1)
-        result["copy_kernel"] = copies[-1][0][:120]
-    return result
+        for res, label, kind in ((gemm, "%s %s" % DOMINANT, "gemm"), (qnt, "%s %s" % QUANT_CALL, "quant")):
+            vals = [rows[i][1] for i, lb, kd in aligned if lb == label and kd == kind]
+            if not vals or not copies:
+                raise SystemExit("%s: %s %s launch or calibration copy not found" % (counter, label, kind))
+            res[counter.lower() + "_kib_per_launch"] = round(float(np.mean(vals)), 1)
+            res[counter.lower() + "_launches"] = len(vals)
+            res["copy_" + counter.lower() + "_kib"] = round(copies[-1][1], 1)
+            res["copy_kernel"] = copies[-1][0][:120]
+    return gemm, qnt
 
 
-def finish_traffic(result, copy_mib, out):
+def finish_traffic(result, copy_mib, out, algorithmic):
     copy_bytes = copy_mib * 1024 * 1024
     result["copy_mib"] = copy_mib
     f_fac = result["copy_fetch_size_kib"] * 1024 / copy_bytes
@@ -513,23 +532,26 @@ def finish_traffic(result, copy_mib, out):
     traffic = (result["fetch_size_kib_per_launch"] * 1024 / f_fac +
                result["write_size_kib_per_launch"] * 1024 / w_fac)
     result["traffic_bytes_per_launch"] = int(traffic)
-    result["algorithmic_bytes_per_launch"] = dominant_algorithmic_bytes()
-    result["traffic_over_algorithmic"] = round(traffic / dominant_algorithmic_bytes(), 3)
+    result["algorithmic_bytes_per_launch"] = algorithmic
+    result["traffic_over_algorithmic"] = round(traffic / algorithmic, 3)
     with open(out, "w") as f:
         json.dump(result, f, indent=1)
     print(json.dumps(result, indent=1))
 
 
-def stored_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed counter summary, or None
-    when it is missing or was taken on different GEMM sources."""
-    p = os.path.join(ROOT, "profiles", "gemm_fp8_grouped_moe_gate_up_traffic.json")
+GEMM_TRAFFIC = os.path.join(ROOT, "profiles", "gemm_fp8_grouped_moe_gate_up_traffic.json")
+QUANT_TRAFFIC = os.path.join(ROOT, "profiles", "quant_rows_moe_down_traffic.json")
+
+
+def stored_traffic(path=GEMM_TRAFFIC, sources=GEMM_SOURCES):
+    """HBM bytes per launch from a committed counter summary, or None when it is missing or
+    was taken on different kernel sources."""
     try:
-        with open(p) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256_16") != gemm_source_hash():
+    if t.get("source_sha256_16") != source_hash(sources):
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -541,8 +563,11 @@ def main():
         return
     if args.traffic_summary:
         fetch_dir, write_dir, out = args.traffic_summary
-        res = traffic_summary(fetch_dir, write_dir, out, args.only, args.steps_in_profile)
-        finish_traffic(res, args.calibrate_copy_mb or 512, out)
+        gemm, qnt = traffic_summary(fetch_dir, write_dir, out, args.only, args.steps_in_profile)
+        finish_traffic(gemm, args.calibrate_copy_mb or 512, out, dominant_algorithmic_bytes())
+        finish_traffic(qnt, args.calibrate_copy_mb or 512, os.path.join(os.path.dirname(out) or ".",
+                                                                        os.path.basename(QUANT_TRAFFIC)),
+                       quant_algorithmic_bytes())
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode (run with --gpus 1)",
@@ -589,7 +614,9 @@ def main():
     q_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in qevs]))
     q_gbs = path.qbytes[path.quant_dominant] / (q_ms * 1e-3) / 1e9
     quant_roofline = {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                      "frac": round(q_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                      "frac": round(q_gbs / HBM_PEAK_GBS, 4),
+                      "traffic": (stored_traffic(QUANT_TRAFFIC, QUANT_SOURCES)
+                                  if (qcall[0], qcall[1]) == QUANT_CALL else None),
                       "kernel": "quant_rows (%s %s)" % (qcall[0], qcall[1]),
                       "bytes_per_launch": path.qbytes[path.quant_dominant], "avg_launch_us": round(q_ms * 1e3, 2)}
 

@@ -46,15 +46,21 @@ def test_traffic_scaling(tmp_path):
     res = {"fetch_size_kib_per_launch": 1000.0, "write_size_kib_per_launch": 300.0,
            "copy_fetch_size_kib": 256.0 * 1024, "copy_write_size_kib": 512.0 * 1024}
     out = tmp_path / "t.json"
-    bench.finish_traffic(res, 512, str(out))
+    bench.finish_traffic(res, 512, str(out), 10 ** 6)
     t = json.loads(out.read_text())
     assert t["fetch_factor"] == 0.5 and t["write_factor"] == 1.0
     assert t["traffic_bytes_per_launch"] == int(1000 * 1024 / 0.5 + 300 * 1024)
+    assert t["algorithmic_bytes_per_launch"] == 10 ** 6
 
 
 def test_algorithmic_bytes_of_the_dominant_call():
     r, k, n, e = 32768, 2048, 8192, 32
     assert bench.dominant_algorithmic_bytes() == r * k + e * n * k + 4 * (r + e * n) + 2 * r * (n // 2)
+
+
+def test_algorithmic_bytes_of_the_largest_quantizer_call():
+    r, k = 32768, 4096
+    assert bench.quant_algorithmic_bytes() == 2 * r * k + r * k + 4 * r
 
 
 def test_more_than_one_gpu_exits_with_a_message():
