@@ -20,6 +20,8 @@ What it computes, and where the pages fix it:
 Arithmetic is float64 and integers.  Every rounding is explicit.  Modules:
 
 * ``e4m3``   - OCP OFP8 E4M3 decode table and saturating round-to-nearest-even encode.
+* ``e5m2``   - the same for OCP OFP8 E5M2 (activations in E5M2: page "FP8量化在生成式推荐系统
+               OneRec-V2中的优化实践", §2.2).
 * ``quant``  - the row quantizer (per output channel for weights, per token for activations).
 * ``linear`` - exact FP8 dot products, per-token x per-channel dequantization to FP16, and
                the parity tolerance.
@@ -34,6 +36,6 @@ brute force over exact rationals, PyTorch's own float8_e4m3fn conversion and SiL
 No function is "parity unpinned".
 """
 
-from . import e4m3, quant, linear, ffn, moe, wscale  # noqa: F401
+from . import e4m3, e5m2, quant, linear, ffn, moe, wscale  # noqa: F401
 
-__all__ = ["e4m3", "quant", "linear", "ffn", "moe", "wscale"]
+__all__ = ["e4m3", "e5m2", "quant", "linear", "ffn", "moe", "wscale"]

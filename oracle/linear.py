@@ -17,6 +17,11 @@ therefore exact in every summation order, BLAS included.  The oracle's accumulat
 the exact real dot product; the "FP32 accumulation" of the pages is what the tolerance
 below allows for.
 
+With E5M2 activations (the variant of page "FP8量化在生成式推荐系统OneRec-V2中的优化实践",
+§2.2) the activation operand is an integer multiple of 2^-16 below 2^15.8, so the integer
+products reach 2^49.6 and sums over K <= 8192 reach 2^62.6: those are accumulated in int64,
+exact below 2^63.
+
 Output: ``y* = acc * s_x[m] * s_w[n]`` in float64, then one round-to-nearest-even to
 FP16 (numpy's float64 -> float16 cast rounds directly, ties to even).
 
@@ -31,34 +36,43 @@ summation order of the K products.
 
 import numpy as np
 
-from . import e4m3
+from . import e4m3, e5m2
 
-_UNIT = 2.0 ** 9   # E4M3 values are integer multiples of 2^-9
-
-
-def _int_operand(codes):
-    vals = e4m3.decode(codes)
-    if np.isnan(vals).any():
-        raise ValueError("NaN E4M3 code in a GEMM operand")
-    return vals * _UNIT
+# E4M3 values are integer multiples of 2^-9, E5M2 values of 2^-16.
+_UNITS = {"e4m3": (e4m3, 2.0 ** 9), "e5m2": (e5m2, 2.0 ** 16)}
 
 
-def gemm_exact(x_q, w_q):
-    """Exact ``acc[m, n] = sum_k dec(x_q[m, k]) * dec(w_q[n, k])`` as float64."""
-    a = _int_operand(x_q)
-    b = _int_operand(w_q)
+def _int_operand(codes, fmt="e4m3"):
+    codec, unit = _UNITS[fmt]
+    vals = codec.decode(codes)
+    if not np.isfinite(vals).all():
+        raise ValueError("NaN or infinite %s code in a GEMM operand" % fmt)
+    return vals * unit
+
+
+def _exact_products(a, b, scale):
+    """a @ b.T / scale for integer-valued float64 operands, exactly."""
     if a.shape[1] != b.shape[1]:
         raise ValueError("K mismatch")
-    if a.shape[1] > 2 ** 17:
-        raise ValueError("K too large for exact float64 accumulation")
-    return (a @ b.T) / (_UNIT * _UNIT)
+    bound = np.max(np.abs(a), initial=0.0) * np.max(np.abs(b), initial=0.0) * a.shape[1]
+    if bound < 2.0 ** 53:
+        return (a @ b.T) / scale                       # every partial sum is an exact float64
+    if bound >= 2.0 ** 63:
+        raise ValueError("K too large for exact accumulation")
+    # E5M2 activations: integer products reach 2^49.6, so sum them in int64 (exact below 2^63)
+    return (a.astype(np.int64) @ b.astype(np.int64).T).astype(np.float64) / scale
 
 
-def gemm_abs_exact(x_q, w_q):
+def gemm_exact(x_q, w_q, a_fmt="e4m3"):
+    """Exact ``acc[m, n] = sum_k dec(x_q[m, k]) * dec(w_q[n, k])`` as float64 (activations in
+    ``a_fmt``, weights E4M3)."""
+    return _exact_products(_int_operand(x_q, a_fmt), _int_operand(w_q), _UNITS[a_fmt][1] * 2.0 ** 9)
+
+
+def gemm_abs_exact(x_q, w_q, a_fmt="e4m3"):
     """Exact ``sum_k |dec(x_q[m, k]) * dec(w_q[n, k])|`` as float64."""
-    a = np.abs(_int_operand(x_q))
-    b = np.abs(_int_operand(w_q))
-    return (a @ b.T) / (_UNIT * _UNIT)
+    return _exact_products(np.abs(_int_operand(x_q, a_fmt)), np.abs(_int_operand(w_q)),
+                           _UNITS[a_fmt][1] * 2.0 ** 9)
 
 
 def dequantize_fp16(acc, s_x, s_w):
@@ -68,9 +82,9 @@ def dequantize_fp16(acc, s_x, s_w):
     return (acc * sx * sw).astype(np.float16)
 
 
-def linear(x_q, s_x, w_q, s_w):
+def linear(x_q, s_x, w_q, s_w, a_fmt="e4m3"):
     """FP16 output of the quantized linear for quantized operands."""
-    return dequantize_fp16(gemm_exact(x_q, w_q), s_x, s_w)
+    return dequantize_fp16(gemm_exact(x_q, w_q, a_fmt), s_x, s_w)
 
 
 def ulp16(y):
@@ -91,10 +105,10 @@ def tolerance(y_ref, s_x, s_w, abs_acc):
     return 2.0 * ulp16(y_ref) + 1e-3 * sx * sw * abs_acc
 
 
-def check(y_gpu, x_q, s_x, w_q, s_w):
+def check(y_gpu, x_q, s_x, w_q, s_w, a_fmt="e4m3"):
     """Compare a GPU output with the oracle.  Returns ``(ok, worst |d|/tol, y_ref)``."""
-    y_ref = linear(x_q, s_x, w_q, s_w)
-    tol = tolerance(y_ref, s_x, s_w, gemm_abs_exact(x_q, w_q))
+    y_ref = linear(x_q, s_x, w_q, s_w, a_fmt)
+    tol = tolerance(y_ref, s_x, s_w, gemm_abs_exact(x_q, w_q, a_fmt))
     d = np.abs(np.asarray(y_gpu, dtype=np.float64) - y_ref.astype(np.float64))
     bad = ~(d <= tol)
     ratio = float(np.max(d / tol)) if d.size else 0.0

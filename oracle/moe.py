@@ -55,7 +55,7 @@ def plan(ids, num_experts):
 
 
 def grouped_linear(x, in_layout, act, ids, w_q, s_w, out_layout=OUT_PERMUTED, topk_w=None,
-                   gran=wscale.CHANNEL):
+                   gran=wscale.CHANNEL, a_fmt="e4m3"):
     """Oracle of one grouped call.
 
     ``x`` FP16 [T or R, K or 2K]; ``ids`` int [T, top_k]; ``w_q`` uint8 [E, N, K];
@@ -80,7 +80,7 @@ def grouped_linear(x, in_layout, act, ids, w_q, s_w, out_layout=OUT_PERMUTED, to
 
     h = ffn.silu_mul(x16, k) if act == ACT_SILU_MUL else None
     rows = h if h is not None else x16
-    a_q, a_scale = quant.quantize_rows(rows)
+    a_q, a_scale = quant.quantize_rows(rows, a_fmt)
 
     y_perm = np.zeros((r_total, n), dtype=np.float16)
     for e in range(e_count):
@@ -90,9 +90,9 @@ def grouped_linear(x, in_layout, act, ids, w_q, s_w, out_layout=OUT_PERMUTED, to
         r = np.arange(lo, hi)
         src = perm[r] // top_k if in_layout == IN_TOKENS else r
         if gran == wscale.CHANNEL:
-            y_perm[r] = linear.linear(a_q[src], a_scale[src], w_q[e], s_w[e])
+            y_perm[r] = linear.linear(a_q[src], a_scale[src], w_q[e], s_w[e], a_fmt)
         else:
-            y_perm[r] = wscale.linear(a_q[src], a_scale[src], w_q[e], s_w[e], gran)
+            y_perm[r] = wscale.linear(a_q[src], a_scale[src], w_q[e], s_w[e], gran, a_fmt)
 
     out = {"y_perm": y_perm, "a_q": a_q, "a_scale": a_scale, "h": h,
            "counts": counts, "offsets": offsets, "perm": perm, "pos": pos}
@@ -114,7 +114,8 @@ def combine(y_perm, pos, topk_w):
     return acc.astype(np.float16)
 
 
-def grouped_linear_check(y_gpu_perm, a_q, a_scale, in_layout, ids, w_q, s_w, gran=wscale.CHANNEL):
+def grouped_linear_check(y_gpu_perm, a_q, a_scale, in_layout, ids, w_q, s_w, gran=wscale.CHANNEL,
+                         a_fmt="e4m3"):
     """Stage check of a GPU permuted GEMM output against the GPU's own quantized input.
 
     Returns ``(ok, worst |d|/tol)`` over all permuted rows.
@@ -129,9 +130,9 @@ def grouped_linear_check(y_gpu_perm, a_q, a_scale, in_layout, ids, w_q, s_w, gra
         r = np.arange(lo, hi)
         src = perm[r] // top_k if in_layout == IN_TOKENS else r
         if gran == wscale.CHANNEL:
-            good, ratio, _ = linear.check(y_gpu_perm[r], a_q[src], a_scale[src], w_q[e], s_w[e])
+            good, ratio, _ = linear.check(y_gpu_perm[r], a_q[src], a_scale[src], w_q[e], s_w[e], a_fmt)
         else:
-            good, ratio, _ = wscale.check(y_gpu_perm[r], a_q[src], a_scale[src], w_q[e], s_w[e], gran)
+            good, ratio, _ = wscale.check(y_gpu_perm[r], a_q[src], a_scale[src], w_q[e], s_w[e], gran, a_fmt)
         ok &= good
         worst = max(worst, ratio)
     return ok, worst

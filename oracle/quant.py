@@ -25,24 +25,29 @@ rounding innocuous?", 1995).
 
 import numpy as np
 
-from . import e4m3
+from . import e4m3, e5m2
 
 EPS = 2.0 ** -24
 QMAX = 448.0
+# Target formats: codec and largest finite magnitude.  E5M2 (57344) serves the variant with
+# E5M2 activations of page "FP8量化在生成式推荐系统OneRec-V2中的优化实践", §2.2.
+FORMATS = {"e4m3": (e4m3, QMAX), "e5m2": (e5m2, e5m2.MAX_FINITE)}
 
 
-def row_scale(amax):
+def row_scale(amax, qmax=QMAX):
     """FP32 scale per row from the rows' absolute maxima (float64 in, float32 out)."""
     amax = np.asarray(amax, dtype=np.float64)
-    return (np.maximum(amax, EPS) / QMAX).astype(np.float32)
+    return (np.maximum(amax, EPS) / qmax).astype(np.float32)
 
 
-def quantize_rows(x):
-    """Quantize each row of a 2-D FP16 array.
+def quantize_rows(x, fmt="e4m3"):
+    """Quantize each row of a 2-D FP16 array to ``fmt`` ("e4m3", or "e5m2" with 57344 in
+    place of 448).
 
-    Returns ``(q, s)``: ``q`` uint8 E4M3 bytes with the shape of ``x`` and ``s``
-    float32 scales, one per row.
+    Returns ``(q, s)``: ``q`` uint8 bytes with the shape of ``x`` and ``s`` float32 scales,
+    one per row.
     """
+    codec, qmax = FORMATS[fmt]
     x16 = np.asarray(x)
     if x16.dtype != np.float16:
         raise TypeError("the quantizer takes FP16 rows")
@@ -53,12 +58,12 @@ def quantize_rows(x):
         return np.zeros((0, k), np.uint8), np.zeros((0,), np.float32)
     xd = x16.astype(np.float64)
     amax = np.max(np.abs(xd), axis=1) if k > 0 else np.zeros(rows)
-    s = row_scale(amax)
+    s = row_scale(amax, qmax)
     quotient = (xd / s.astype(np.float64)[:, None]).astype(np.float32)
-    q = e4m3.encode(quotient.astype(np.float64))
+    q = codec.encode(quotient.astype(np.float64))
     return q, s
 
 
-def dequantize_rows(q, s):
+def dequantize_rows(q, s, fmt="e4m3"):
     """float64 values ``decode(q) * s`` (row-wise scale)."""
-    return e4m3.decode(q) * np.asarray(s, dtype=np.float64)[:, None]
+    return FORMATS[fmt][0].decode(q) * np.asarray(s, dtype=np.float64)[:, None]

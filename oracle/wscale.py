@@ -89,15 +89,15 @@ def _k_blocks(k):
     return [(j, slice(j * BLOCK, (j + 1) * BLOCK)) for j in range(k // BLOCK)]
 
 
-def _reference(x_q, s_x, w_q, w_s, gran):
+def _reference(x_q, s_x, w_q, w_s, gran, a_fmt="e4m3"):
     """(float64 y*, float64 tolerance weight sum_j S |P|_j) for each output."""
     sx = np.asarray(s_x, dtype=np.float64)[:, None]
     if gran == CHANNEL or gran == TENSOR:
         n = w_q.shape[0]
         sw = np.asarray(w_s, dtype=np.float64).reshape(-1)
         sw = np.full(n, sw[0]) if gran == TENSOR else sw
-        acc = lin.gemm_exact(x_q, w_q)
-        absacc = lin.gemm_abs_exact(x_q, w_q)
+        acc = lin.gemm_exact(x_q, w_q, a_fmt)
+        absacc = lin.gemm_abs_exact(x_q, w_q, a_fmt)
         return acc * sx * sw[None, :], absacc * sw[None, :]
     if gran != BLOCK128:
         raise ValueError("unknown granularity %r" % (gran,))
@@ -109,20 +109,20 @@ def _reference(x_q, s_x, w_q, w_s, gran):
     weight = np.zeros((x_q.shape[0], n))
     for j, ks in _k_blocks(k):
         s_col = np.repeat(S[:, j], BLOCK)[None, :]          # block scale of each output column
-        total += s_col * lin.gemm_exact(x_q[:, ks], w_q[:, ks])
-        weight += s_col * lin.gemm_abs_exact(x_q[:, ks], w_q[:, ks])
+        total += s_col * lin.gemm_exact(x_q[:, ks], w_q[:, ks], a_fmt)
+        weight += s_col * lin.gemm_abs_exact(x_q[:, ks], w_q[:, ks], a_fmt)
     return total * sx, weight
 
 
-def linear(x_q, s_x, w_q, w_s, gran):
+def linear(x_q, s_x, w_q, w_s, gran, a_fmt="e4m3"):
     """FP16 output of the quantized linear with weight scales of granularity ``gran``."""
-    y, _ = _reference(x_q, s_x, w_q, w_s, gran)
+    y, _ = _reference(x_q, s_x, w_q, w_s, gran, a_fmt)
     return y.astype(np.float16)
 
 
-def check(y_gpu, x_q, s_x, w_q, w_s, gran):
+def check(y_gpu, x_q, s_x, w_q, w_s, gran, a_fmt="e4m3"):
     """Compare a GPU output with the oracle.  Returns ``(ok, worst |d|/tol, y_ref)``."""
-    y, weight = _reference(x_q, s_x, w_q, w_s, gran)
+    y, weight = _reference(x_q, s_x, w_q, w_s, gran, a_fmt)
     y_ref = y.astype(np.float16)
     tol = 2.0 * lin.ulp16(y_ref) + 1e-3 * np.asarray(s_x, dtype=np.float64)[:, None] * weight
     d = np.abs(np.asarray(y_gpu, dtype=np.float64) - y_ref.astype(np.float64))
