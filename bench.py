@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel breakdown")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the weight-scale variants (per-tensor FFN, 128x128-block MoE weights)")
+                    help="skip the variants (per-tensor FFN and 128x128-block MoE weight scales, E5M2 activations)")
     ap.add_argument("--rocprof-summary", default=None, metavar="PATH",
                     help="print per-(kernel, grid) dispatch statistics of a rocprofv3 output "
                          "(a *_results.db, a *_kernel_trace.csv, or a directory holding one) and exit")
@@ -114,8 +114,8 @@ class Path:
         dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
         self.calls = []     # (workload, label, kind, flops, bytes_moved, fn)
         self.qbytes = []    # per call: bytes the row quantizer must move
-        # weight-scale variants, timed apart from the step: (workload, call, wscale, flops,
-        # index of the per-channel call of the same shape, fn)
+        # variants, timed apart from the step: (workload, call, variant, flops, index of the
+        # per-channel E4M3 call of the same shape, fn)
         self.variants = []
         self.flops = 0
         want = set(only.split(",")) if only else {"attention", "ffn", "moe", "layer_small_m"}
@@ -192,6 +192,13 @@ class Path:
                 self.variants.append(("ffn", "down", "tensor", self.calls[n0 - 1][3], n0 - 1,
                                       lambda h_t=h_t, tdn=tdn, y_t=y_t, ws_dn=ws_dn: rq.linear(
                                           h_t, *tdn, out=y_t, workspace=ws_dn, wscale="tensor")))
+                # the dense FFN with E5M2 activations (per-channel E4M3 weights)
+                self.variants.append(("ffn", "gate_up", "e5m2 activations", self.calls[n0 - 2][3], n0 - 2,
+                                      lambda x3=x3, w=wgu, h_t=h_t, ws_gu=ws_gu: rq.linear(
+                                          x3, *w, act="gate_silu", out=h_t, workspace=ws_gu, afmt="e5m2")))
+                self.variants.append(("ffn", "down", "e5m2 activations", self.calls[n0 - 1][3], n0 - 1,
+                                      lambda h_t=h_t, w=wdn, y_t=y_t, ws_dn=ws_dn: rq.linear(
+                                          h_t, *w, out=y_t, workspace=ws_dn, afmt="e5m2")))
             self.config["ffn"] = "4096 tokens x 2048; gate/up 2x8192, down K=8192"
         if "moe" in want:
             d = workloads.make(4)
@@ -277,27 +284,29 @@ def kernel_breakdown(path, hip, reps=5):
 
 
 def variant_breakdown(path, hip, reps=5):
-    """GEMM time of each weight-scale variant next to the per-channel call of the same shape."""
+    """GEMM and quantizer time of each variant next to the per-channel E4M3 call of the same
+    shape."""
     from fp8_quantized_generative_amd import _lib
     lib = _lib.load()
 
-    def gemm_ms(fn):
+    def kernel_ms(fn, kind):
         fn()
         ts = []
         for _ in range(reps):
             a, b = hip.event(), hip.event()
-            lib.rq_time_next_kernel(_lib.RQ_KERNEL_GEMM, a, b)
+            lib.rq_time_next_kernel(kind, a, b)
             fn()
             ts.append(hip.elapsed_ms(a, b))
         return float(np.median(ts))
 
     rows = []
-    for work, label, wscale, fl, ref, fn in path.variants:
-        ms, ref_ms = gemm_ms(fn), gemm_ms(path.calls[ref][5])
-        rows.append({"workload": work, "call": label, "wscale": wscale, "gemm_us": round(ms * 1e3, 2),
+    for work, label, variant, fl, ref, fn in path.variants:
+        ms, ref_ms = kernel_ms(fn, _lib.RQ_KERNEL_GEMM), kernel_ms(path.calls[ref][5], _lib.RQ_KERNEL_GEMM)
+        q_ms = kernel_ms(fn, _lib.RQ_KERNEL_QUANT)
+        rows.append({"workload": work, "call": label, "variant": variant, "gemm_us": round(ms * 1e3, 2),
                      "gemm_tflops": round(fl / (ms * 1e-3) / 1e12, 1),
                      "gemm_frac_fp8_peak": round(fl / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
-                     "channel_gemm_us": round(ref_ms * 1e3, 2)})
+                     "quant_us": round(q_ms * 1e3, 2), "reference_gemm_us": round(ref_ms * 1e3, 2)})
     return rows
 
 
@@ -648,8 +657,8 @@ def main():
         print("[bench] per-kernel breakdown", file=sys.stderr, flush=True)
         result["kernels"] = kernel_breakdown(path, hip)
     if path.variants:
-        print("[bench] weight-scale variants", file=sys.stderr, flush=True)
-        result["wscale_variants"] = variant_breakdown(path, hip)
+        print("[bench] variants", file=sys.stderr, flush=True)
+        result["variants"] = variant_breakdown(path, hip)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         del path

@@ -18,12 +18,13 @@ import torch
 from . import _lib
 from ._lib import (RQ_ACT_GATE_SILU, RQ_ACT_NONE, RQ_ACT_SILU_MUL, RQ_MOE_IN_PERMUTED, RQ_MOE_IN_TOKENS,  # noqa: F401
                    RQ_MOE_OUT_COMBINED, RQ_MOE_OUT_PERMUTED, RQ_WSCALE_BLOCK128, RQ_WSCALE_CHANNEL,
-                   RQ_WSCALE_TENSOR, DebugOut, RqError)
+                   RQ_WSCALE_TENSOR, RQ_FP8_E4M3, RQ_FP8_E5M2, DebugOut, RqError)
 
 ACTS = {"none": RQ_ACT_NONE, "silu_mul": RQ_ACT_SILU_MUL, "gate_silu": RQ_ACT_GATE_SILU}
 IN_LAYOUTS = {"tokens": RQ_MOE_IN_TOKENS, "permuted": RQ_MOE_IN_PERMUTED}
 OUT_LAYOUTS = {"permuted": RQ_MOE_OUT_PERMUTED, "combined": RQ_MOE_OUT_COMBINED}
 WSCALES = {"channel": RQ_WSCALE_CHANNEL, "tensor": RQ_WSCALE_TENSOR, "block128": RQ_WSCALE_BLOCK128}
+AFMTS = {"e4m3": RQ_FP8_E4M3, "e5m2": RQ_FP8_E5M2}
 
 
 def scale_shape(lead, n, k, wscale):
@@ -118,17 +119,20 @@ def _debug(debug, q_rows, h_rows, k, act, device):
     return d, s
 
 
-def linear(x, w_q, w_scale, act="none", out=None, workspace=None, debug=False, stream=None, wscale="channel"):
+def linear(x, w_q, w_scale, act="none", out=None, workspace=None, debug=False, stream=None, wscale="channel",
+           afmt="e4m3"):
     """W8A8 FP8 linear: FP16 x [M, K] (or [M, 2K] for ``act='silu_mul'``) -> FP16 y [M, N]
     (or h [M, N/2] for ``act='gate_silu'``, whose weight rows interleave 32 gate and 32 up
     features; see ``interleave_gate_up``).
 
     With ``debug=True`` returns ``(y, {"a_q", "a_scale", "h"})``: the quantized GEMM input
     (and the SiLU*up rows).  ``wscale`` names the granularity of ``w_scale`` (see
-    ``quant_weights``).
+    ``quant_weights``); ``afmt`` the format the activations are quantized to ("e4m3" or
+    "e5m2").
     """
     a = _code(ACTS, act, "act")
     g = _code(WSCALES, wscale, "wscale")
+    f = _code(AFMTS, afmt, "afmt")
     _dev(x, torch.float16, "x")
     _dev(w_q, torch.uint8, "w_q")
     _dev(w_scale, torch.float32, "w_scale")
@@ -148,7 +152,7 @@ def linear(x, w_q, w_scale, act="none", out=None, workspace=None, debug=False, s
     ws = _workspace(ws_bytes, x.device, workspace)
     dbg, dbg_s = _debug(debug, m, m, k, a, x.device)
     _shape(w_scale, scale_shape((), n, k, g), "w_scale")
-    st = lib.rq_fp8_linear_ex(_ptr(x), m, k, a, _ptr(w_q), _ptr(w_scale), g, n, _ptr(out), _ptr(ws),
+    st = lib.rq_fp8_linear_ex(_ptr(x), m, k, a, f, _ptr(w_q), _ptr(w_scale), g, n, _ptr(out), _ptr(ws),
                               ws.numel(), ctypes.byref(dbg_s) if dbg_s is not None else None,
                               _stream(x, stream))
     _lib.check("rq_fp8_linear_ex", st)
@@ -157,7 +161,7 @@ def linear(x, w_q, w_scale, act="none", out=None, workspace=None, debug=False, s
 
 def moe_grouped_linear(x, topk_ids, w_q, w_scale, in_layout="tokens", act="none",
                        out_layout="permuted", topk_w=None, out=None, workspace=None,
-                       debug=False, stream=None, wscale="channel"):
+                       debug=False, stream=None, wscale="channel", afmt="e4m3"):
     """Expert grouped W8A8 linear.
 
     ``x``: FP16 [T, K*] (tokens) or [T*top_k, K*] (permuted), K* = 2K for ``silu_mul``;
@@ -172,6 +176,7 @@ def moe_grouped_linear(x, topk_ids, w_q, w_scale, in_layout="tokens", act="none"
     a = _code(ACTS, act, "act")
     ol = _code(OUT_LAYOUTS, out_layout, "out_layout")
     g = _code(WSCALES, wscale, "wscale")
+    f = _code(AFMTS, afmt, "afmt")
     _dev(x, torch.float16, "x")
     _dev(topk_ids, torch.int32, "topk_ids")
     _dev(w_q, torch.uint8, "w_q")
@@ -195,7 +200,7 @@ def moe_grouped_linear(x, topk_ids, w_q, w_scale, in_layout="tokens", act="none"
     dbg, dbg_s = _debug(debug, r, rows, k, a, x.device)
     _shape(w_scale, scale_shape((e,), n, k, g), "w_scale")
     st = lib.rq_fp8_moe_grouped_linear_ex(
-        _ptr(x), il, a, _ptr(topk_ids), _ptr(topk_w), t, top_k, _ptr(w_q), _ptr(w_scale), g, e, n, k,
+        _ptr(x), il, a, f, _ptr(topk_ids), _ptr(topk_w), t, top_k, _ptr(w_q), _ptr(w_scale), g, e, n, k,
         _ptr(out), ol, _ptr(ws), ws.numel(), ctypes.byref(dbg_s) if dbg_s is not None else None,
         _stream(x, stream))
     _lib.check("rq_fp8_moe_grouped_linear_ex", st)

@@ -157,10 +157,11 @@ size_t rq_fp8_linear_workspace_size(int64_t M, int64_t K, int act) {
   return align_up((size_t)(M * K)) + align_up((size_t)M * sizeof(float));
 }
 
-int rq_fp8_linear_ex(const uint16_t* x, int64_t M, int64_t K, int act, const uint8_t* w_q,
+int rq_fp8_linear_ex(const uint16_t* x, int64_t M, int64_t K, int act, int a_fmt, const uint8_t* w_q,
                      const float* w_scale, int w_gran, int64_t N, uint16_t* y, void* workspace,
                      size_t workspace_bytes, const rq_debug_out* dbg, void* stream) {
   if (act != RQ_ACT_NONE && act != RQ_ACT_SILU_MUL && act != RQ_ACT_GATE_SILU) return RQ_ERR_ARG;
+  if (a_fmt != RQ_FP8_E4M3 && a_fmt != RQ_FP8_E5M2) return RQ_ERR_ARG;
   if (w_gran != RQ_WSCALE_CHANNEL && w_gran != RQ_WSCALE_TENSOR && w_gran != RQ_WSCALE_BLOCK128) return RQ_ERR_ARG;
   if (M < 0 || K <= 0 || N <= 0) return RQ_ERR_SHAPE;
   if (K % 16 != 0 || N % 16 != 0 || (act == RQ_ACT_GATE_SILU && N % 64 != 0)) return RQ_ERR_ALIGN;
@@ -190,8 +191,8 @@ int rq_fp8_linear_ex(const uint16_t* x, int64_t M, int64_t K, int act, const uin
   {
     Hook hook(RQ_KERNEL_QUANT, s);
     const int in_act = act == RQ_ACT_SILU_MUL ? RQ_ACT_SILU_MUL : RQ_ACT_NONE;
-    if (rq::launch_quant_rows(x, M, K, in_act, xq, sx, act == RQ_ACT_SILU_MUL ? dh : nullptr, nullptr, 0, s) !=
-        hipSuccess)
+    if (rq::launch_quant_rows(x, M, K, in_act, xq, sx, act == RQ_ACT_SILU_MUL ? dh : nullptr, nullptr, 0, s,
+                              a_fmt) != hipSuccess)
       return RQ_ERR_HIP;
   }
   rq::GemmArgs g{};
@@ -207,6 +208,7 @@ int rq_fp8_linear_ex(const uint16_t* x, int64_t M, int64_t K, int act, const uin
   g.E = 1;
   g.gate = act == RQ_ACT_GATE_SILU ? 1 : 0;
   g.b_gran = w_gran;
+  g.a_fmt = a_fmt;
   Hook hook(RQ_KERNEL_GEMM, s);
   return rq::launch_gemm_dense(g, s) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
@@ -214,8 +216,8 @@ int rq_fp8_linear_ex(const uint16_t* x, int64_t M, int64_t K, int act, const uin
 int rq_fp8_linear(const uint16_t* x, int64_t M, int64_t K, int act, const uint8_t* w_q,
                   const float* w_scale, int64_t N, uint16_t* y, void* workspace,
                   size_t workspace_bytes, const rq_debug_out* dbg, void* stream) {
-  return rq_fp8_linear_ex(x, M, K, act, w_q, w_scale, RQ_WSCALE_CHANNEL, N, y, workspace, workspace_bytes, dbg,
-                          stream);
+  return rq_fp8_linear_ex(x, M, K, act, RQ_FP8_E4M3, w_q, w_scale, RQ_WSCALE_CHANNEL, N, y, workspace,
+                          workspace_bytes, dbg, stream);
 }
 
 size_t rq_fp8_moe_workspace_size(int64_t T, int top_k, int64_t E, int64_t N, int64_t K,
@@ -226,13 +228,14 @@ size_t rq_fp8_moe_workspace_size(int64_t T, int top_k, int64_t E, int64_t N, int
          align_up(l.tile_table) + align_up(l.perm) + align_up(l.pos) + align_up(l.block_hist) + align_up(l.y_perm);
 }
 
-int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act, const int32_t* topk_ids,
+int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act, int a_fmt, const int32_t* topk_ids,
                                  const uint16_t* topk_w, int64_t T, int top_k, const uint8_t* w_q,
                                  const float* w_scale, int w_gran, int64_t E, int64_t N, int64_t K, uint16_t* y,
                                  int out_layout, void* workspace, size_t workspace_bytes,
                                  const rq_debug_out* dbg, void* stream) {
   if (act != RQ_ACT_NONE && act != RQ_ACT_SILU_MUL && act != RQ_ACT_GATE_SILU) return RQ_ERR_ARG;
   if (w_gran != RQ_WSCALE_CHANNEL && w_gran != RQ_WSCALE_TENSOR && w_gran != RQ_WSCALE_BLOCK128) return RQ_ERR_ARG;
+  if (a_fmt != RQ_FP8_E4M3 && a_fmt != RQ_FP8_E5M2) return RQ_ERR_ARG;
   if (in_layout != RQ_MOE_IN_TOKENS && in_layout != RQ_MOE_IN_PERMUTED) return RQ_ERR_ARG;
   if (out_layout != RQ_MOE_OUT_PERMUTED && out_layout != RQ_MOE_OUT_COMBINED) return RQ_ERR_ARG;
   if (T < 0 || K <= 0 || N <= 0 || E < 1 || E > kMaxExperts || top_k < 1 || top_k > E)
@@ -285,7 +288,7 @@ int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act, cons
     const bool tokens = in_layout == RQ_MOE_IN_TOKENS;
     const int in_act = act == RQ_ACT_SILU_MUL ? RQ_ACT_SILU_MUL : RQ_ACT_NONE;
     if (rq::launch_quant_rows(x, rows, K, in_act, aq, as, act == RQ_ACT_SILU_MUL ? dh : nullptr,
-                              tokens ? pos : nullptr, tokens ? top_k : 0, s) != hipSuccess)
+                              tokens ? pos : nullptr, tokens ? top_k : 0, s, a_fmt) != hipSuccess)
       return RQ_ERR_HIP;
   }
   rq::GemmArgs g{};
@@ -303,6 +306,7 @@ int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act, cons
   g.E = (int32_t)E;
   g.gate = act == RQ_ACT_GATE_SILU ? 1 : 0;
   g.b_gran = w_gran;
+  g.a_fmt = a_fmt;
   {
     Hook hook(RQ_KERNEL_GEMM, s);
     if (rq::launch_gemm_grouped(g, kind, s) != hipSuccess) return RQ_ERR_HIP;
@@ -320,7 +324,7 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const i
                               const float* w_scale, int64_t E, int64_t N, int64_t K, uint16_t* y,
                               int out_layout, void* workspace, size_t workspace_bytes,
                               const rq_debug_out* dbg, void* stream) {
-  return rq_fp8_moe_grouped_linear_ex(x, in_layout, act, topk_ids, topk_w, T, top_k, w_q, w_scale,
+  return rq_fp8_moe_grouped_linear_ex(x, in_layout, act, RQ_FP8_E4M3, topk_ids, topk_w, T, top_k, w_q, w_scale,
                                       RQ_WSCALE_CHANNEL, E, N, K, y, out_layout, workspace, workspace_bytes, dbg,
                                       stream);
 }

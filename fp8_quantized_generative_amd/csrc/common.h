@@ -64,9 +64,12 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // Quantize `rows` FP16 rows (act: 0 none, 1 SiLU*up).  With pos == nullptr row t goes to
 // output row t; otherwise to output rows pos[t * fanout + k], k < fanout (a token's copies
 // in the permuted MoE order).  h (SiLU only, may be null) receives the FP16 SiLU*up rows.
+// Activation formats (the values of the C ABI's RQ_FP8_*): OCP E4M3, or OCP E5M2.
+enum { kFmtE4M3 = 0, kFmtE5M2 = 1 };
+
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t K, int act,
                              uint8_t* q, float* scale, uint16_t* h, const int32_t* pos, int fanout,
-                             hipStream_t stream);
+                             hipStream_t stream, int fmt = kFmtE4M3);
 
 // Weight-scale granularities (the values of the C ABI's RQ_WSCALE_*): one FP32 scale per
 // output channel ([E][N]), per tensor ([E]) or per 128 x 128 block ([E][N/128][K/128]).
@@ -96,6 +99,7 @@ struct GemmArgs {
   int32_t E;
   int32_t gate;               // 1: gated SiLU output (see rq_fp8.h, RQ_ACT_GATE_SILU), y is [rows][N/2]
   int32_t b_gran;             // kScaleChannel, kScaleTensor or kScaleBlock128 (layout of b_scale)
+  int32_t a_fmt;              // kFmtE4M3 or kFmtE5M2 (the bytes of a)
 };
 
 // GEMM tile shapes (rows x columns of output per workgroup).

@@ -277,8 +277,11 @@ __device__ __forceinline__ TileDesc2 tile_descs(const GemmArgs& p, const TileInf
   return d;
 }
 
-template <class C, bool GROUPED, bool GATE, bool BLK>
+template <class C, bool GROUPED, bool GATE, bool BLK, bool A5>
 __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles, int n_tiles) {
+  // operand formats of the MFMA: the weight fragment (first operand) is E4M3, the activation
+  // fragment (second) E4M3 or, with A5, E5M2 (format code 1 of the f8f6f4 instruction)
+  constexpr int kFmtB = A5 ? 1 : 0;
   static_assert(!BLK || (C::WN <= kScaleBlock && kScaleBlock % C::WN == 0),
                 "a wave's columns lie in one 128-column scale block");
   static_assert(!GATE || C::TJ % 2 == 0, "gated output pairs 32-column gate and up blocks in a wave");
@@ -524,9 +527,9 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
         const v8i bf = as_v8(bc[2 * jj], bc[2 * jj + 1]);
         const v8i af = as_v8(fa[2 * i], fa[2 * i + 1]);
         if constexpr (kFirst)
-          acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, (v16f){}, 0, 0, 0, 0, 0, 0);
+          acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, (v16f){}, 0, kFmtB, 0, 0, 0, 0);
         else
-          acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[i][jj], 0, 0, 0, 0, 0, 0);
+          acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[i][jj], 0, kFmtB, 0, 0, 0, 0);
         if constexpr (BLK) {
           if (resc_last && q >= 1) acc[(q - 1) / C::TJ][(q - 1) % C::TJ] *= ratio;
           if (resc_first && q == 0) acc[C::TI - 1][C::TJ - 1] *= ratio;
@@ -679,7 +682,7 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
 }
 
 // Workgroups of this kernel the device keeps resident at once (all CUs), cached per device.
-template <class C, bool GROUPED, bool GATE, bool BLK>
+template <class C, bool GROUPED, bool GATE, bool BLK, bool A5>
 int resident_workgroups() {
   constexpr int kDevices = 64;
   static int cache[kDevices] = {};
@@ -689,7 +692,7 @@ int resident_workgroups() {
   if (cache[slot] > 0) return cache[slot];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_fp8_kernel<C, GROUPED, GATE, BLK>, C::NT, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_fp8_kernel<C, GROUPED, GATE, BLK, A5>, C::NT, 0) !=
           hipSuccess ||
       per_cu <= 0)
     per_cu = 1;
@@ -706,33 +709,39 @@ int64_t grid_cap_override() {
   return v > 0 ? (int64_t)v : 0;
 }
 
-template <class C, bool GROUPED, bool GATE, bool BLK>
+template <class C, bool GROUPED, bool GATE, bool BLK, bool A5>
 hipError_t launch_one(const GemmArgs& g, int m_tiles, hipStream_t stream) {
   const int n_tiles = (int)((g.N + C::BN - 1) / C::BN);
   const int64_t tiles = (int64_t)m_tiles * n_tiles;  // grouped: the worst case
-  int64_t cap = resident_workgroups<C, GROUPED, GATE, BLK>();
+  int64_t cap = resident_workgroups<C, GROUPED, GATE, BLK, A5>();
   const int64_t forced = grid_cap_override();
   if (forced > 0 && forced < cap) cap = forced;
   const int64_t want = (tiles + 7) / 8 * 8;
   const int64_t grid = want < cap ? want : cap;
-  gemm_fp8_kernel<C, GROUPED, GATE, BLK><<<dim3((unsigned)grid), dim3(C::NT), 0, stream>>>(g, m_tiles, n_tiles);
+  gemm_fp8_kernel<C, GROUPED, GATE, BLK, A5><<<dim3((unsigned)grid), dim3(C::NT), 0, stream>>>(g, m_tiles, n_tiles);
   return hipGetLastError();
 }
 
-template <class C, bool GROUPED, bool BLK>
+template <class C, bool GROUPED, bool BLK, bool A5>
 hipError_t launch_gate(const GemmArgs& g, int m_tiles, hipStream_t stream) {
   if constexpr (C::TJ % 2 == 0) {
-    if (g.gate) return launch_one<C, GROUPED, true, BLK>(g, m_tiles, stream);
+    if (g.gate) return launch_one<C, GROUPED, true, BLK, A5>(g, m_tiles, stream);
   } else {
     if (g.gate) return hipErrorInvalidValue;  // tile shapes with one 32-column block per wave
   }
-  return launch_one<C, GROUPED, false, BLK>(g, m_tiles, stream);
+  return launch_one<C, GROUPED, false, BLK, A5>(g, m_tiles, stream);
+}
+
+template <class C, bool GROUPED, bool A5>
+hipError_t launch_fmt(const GemmArgs& g, int m_tiles, hipStream_t stream) {
+  if (g.b_gran == kScaleBlock128) return launch_gate<C, GROUPED, true, A5>(g, m_tiles, stream);
+  return launch_gate<C, GROUPED, false, A5>(g, m_tiles, stream);
 }
 
 template <class C, bool GROUPED>
 hipError_t launch(const GemmArgs& g, int m_tiles, hipStream_t stream) {
-  if (g.b_gran == kScaleBlock128) return launch_gate<C, GROUPED, true>(g, m_tiles, stream);
-  return launch_gate<C, GROUPED, false>(g, m_tiles, stream);
+  if (g.a_fmt == kFmtE5M2) return launch_fmt<C, GROUPED, true>(g, m_tiles, stream);
+  return launch_fmt<C, GROUPED, false>(g, m_tiles, stream);
 }
 
 // Eight wavefronts (two per SIMD) for the large tiles: while one wavefront of a SIMD waits

@@ -72,26 +72,45 @@ __device__ __forceinline__ uint4 silu_mul8(uint4 g, uint4 u) {
                     silu_mul_pair(g.z, u.z), silu_mul_pair(g.w, u.w));
 }
 
+// Largest finite magnitude of the target format: E4M3 448, or E5M2 57344 (the E5M2
+// activations of page "FP8量化在生成式推荐系统OneRec-V2中的优化实践", §2.2).  57344 = 448 * 128,
+// so an E5M2 row's scale and rcp(scale) are the E4M3 ones times 2^-7 and 2^7 exactly and every
+// step of the quotient below scales by 2^7 exactly: the exhaustive check of the E4M3 quotient
+// covers the E5M2 one as well.
+template <bool E5>
+constexpr float kQMax = E5 ? 57344.0f : kFp8Max;
+
+template <bool E5>
 __device__ __forceinline__ float quotient(uint32_t hbits, float s, float rcp) {
   float ax = half_bits_to_float(hbits & 0x7FFFu);
   float q0 = ax * rcp;
   float r = __builtin_fmaf(-q0, s, ax);
   float q = __builtin_fmaf(r, rcp, q0);
-  return __builtin_fminf(q, kFp8Max);
+  return __builtin_fminf(q, kQMax<E5>);
 }
 
-// Four FP16 values (two packed words) -> four E4M3 bytes (one word).
+// Four FP16 values (two packed words) -> four E4M3 (or E5M2) bytes (one word).  The cast is
+// the hardware v_cvt_pk_fp8_f32 (v_cvt_pk_bf8_f32 for E5M2: OCP formats on gfx950, round to
+// nearest even) on magnitudes already clamped to the format's largest finite value.
+template <bool E5 = false>
 __device__ __forceinline__ uint32_t cast4(uint32_t d0, uint32_t d1, float s, float rcp) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(quotient(d0, s, rcp), quotient(d0 >> 16, s, rcp), 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(quotient(d1, s, rcp), quotient(d1 >> 16, s, rcp), w, true);
+  int w;
+  if constexpr (E5) {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(quotient<E5>(d0, s, rcp), quotient<E5>(d0 >> 16, s, rcp), 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(quotient<E5>(d1, s, rcp), quotient<E5>(d1 >> 16, s, rcp), w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(quotient<E5>(d0, s, rcp), quotient<E5>(d0 >> 16, s, rcp), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(quotient<E5>(d1, s, rcp), quotient<E5>(d1 >> 16, s, rcp), w, true);
+  }
   uint32_t signs = ((d0 >> 8) & 0x80u) | ((d0 >> 16) & 0x8000u) | ((d1 << 8) & 0x800000u) |
                    (d1 & 0x80000000u);
   return (uint32_t)w | signs;
 }
 
+template <bool E5 = false>
 __device__ __forceinline__ void row_scale(uint32_t amax_bits, float& s, float& rcp) {
   float amax = half_bits_to_float(amax_bits);
-  s = __fdiv_rn(__builtin_fmaxf(amax, kScaleFloor), kFp8Max);
+  s = __fdiv_rn(__builtin_fmaxf(amax, kScaleFloor), kQMax<E5>);
   rcp = __fdiv_rn(1.0f, s);
 }
 
@@ -99,7 +118,7 @@ __device__ __forceinline__ void row_scale(uint32_t amax_bits, float& s, float& r
 // wavefront part p owns chunks c = 64 p + l + 64 SPLIT j, j < CPL.  Splitting a long row over
 // several wavefronts keeps enough of them in flight when there are few rows; their partial
 // maxima meet in LDS.
-template <int CPL, bool SILU, int SPLIT>
+template <int CPL, bool SILU, int SPLIT, bool E5>
 __global__ __launch_bounds__(256) void quant_rows_regs(const uint16_t* __restrict__ x, int64_t rows,
                                                        int K, uint8_t* __restrict__ q,
                                                        float* __restrict__ scale,
@@ -143,15 +162,15 @@ __global__ __launch_bounds__(256) void quant_rows_regs(const uint16_t* __restric
     if (!valid) return;
   }
   float s, rcp;
-  row_scale(amax, s, rcp);
+  row_scale<E5>(amax, s, rcp);
 
   uint2 out[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int c = c0 + 64 * SPLIT * j;
     if (c < nchunk) {
-      out[j].x = cast4(v[j].x, v[j].y, s, rcp);
-      out[j].y = cast4(v[j].z, v[j].w, s, rcp);
+      out[j].x = cast4<E5>(v[j].x, v[j].y, s, rcp);
+      out[j].y = cast4<E5>(v[j].z, v[j].w, s, rcp);
       if (SILU && h_out != nullptr) st_global_16(h_out + row * (int64_t)K + 8 * c, v[j]);
     }
   }
@@ -169,7 +188,7 @@ __global__ __launch_bounds__(256) void quant_rows_regs(const uint16_t* __restric
 }
 
 // Rows wider than 64 * 8 * 16 values: two passes, the second re-reading the row.
-template <bool SILU>
+template <bool SILU, bool E5>
 __global__ __launch_bounds__(256) void quant_rows_loop(const uint16_t* __restrict__ x, int64_t rows,
                                                        int64_t K, uint8_t* __restrict__ q,
                                                        float* __restrict__ scale,
@@ -191,13 +210,13 @@ __global__ __launch_bounds__(256) void quant_rows_loop(const uint16_t* __restric
   for (int64_t c = lane; c < nchunk; c += 64) amax = absmax_packed(chunk(c, false), amax);
   amax = wave_max_u32(amax);
   float s, rcp;
-  row_scale(amax, s, rcp);
+  row_scale<E5>(amax, s, rcp);
   const int copies = pos != nullptr ? fanout : 1;
   for (int64_t c = lane; c < nchunk; c += 64) {
     uint4 v = chunk(c, true);
     uint2 out;
-    out.x = cast4(v.x, v.y, s, rcp);
-    out.y = cast4(v.z, v.w, s, rcp);
+    out.x = cast4<E5>(v.x, v.y, s, rcp);
+    out.y = cast4<E5>(v.z, v.w, s, rcp);
     for (int d = 0; d < copies; ++d) {
       const int64_t orow = pos != nullptr ? (int64_t)pos[row * fanout + d] : row;
       *reinterpret_cast<uint2*>(q + orow * K + 8 * c) = out;
@@ -208,29 +227,29 @@ __global__ __launch_bounds__(256) void quant_rows_loop(const uint16_t* __restric
     scale[pos != nullptr ? (int64_t)pos[row * fanout + d] : row] = s;
 }
 
-template <int CPL, bool SILU>
+template <int CPL, bool SILU, bool E5>
 hipError_t launch_split(int split, const uint16_t* x, int64_t rows, int k, uint8_t* q, float* scale, uint16_t* h,
                         const int32_t* pos, int fanout, hipStream_t stream) {
   const dim3 block(64 * kRowsPerBlock);
   const int per_block = kRowsPerBlock / split;
   const dim3 grid((unsigned)((rows + per_block - 1) / per_block));
   if (split == 4)
-    quant_rows_regs<CPL, SILU, 4><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h, pos, fanout);
+    quant_rows_regs<CPL, SILU, 4, E5><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h, pos, fanout);
   else if (split == 2)
-    quant_rows_regs<CPL, SILU, 2><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h, pos, fanout);
+    quant_rows_regs<CPL, SILU, 2, E5><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h, pos, fanout);
   else
-    quant_rows_regs<CPL, SILU, 1><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h, pos, fanout);
+    quant_rows_regs<CPL, SILU, 1, E5><<<grid, block, 0, stream>>>(x, rows, k, q, scale, h, pos, fanout);
   return hipGetLastError();
 }
 
-template <bool SILU>
+template <bool SILU, bool E5>
 hipError_t launch_impl(const uint16_t* x, int64_t rows, int64_t K, uint8_t* q, float* scale,
                        uint16_t* h, const int32_t* pos, int fanout, hipStream_t stream) {
   const int64_t nchunk = K / 8;
   const int k = (int)K;
   if (nchunk > 64 * 16) {
     const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-    quant_rows_loop<SILU><<<grid, dim3(64 * kRowsPerBlock), 0, stream>>>(x, rows, K, q, scale, h, pos, fanout);
+    quant_rows_loop<SILU, E5><<<grid, dim3(64 * kRowsPerBlock), 0, stream>>>(x, rows, K, q, scale, h, pos, fanout);
     return hipGetLastError();
   }
   // Wavefronts per row: split long rows while the launch would hold fewer than 8192
@@ -238,11 +257,11 @@ hipError_t launch_impl(const uint16_t* x, int64_t rows, int64_t K, uint8_t* q, f
   int split = 1;
   while (split < 4 && rows * split < 8192 && nchunk >= 64 * 4 * 2 * split) split *= 2;
   const int64_t per_lane = (nchunk + 64 * split - 1) / (64 * split);
-  if (per_lane <= 1) return launch_split<1, SILU>(split, x, rows, k, q, scale, h, pos, fanout, stream);
-  if (per_lane <= 2) return launch_split<2, SILU>(split, x, rows, k, q, scale, h, pos, fanout, stream);
-  if (per_lane <= 4) return launch_split<4, SILU>(split, x, rows, k, q, scale, h, pos, fanout, stream);
-  if (per_lane <= 8) return launch_split<8, SILU>(split, x, rows, k, q, scale, h, pos, fanout, stream);
-  return launch_split<16, SILU>(split, x, rows, k, q, scale, h, pos, fanout, stream);
+  if (per_lane <= 1) return launch_split<1, SILU, E5>(split, x, rows, k, q, scale, h, pos, fanout, stream);
+  if (per_lane <= 2) return launch_split<2, SILU, E5>(split, x, rows, k, q, scale, h, pos, fanout, stream);
+  if (per_lane <= 4) return launch_split<4, SILU, E5>(split, x, rows, k, q, scale, h, pos, fanout, stream);
+  if (per_lane <= 8) return launch_split<8, SILU, E5>(split, x, rows, k, q, scale, h, pos, fanout, stream);
+  return launch_split<16, SILU, E5>(split, x, rows, k, q, scale, h, pos, fanout, stream);
 }
 
 // ---- weight scales per 128 x 128 block and per tensor (page "FP8量化在生成式推荐系统
@@ -358,10 +377,14 @@ hipError_t launch_quant_tensor(const uint16_t* w, int64_t B, int64_t N, int64_t 
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t K, int act, uint8_t* q,
                              float* scale, uint16_t* h, const int32_t* pos, int fanout,
-                             hipStream_t stream) {
+                             hipStream_t stream, int fmt) {
   if (rows <= 0) return hipSuccess;
-  if (act == 1) return launch_impl<true>(x, rows, K, q, scale, h, pos, fanout, stream);
-  return launch_impl<false>(x, rows, K, q, scale, nullptr, pos, fanout, stream);
+  if (fmt == kFmtE5M2) {
+    if (act == 1) return launch_impl<true, true>(x, rows, K, q, scale, h, pos, fanout, stream);
+    return launch_impl<false, true>(x, rows, K, q, scale, nullptr, pos, fanout, stream);
+  }
+  if (act == 1) return launch_impl<true, false>(x, rows, K, q, scale, h, pos, fanout, stream);
+  return launch_impl<false, false>(x, rows, K, q, scale, nullptr, pos, fanout, stream);
 }
 
 }  // namespace rq

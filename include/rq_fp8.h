@@ -60,7 +60,7 @@ typedef enum {
   RQ_ERR_WORKSPACE = 4,   /* workspace smaller than the *_workspace_size result */
   RQ_ERR_UNSUPPORTED = 5, /* the current device is not gfx950 */
   RQ_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed */
-  RQ_ERR_ARG = 7          /* an unknown act / layout / w_gran value, or a missing topk_w */
+  RQ_ERR_ARG = 7          /* an unknown act / layout / a_fmt / w_gran value, or a missing topk_w */
 } rq_status;
 
 /* Activation applied to the FP16 input rows before they are quantized.
@@ -179,23 +179,33 @@ int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act,
  * s_x[m] and the last block's scale, each in FP32, and rounded to FP16. */
 enum { RQ_WSCALE_CHANNEL = 0, RQ_WSCALE_TENSOR = 1, RQ_WSCALE_BLOCK128 = 2 };
 
+/* Activation format (page "FP8量化在生成式推荐系统OneRec-V2中的优化实践", §2.2, puts
+ * activations in E5M2 and weights in E4M3).  RQ_FP8_E5M2: the run-time quantizer writes OCP
+ * E5M2 bytes (5 exponent bits, 2 mantissa bits, largest finite 57344) with the row formula
+ * above and 57344 in place of 448 - s = fl32(max(amax, 2^-24) / 57344),
+ * q = E5M2(fl32(x / s)), rounded to nearest even and saturated at +/-57344 - and the GEMM
+ * multiplies them with the E4M3 weights.  Weights are always E4M3. */
+enum { RQ_FP8_E4M3 = 0, RQ_FP8_E5M2 = 1 };
+
 /* rq_fp8_quant_weights with the weight-scale granularity w_gran (layouts above).
  * RQ_ERR_ARG for an unknown w_gran.  Per-tensor scales take four short kernels (amax words
  * are kept in w_scale until the last one writes the scales). */
 int rq_fp8_quant_weights_ex(const uint16_t* w, int64_t B, int64_t N, int64_t K, int w_gran,
                             uint8_t* w_q, float* w_scale, void* stream);
 
-/* rq_fp8_linear with weights quantized at granularity w_gran; w_scale has that layout
- * (B = 1).  rq_fp8_linear is this call with RQ_WSCALE_CHANNEL. */
-int rq_fp8_linear_ex(const uint16_t* x, int64_t M, int64_t K, int act,
+/* rq_fp8_linear with activations quantized to a_fmt (RQ_FP8_*; dbg->a_q then holds bytes of
+ * that format) and weights quantized at granularity w_gran; w_scale has that layout (B = 1).
+ * rq_fp8_linear is this call with RQ_FP8_E4M3 and RQ_WSCALE_CHANNEL.  RQ_ERR_ARG for an
+ * unknown a_fmt or w_gran. */
+int rq_fp8_linear_ex(const uint16_t* x, int64_t M, int64_t K, int act, int a_fmt,
                      const uint8_t* w_q, const float* w_scale, int w_gran, int64_t N,
                      uint16_t* y, void* workspace, size_t workspace_bytes,
                      const rq_debug_out* dbg, void* stream);
 
-/* rq_fp8_moe_grouped_linear with expert weights quantized at granularity w_gran; w_scale
- * has that layout with B = E.  rq_fp8_moe_grouped_linear is this call with
- * RQ_WSCALE_CHANNEL.  The workspace size does not depend on w_gran. */
-int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act,
+/* rq_fp8_moe_grouped_linear with activations quantized to a_fmt and expert weights quantized
+ * at granularity w_gran; w_scale has that layout with B = E.  rq_fp8_moe_grouped_linear is
+ * this call with RQ_FP8_E4M3 and RQ_WSCALE_CHANNEL.  The workspace size depends on neither. */
+int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act, int a_fmt,
                                  const int32_t* topk_ids, const uint16_t* topk_w,
                                  int64_t T, int top_k,
                                  const uint8_t* w_q, const float* w_scale, int w_gran,
