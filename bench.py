@@ -117,6 +117,7 @@ class Path:
         # variants, timed apart from the step: (workload, call, variant, flops, index of the
         # per-channel E4M3 call of the same shape, fn)
         self.variants = []
+        self.router = None  # (bytes per launch, fn) of the MoE router, timed apart from the step
         self.flops = 0
         want = set(only.split(",")) if only else {"attention", "ffn", "moe", "layer_small_m"}
 
@@ -219,6 +220,13 @@ class Path:
                                     dtype=torch.uint8, device="cuda")
                 ws_dn = torch.empty(rq.moe_workspace_size(16384, 2, 32, 2048, 4096, "permuted", "none", "combined"),
                                     dtype=torch.uint8, device="cuda")
+                # the FP16 router that would produce this step's routing (synthetic gate weights)
+                wg = dev((np.random.default_rng(1104).standard_normal((32, 2048)) / np.sqrt(2048)).astype(np.float16))
+                r_ids = torch.empty((16384, 2), dtype=torch.int32, device="cuda")
+                r_w = torch.empty((16384, 2), dtype=torch.float16, device="cuda")
+                self.router = (16384 * 2048 * 2 + 32 * 2048 * 2 + 16384 * 2 * 6,
+                               lambda x4=x4, wg=wg, r_ids=r_ids, r_w=r_w: rq.router_topk(
+                                   x4, wg, 2, topk_ids=r_ids, topk_w=r_w))
                 n0 = len(self.calls)
                 self.variants.append(("moe", "gate_up", "block128", self.calls[n0 - 2][3], n0 - 2,
                                       lambda x4=x4, ids=ids, bgu=bgu, h_b=h_b, ws_gu=ws_gu: rq.moe_grouped_linear(
@@ -659,6 +667,20 @@ def main():
     if path.variants:
         print("[bench] variants", file=sys.stderr, flush=True)
         result["variants"] = variant_breakdown(path, hip)
+    if path.router is not None:
+        by, fn = path.router
+        fn()
+        ts = []
+        for _ in range(5):
+            a, b = hip.event(), hip.event()
+            _lib.load().rq_time_next_kernel(_lib.RQ_KERNEL_ROUTER, a, b)
+            fn()
+            ts.append(hip.elapsed_ms(a, b))
+        r_ms = float(np.median(ts))
+        result["router"] = {"workload": "MoE router: 16384 tokens x 2048 FP16, 32 experts, top-2",
+                            "us": round(r_ms * 1e3, 2), "bytes_per_launch": by,
+                            "achieved_gbs": round(by / (r_ms * 1e-3) / 1e9, 1),
+                            "frac_hbm": round(by / (r_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         del path

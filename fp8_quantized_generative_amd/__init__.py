@@ -8,6 +8,7 @@ PyTorch provides device memory and the current stream.
                                                output channel, per tensor or per 128x128 block)
 * ``linear(x, w_q, w_scale, act=...)``         per-token quantization + FP8 GEMM + FP16 epilogue
 * ``moe_grouped_linear(x, ids, w_q, w_scale, ...)``  routing plan + grouped GEMM (+ combine)
+* ``router_topk(x, w_gate, top_k)``            FP16 MoE gate logits -> top-k expert ids and weights
 * ``linear_workspace_size`` / ``moe_workspace_size``  scratch sizes for caller-held workspaces
 """
 
@@ -205,6 +206,31 @@ def moe_grouped_linear(x, topk_ids, w_q, w_scale, in_layout="tokens", act="none"
         _stream(x, stream))
     _lib.check("rq_fp8_moe_grouped_linear_ex", st)
     return (out, dbg) if debug else out
+
+
+def router_topk(x, w_gate, top_k=2, topk_ids=None, topk_w=None, logits=False, stream=None):
+    """FP16 MoE gate: x [T, K] FP16 and gate weights [E, K] FP16 -> (topk_ids int32 [T, top_k],
+    topk_w FP16 [T, top_k]) - the routing inputs of ``moe_grouped_linear`` - plus the FP32
+    logits [T, E] when ``logits=True``."""
+    _dev(x, torch.float16, "x")
+    _dev(w_gate, torch.float16, "w_gate")
+    if x.dim() != 2 or w_gate.dim() != 2 or x.shape[1] != w_gate.shape[1]:
+        raise ValueError("x [T, K] and w_gate [E, K] must share K")
+    t, k = x.shape
+    e = w_gate.shape[0]
+    if topk_ids is None:
+        topk_ids = torch.empty((t, top_k), dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty((t, top_k), dtype=torch.float16, device=x.device)
+    _dev(topk_ids, torch.int32, "topk_ids")
+    _dev(topk_w, torch.float16, "topk_w")
+    _shape(topk_ids, (t, top_k), "topk_ids")
+    _shape(topk_w, (t, top_k), "topk_w")
+    lg = torch.empty((t, e), dtype=torch.float32, device=x.device) if logits else None
+    st = _lib.load().rq_moe_router_topk(_ptr(x), t, k, _ptr(w_gate), e, top_k, _ptr(topk_ids), _ptr(topk_w),
+                                        _ptr(lg), _stream(x, stream))
+    _lib.check("rq_moe_router_topk", st)
+    return (topk_ids, topk_w, lg) if logits else (topk_ids, topk_w)
 
 
 def interleave_gate_up(w_gu, block=32):

@@ -319,6 +319,27 @@ int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act, int 
   return RQ_OK;
 }
 
+int rq_moe_router_topk(const uint16_t* x, int64_t T, int64_t K, const uint16_t* w_gate, int64_t E, int top_k,
+                       int32_t* topk_ids, uint16_t* topk_w, float* logits, void* stream) {
+  if (T < 0 || K <= 0 || E < 1 || E > 32 || top_k < 1 || top_k > E || top_k > rq::router_max_topk())
+    return RQ_ERR_SHAPE;
+  if (K % 64 != 0) return RQ_ERR_ALIGN;
+  if (K > kMaxK || T * K > ((int64_t)1 << 40)) return RQ_ERR_SHAPE;
+  if (!w_gate) return RQ_ERR_NULL;
+  if (T > 0 && (!x || !topk_ids || !topk_w)) return RQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_gate, 16) || !aligned(topk_ids, 4) || !aligned(topk_w, 2) ||
+      !aligned(logits, 16))
+    return RQ_ERR_ALIGN;
+  if (T == 0) return RQ_OK;
+  const int dev = check_device();
+  if (dev != RQ_OK) return dev;
+  Hook hook(RQ_KERNEL_ROUTER, (hipStream_t)stream);
+  return rq::launch_router_topk(x, T, K, w_gate, E, top_k, topk_ids, topk_w, logits, (hipStream_t)stream) ==
+                 hipSuccess
+             ? RQ_OK
+             : RQ_ERR_HIP;
+}
+
 int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const int32_t* topk_ids,
                               const uint16_t* topk_w, int64_t T, int top_k, const uint8_t* w_q,
                               const float* w_scale, int64_t E, int64_t N, int64_t K, uint16_t* y,

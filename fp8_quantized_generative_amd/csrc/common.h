@@ -117,6 +117,12 @@ hipError_t launch_moe_plan(const int32_t* ids, int64_t T, int top_k, int64_t E, 
                            int32_t* pos, int32_t* block_hist, hipStream_t stream);
 int64_t moe_plan_blocks(int64_t R);
 
+// MoE router: FP16 logits of T rows x [K] against E <= 32 gate rows, top_k <= router_max_topk()
+// ids and FP16 weights per row, optional FP32 logits [T][E].  K a multiple of 64.
+hipError_t launch_router_topk(const uint16_t* x, int64_t T, int64_t K, const uint16_t* w, int64_t E, int top_k,
+                              int32_t* ids, uint16_t* topk_w, float* logits, hipStream_t stream);
+int router_max_topk();
+
 hipError_t launch_moe_combine(const uint16_t* y_perm, const int32_t* pos, const uint16_t* topk_w,
                               int64_t T, int top_k, int64_t N, uint16_t* out, hipStream_t stream);
 

@@ -214,6 +214,21 @@ int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act, int 
                                  void* workspace, size_t workspace_bytes,
                                  const rq_debug_out* dbg, void* stream);
 
+/* MoE router (page "FP8量化在生成式推荐系统OneRec-V2中的优化实践", §2.1: the routing gate
+ * stays FP16 and its top-k result is the input of the grouped GEMM above).
+ * x [T][K] FP16 token rows, w_gate [E][K] FP16 gate weights.  For each token:
+ *   logit[e] = sum_k x[k] * w_gate[e][k]   (FP16 products, FP32 accumulation, any order)
+ *   topk_ids[t][0..top_k)                  the top_k experts by logit, larger first, equal
+ *                                          logits to the lower expert index (int32)
+ *   topk_w[t][i] = fl16(exp(l_i - l_0) / sum_j exp(l_j - l_0))  over the selected logits,
+ *                                          computed in FP32 (FP16 out)
+ *   logits (optional, may be NULL)         the FP32 logits [T][E] the selection used.
+ * topk_ids and topk_w are exactly the inputs rq_fp8_moe_grouped_linear takes.
+ * Limits: 1 <= E <= 32, 1 <= top_k <= min(E, 4) (RQ_ERR_SHAPE), K a multiple of 64
+ * (RQ_ERR_ALIGN).  One kernel on `stream`; no workspace. */
+int rq_moe_router_topk(const uint16_t* x, int64_t T, int64_t K, const uint16_t* w_gate, int64_t E,
+                       int top_k, int32_t* topk_ids, uint16_t* topk_w, float* logits, void* stream);
+
 /* Kernel-level timing for benchmarks and profilers.  After this call, the next kernel
  * of the given kind that the calling thread enqueues (through any entry point above) is
  * bracketed by hipEventRecord(start_event) just before its launch and
@@ -221,7 +236,7 @@ int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act, int 
  * then disarms itself.  start_event / stop_event are hipEvent_t handles owned by the
  * caller; passing NULL for both disarms the hook.  Each kind has its own one-shot slot.
  * Returns RQ_ERR_ARG for an unknown kind and RQ_ERR_NULL if only one event is NULL. */
-enum { RQ_KERNEL_QUANT = 0, RQ_KERNEL_GEMM = 1, RQ_KERNEL_COMBINE = 2, RQ_KERNEL_KINDS = 3 };
+enum { RQ_KERNEL_QUANT = 0, RQ_KERNEL_GEMM = 1, RQ_KERNEL_COMBINE = 2, RQ_KERNEL_ROUTER = 3, RQ_KERNEL_KINDS = 4 };
 int rq_time_next_kernel(int kernel, void* start_event, void* stop_event);
 
 /* Static description of a status code ("ok", "null pointer", ...). */
