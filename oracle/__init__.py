@@ -27,6 +27,7 @@ Arithmetic is float64 and integers.  Every rounding is explicit.  Modules:
                the parity tolerance.
 * ``ffn``    - the SiLU(gate) * up intermediate of the dense and expert FFNs.
 * ``moe``    - the MoE routing plan, grouped linear over experts and the weighted combine.
+* ``attention`` - the FP16 short-context attention core between the QKV and O linears.
 * ``router`` - the FP16 MoE gate: logits, top-k expert selection and combine weights.
 * ``wscale`` - weight scales per tensor and per 128 x 128 block (page "FP8量化在生成式推荐
                系统OneRec-V2中的优化实践", §2.1 / §2.2) and the linear that uses them.
@@ -37,6 +38,6 @@ brute force over exact rationals, PyTorch's own float8_e4m3fn conversion and SiL
 No function is "parity unpinned".
 """
 
-from . import e4m3, e5m2, quant, linear, ffn, moe, router, wscale  # noqa: F401
+from . import attention, e4m3, e5m2, quant, linear, ffn, moe, router, wscale  # noqa: F401
 
-__all__ = ["e4m3", "e5m2", "quant", "linear", "ffn", "moe", "router", "wscale"]
+__all__ = ["attention", "e4m3", "e5m2", "quant", "linear", "ffn", "moe", "router", "wscale"]
