@@ -118,6 +118,7 @@ class Path:
         # per-channel E4M3 call of the same shape, fn)
         self.variants = []
         self.router = None  # (bytes per launch, fn) of the MoE router, timed apart from the step
+        self.attention = None  # the same for the attention core
         self.flops = 0
         want = set(only.split(",")) if only else {"attention", "ffn", "moe", "layer_small_m"}
 
@@ -169,8 +170,14 @@ class Path:
             d = workloads.make(2)
             wqkv = qw(d["w_qkv"])
             wo = qw(d["w_o"])
-            add_linear("attention", "qkv", dev(d["x"]), *wqkv)
+            qkv = add_linear("attention", "qkv", dev(d["x"]), *wqkv)
             add_linear("attention", "o", dev(d["attn_out"]), *wo)
+            if variants:
+                # the FP16 attention core between them, on the QKV call's output (128 requests x
+                # 32 positions, 16 heads of 128)
+                ao = torch.empty((4096, 2048), dtype=torch.float16, device="cuda")
+                self.attention = (qkv.numel() * 2 + ao.numel() * 2,
+                                  lambda qkv=qkv, ao=ao: rq.attention_core(qkv, 128, 32, 16, out=ao))
             self.config["attention"] = "4096 tokens x 2048; QKV 6144, O 2048"
         if "ffn" in want:
             d = workloads.make(3)
@@ -667,20 +674,24 @@ def main():
     if path.variants:
         print("[bench] variants", file=sys.stderr, flush=True)
         result["variants"] = variant_breakdown(path, hip)
-    if path.router is not None:
-        by, fn = path.router
+    for key, kind, what in (("router", _lib.RQ_KERNEL_ROUTER, "MoE router: 16384 tokens x 2048 FP16, 32 experts, top-2"),
+                            ("attention_core", _lib.RQ_KERNEL_ATTENTION,
+                             "attention core: 128 requests x 32 positions, 16 heads of 128, causal, FP16")):
+        item = path.router if key == "router" else path.attention
+        if item is None:
+            continue
+        by, fn = item
         fn()
         ts = []
         for _ in range(5):
             a, b = hip.event(), hip.event()
-            _lib.load().rq_time_next_kernel(_lib.RQ_KERNEL_ROUTER, a, b)
+            _lib.load().rq_time_next_kernel(kind, a, b)
             fn()
             ts.append(hip.elapsed_ms(a, b))
-        r_ms = float(np.median(ts))
-        result["router"] = {"workload": "MoE router: 16384 tokens x 2048 FP16, 32 experts, top-2",
-                            "us": round(r_ms * 1e3, 2), "bytes_per_launch": by,
-                            "achieved_gbs": round(by / (r_ms * 1e-3) / 1e9, 1),
-                            "frac_hbm": round(by / (r_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        k_ms = float(np.median(ts))
+        result[key] = {"workload": what, "us": round(k_ms * 1e3, 2), "bytes_per_launch": by,
+                       "achieved_gbs": round(by / (k_ms * 1e-3) / 1e9, 1),
+                       "frac_hbm": round(by / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         del path

@@ -8,6 +8,7 @@ PyTorch provides device memory and the current stream.
                                                output channel, per tensor or per 128x128 block)
 * ``linear(x, w_q, w_scale, act=...)``         per-token quantization + FP8 GEMM + FP16 epilogue
 * ``moe_grouped_linear(x, ids, w_q, w_scale, ...)``  routing plan + grouped GEMM (+ combine)
+* ``attention_core(qkv, requests, length, heads)``  FP16 causal short-context attention (QKV -> O input)
 * ``router_topk(x, w_gate, top_k)``            FP16 MoE gate logits -> top-k expert ids and weights
 * ``linear_workspace_size`` / ``moe_workspace_size``  scratch sizes for caller-held workspaces
 """
@@ -231,6 +232,21 @@ def router_topk(x, w_gate, top_k=2, topk_ids=None, topk_w=None, logits=False, st
                                         _ptr(lg), _stream(x, stream))
     _lib.check("rq_moe_router_topk", st)
     return (topk_ids, topk_w, lg) if logits else (topk_ids, topk_w)
+
+
+def attention_core(qkv, requests, length, heads, head_dim=128, out=None, stream=None):
+    """Causal short-context attention over the merged QKV output: qkv FP16
+    [requests * length, 3 * heads * head_dim] -> FP16 [requests * length, heads * head_dim]."""
+    _dev(qkv, torch.float16, "qkv")
+    hidden = heads * head_dim
+    _shape(qkv, (requests * length, 3 * hidden), "qkv")
+    if out is None:
+        out = torch.empty((requests * length, hidden), dtype=torch.float16, device=qkv.device)
+    _dev(out, torch.float16, "out")
+    _shape(out, (requests * length, hidden), "out")
+    st = _lib.load().rq_attention_core(_ptr(qkv), requests, length, heads, head_dim, _ptr(out), _stream(qkv, stream))
+    _lib.check("rq_attention_core", st)
+    return out
 
 
 def interleave_gate_up(w_gu, block=32):

@@ -13,7 +13,7 @@ RQ_OK = 0
 RQ_ACT_NONE, RQ_ACT_SILU_MUL, RQ_ACT_GATE_SILU = 0, 1, 2
 RQ_MOE_IN_TOKENS, RQ_MOE_IN_PERMUTED = 0, 1
 RQ_MOE_OUT_PERMUTED, RQ_MOE_OUT_COMBINED = 0, 1
-RQ_KERNEL_QUANT, RQ_KERNEL_GEMM, RQ_KERNEL_COMBINE, RQ_KERNEL_ROUTER = 0, 1, 2, 3
+RQ_KERNEL_QUANT, RQ_KERNEL_GEMM, RQ_KERNEL_COMBINE, RQ_KERNEL_ROUTER, RQ_KERNEL_ATTENTION = 0, 1, 2, 3, 4
 RQ_WSCALE_CHANNEL, RQ_WSCALE_TENSOR, RQ_WSCALE_BLOCK128 = 0, 1, 2
 RQ_FP8_E4M3, RQ_FP8_E5M2 = 0, 1
 
@@ -42,6 +42,7 @@ SIGNATURES = {
     "rq_fp8_moe_grouped_linear_ex": (_I, [_P, _I, _I, _I, _P, _P, _I64, _I, _P, _P, _I, _I64, _I64, _I64,
                                           _P, _I, _P, _SZ, ctypes.POINTER(DebugOut), _P]),
     "rq_moe_router_topk": (_I, [_P, _I64, _I64, _P, _I64, _I, _P, _P, _P, _P]),
+    "rq_attention_core": (_I, [_P, _I64, _I, _I, _I, _P, _P]),
     "rq_time_next_kernel": (_I, [_I, _P, _P]),
     "rq_status_string": (ctypes.c_char_p, [_I]),
     "rq_device_supported": (_I, [_I]),

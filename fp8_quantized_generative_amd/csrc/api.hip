@@ -340,6 +340,25 @@ int rq_moe_router_topk(const uint16_t* x, int64_t T, int64_t K, const uint16_t* 
              : RQ_ERR_HIP;
 }
 
+int rq_attention_core(const uint16_t* qkv, int64_t requests, int length, int heads, int head_dim, uint16_t* out,
+                      void* stream) {
+  if (requests < 0 || length < 1 || length > rq::attention_max_len() || heads < 1 ||
+      head_dim != rq::attention_head_dim())
+    return RQ_ERR_SHAPE;
+  if ((int64_t)heads * head_dim * 3 > kMaxOperandBytes / 2 ||
+      requests * length * (int64_t)heads * head_dim * 3 > ((int64_t)1 << 40))
+    return RQ_ERR_SHAPE;
+  if (requests > 0 && (!qkv || !out)) return RQ_ERR_NULL;
+  if (!aligned(qkv, 16) || !aligned(out, 16)) return RQ_ERR_ALIGN;
+  if (requests == 0) return RQ_OK;
+  const int dev = check_device();
+  if (dev != RQ_OK) return dev;
+  Hook hook(RQ_KERNEL_ATTENTION, (hipStream_t)stream);
+  return rq::launch_attention_core(qkv, requests, length, heads, out, (hipStream_t)stream) == hipSuccess
+             ? RQ_OK
+             : RQ_ERR_HIP;
+}
+
 int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const int32_t* topk_ids,
                               const uint16_t* topk_w, int64_t T, int top_k, const uint8_t* w_q,
                               const float* w_scale, int64_t E, int64_t N, int64_t K, uint16_t* y,

@@ -123,6 +123,13 @@ hipError_t launch_router_topk(const uint16_t* x, int64_t T, int64_t K, const uin
                               int32_t* ids, uint16_t* topk_w, float* logits, hipStream_t stream);
 int router_max_topk();
 
+// Short-context attention core: requests of `length` <= attention_max_len() rows, `heads` heads
+// of attention_head_dim() columns; qkv [requests * length][3 * hidden], out [.][hidden].
+hipError_t launch_attention_core(const uint16_t* qkv, int64_t requests, int length, int heads, uint16_t* out,
+                                 hipStream_t stream);
+int attention_head_dim();
+int attention_max_len();
+
 hipError_t launch_moe_combine(const uint16_t* y_perm, const int32_t* pos, const uint16_t* topk_w,
                               int64_t T, int top_k, int64_t N, uint16_t* out, hipStream_t stream);
 

@@ -229,6 +229,20 @@ int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act, int 
 int rq_moe_router_topk(const uint16_t* x, int64_t T, int64_t K, const uint16_t* w_gate, int64_t E,
                        int top_k, int32_t* topk_ids, uint16_t* topk_w, float* logits, void* stream);
 
+/* Short-context attention core between the QKV and O linears (page "FP8量化在生成式推荐系统
+ * OneRec-V2中的优化实践", §3.2: short serving contexts; the core stays FP16, page "Quantized
+ * Inference for OneRec-V2", section 关键证据, quantizes only the linears).
+ * qkv [requests * length][3 * hidden] FP16: each row is [q | k | v] (the merged QKV linear's
+ * output), hidden = heads * head_dim, head h owning columns [h * head_dim, (h + 1) * head_dim)
+ * of each part.  Requests are `length` consecutive rows; position i attends causally to
+ * positions j <= i of its own request:
+ *   s_ij = q_i . k_j / sqrt(head_dim) (FP16 products, FP32 accumulation),
+ *   p_ij = softmax_j(s_ij) in FP32,  out_i = fl16(sum_j fl16(p_ij) v_j), FP32 accumulation.
+ * out [requests * length][hidden] FP16 (the O linear's input).
+ * Limits: 1 <= length <= 32 and head_dim == 128 (RQ_ERR_SHAPE).  One kernel on `stream`. */
+int rq_attention_core(const uint16_t* qkv, int64_t requests, int length, int heads, int head_dim,
+                      uint16_t* out, void* stream);
+
 /* Kernel-level timing for benchmarks and profilers.  After this call, the next kernel
  * of the given kind that the calling thread enqueues (through any entry point above) is
  * bracketed by hipEventRecord(start_event) just before its launch and
@@ -236,7 +250,14 @@ int rq_moe_router_topk(const uint16_t* x, int64_t T, int64_t K, const uint16_t* 
  * then disarms itself.  start_event / stop_event are hipEvent_t handles owned by the
  * caller; passing NULL for both disarms the hook.  Each kind has its own one-shot slot.
  * Returns RQ_ERR_ARG for an unknown kind and RQ_ERR_NULL if only one event is NULL. */
-enum { RQ_KERNEL_QUANT = 0, RQ_KERNEL_GEMM = 1, RQ_KERNEL_COMBINE = 2, RQ_KERNEL_ROUTER = 3, RQ_KERNEL_KINDS = 4 };
+enum {
+  RQ_KERNEL_QUANT = 0,
+  RQ_KERNEL_GEMM = 1,
+  RQ_KERNEL_COMBINE = 2,
+  RQ_KERNEL_ROUTER = 3,
+  RQ_KERNEL_ATTENTION = 4,
+  RQ_KERNEL_KINDS = 5
+};
 int rq_time_next_kernel(int kernel, void* start_event, void* stop_event);
 
 /* Static description of a status code ("ok", "null pointer", ...). */
