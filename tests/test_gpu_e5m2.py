@@ -132,3 +132,22 @@ def test_unknown_activation_format_is_rejected():
     x = dev(np.zeros((4, 64), np.float16))
     with pytest.raises(rq.RqError):
         rq.linear(x, torch.zeros((16, 64), dtype=torch.uint8, device="cuda"), torch.ones(16, device="cuda"), afmt=7)
+
+
+@pytest.mark.parametrize("tile", [None, "256x256", "64x256"])
+def test_moe_e5m2_with_block_scales(monkeypatch, tile):
+    """Both variants at once: E5M2 token rows against 128x128-block-scaled E4M3 experts."""
+    rq = require_gpu()
+    case("e5m2 + block128 moe tile=%s" % tile)
+    if tile is not None:
+        monkeypatch.setenv("RQ_GEMM_TILE", tile)
+    t, k, f, e = 300, 256, 128, 6
+    d = workloads.make(4, t=t, k=k, f=f, e=e)
+    ids = d["ids"].astype(np.int32)
+    wq, ws = rq.quant_weights(dev(d["w_gu"]), wscale="block128")
+    y, dbg = rq.moe_grouped_linear(dev(d["x"]), dev(ids), wq, ws, "tokens", "none", "permuted", debug=True,
+                                   afmt="e5m2", wscale="block128")
+    xq, sx = quant.quantize_rows(d["x"], "e5m2")
+    ok, ratio = moe.grouped_linear_check(host(y), xq, sx, moe.IN_TOKENS, ids, host(wq), host(ws),
+                                         gran=wscale.BLOCK128, a_fmt="e5m2")
+    assert ok, ratio
