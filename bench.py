@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--rocprof-summary", default=None, metavar="PATH",
                     help="print per-(kernel, grid) dispatch statistics of a rocprofv3 output "
                          "(a *_results.db, a *_kernel_trace.csv, or a directory holding one) and exit")
+    ap.add_argument("--kernel-stats", default=None, metavar="PATH",
+                    help="print this library's kernels from a rocprofv3 --stats output (*_kernel_stats.csv, or a "
+                         "directory holding one): calls and average duration per kernel instantiation, and exit")
     ap.add_argument("--only", default=None,
                     help="comma list of attention,ffn,moe,layer_small_m to restrict the step (profiling)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0, metavar="MB",
@@ -388,6 +391,34 @@ def cpu_baseline(target_s=12.0):
                       "rows sized from 64- and 256-row passes to about %.0f s" % (rows, rows, target_s)}
 
 
+def cpu_router(tokens=16384):
+    """The oracle router on the router workload (16384 tokens), in GB/s of its algorithmic bytes."""
+    from oracle import router
+    rng = np.random.default_rng(1104)
+    x = (rng.standard_normal((tokens, 2048))).astype(np.float16)
+    w = (rng.standard_normal((32, 2048)) / np.sqrt(2048)).astype(np.float16)
+    t0 = time.perf_counter()
+    router.route(x, w, 2)
+    dt = time.perf_counter() - t0
+    by = tokens * 2048 * 2 + 32 * 2048 * 2 + tokens * 2 * 6
+    return {"value": round(by / dt / 1e9, 3), "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle", "seconds": round(dt, 3), "sample": "%d tokens x 2048, 32 experts, top-2" % tokens}
+
+
+def cpu_attention(requests=128):
+    """The oracle attention core on the attention workload (128 requests), in GB/s."""
+    from oracle import attention
+    rng = np.random.default_rng(2002)
+    x = rng.standard_normal((requests * 32, 3 * 2048)).astype(np.float16)
+    t0 = time.perf_counter()
+    attention.attention(x, requests, 32, 16)
+    dt = time.perf_counter() - t0
+    by = x.size * 2 + requests * 32 * 2048 * 2
+    return {"value": round(by / dt / 1e9, 3), "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "%d requests x 32 positions, 16 heads of 128" % requests}
+
+
 def _find(path, patterns):
     import glob
     if not os.path.isdir(path):
@@ -580,8 +611,32 @@ def stored_traffic(path=GEMM_TRAFFIC, sources=GEMM_SOURCES):
     return t.get("traffic_bytes_per_launch")
 
 
+def kernel_stats(path):
+    """Per-instantiation statistics of this library's kernels from rocprofv3 --stats."""
+    import csv
+    src = _find(path, ["*kernel_stats.csv"])
+    rows = []
+    with open(src) as f:
+        for r in csv.DictReader(f):
+            name = r["Name"]
+            if not any(k in name for k in OUR_KERNELS + ("router_topk", "attention_core", "quant_blocks", "tensor_")):
+                continue
+            short = name.replace("rq::(anonymous namespace)::", "").replace("void ", "")
+            short = short.split("(")[0] if "(" in short else short
+            rows.append((float(r["TotalDurationNs"]), int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
+                         float(r["MaxNs"]), short))
+    rows.sort(reverse=True)
+    print("# rocprofv3 kernel statistics: %s" % os.path.basename(src))
+    print("# %6s %10s %10s %10s  %s" % ("calls", "avg_us", "min_us", "max_us", "kernel"))
+    for total, calls, avg, mn, mx, name in rows:
+        print("  %6d %10.2f %10.2f %10.2f  %s" % (calls, avg / 1e3, mn / 1e3, mx / 1e3, name))
+
+
 def main():
     args = parse()
+    if args.kernel_stats:
+        kernel_stats(args.kernel_stats)
+        return
     if args.rocprof_summary:
         rocprof_summary(args.rocprof_summary, args.only, args.steps_in_profile)
         return
@@ -697,6 +752,9 @@ def main():
         del path
         torch.cuda.empty_cache()
         result["cpu_baseline"] = cpu_baseline()
+        for key, fn in (("router", cpu_router), ("attention_core", cpu_attention)):
+            if key in result:
+                result[key]["cpu_oracle"] = fn()
     print(json.dumps(result), flush=True)
 
 
