@@ -37,7 +37,9 @@
 // * Tile order: the hardware hands consecutive workgroup ids to the 8 XCDs in turn; each
 //   XCD's workgroups share a contiguous slice of the logical order, and the logical order
 //   walks groups of 8 M-tiles across all N-tiles, so tiles that share A rows or B columns
-//   run on the same XCD at the same time and hit its L2.
+//   run on the same XCD at the same time and hit its L2.  In grouped mode the groups never
+//   straddle two experts (an expert's M-tiles are cut into groups of at most 8), so the
+//   tiles running together read one expert's weights rather than two.
 // * Epilogue: each lane scales its four-column groups (FP32 row and column scales read from
 //   LDS) and rounds them to FP16; column groups are paired across the two 32-lane halves
 //   so each lane stores 16 bytes.
@@ -235,15 +237,28 @@ struct TileInfo {
   int expert;
 };
 
-// Logical tile L -> rows and columns: groups of kGroupM M-tiles walked column by column.
+// Logical tile L -> rows and columns: groups of kGroupM M-tiles walked column by column.  In
+// grouped mode expert e owns logical tiles [tile_start[e], tile_start[e + 1]) * n_tiles and
+// its M-tiles are grouped on their own.
 template <int BM, int BN, bool GROUPED>
 __device__ __forceinline__ TileInfo tile_info(const GemmArgs& p, int L, int m_tiles, int n_tiles) {
+  int base = 0;
+  if (GROUPED) {  // the expert whose M-tiles hold L: largest e with tile_start[e] * n_tiles <= L
+    int lo = 0, hi = p.E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (load_uniform(p.tile_start + mid) * n_tiles <= L) lo = mid; else hi = mid;
+    }
+    base = load_uniform(p.tile_start + lo);
+    m_tiles = load_uniform(p.tile_start + lo + 1) - base;
+    L -= base * n_tiles;
+  }
   const int per_group = kGroupM * n_tiles;
   const int group = L / per_group;
   const int first_m = group * kGroupM;
   const int gm = min(m_tiles - first_m, kGroupM);
   const int in_group = L - group * per_group;
-  const int mt = first_m + in_group % gm;
+  const int mt = base + first_m + in_group % gm;
   TileInfo t;
   t.n0 = (in_group / gm) * BN;
   if (GROUPED) {
