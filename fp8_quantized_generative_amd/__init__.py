@@ -13,6 +13,7 @@ PyTorch provides device memory and the current stream.
 * ``linear_workspace_size`` / ``moe_workspace_size``  scratch sizes for caller-held workspaces
 """
 
+import contextlib
 import ctypes
 
 import torch
@@ -20,7 +21,7 @@ import torch
 from . import _lib
 from ._lib import (RQ_ACT_GATE_SILU, RQ_ACT_NONE, RQ_ACT_SILU_MUL, RQ_MOE_IN_PERMUTED, RQ_MOE_IN_TOKENS,  # noqa: F401
                    RQ_MOE_OUT_COMBINED, RQ_MOE_OUT_PERMUTED, RQ_WSCALE_BLOCK128, RQ_WSCALE_CHANNEL,
-                   RQ_WSCALE_TENSOR, RQ_FP8_E4M3, RQ_FP8_E5M2, DebugOut, RqError)
+                   RQ_WSCALE_TENSOR, RQ_FP8_E4M3, RQ_FP8_E5M2, RQ_FLAG_EXPERT_ID, DebugOut, RqError)
 
 ACTS = {"none": RQ_ACT_NONE, "silu_mul": RQ_ACT_SILU_MUL, "gate_silu": RQ_ACT_GATE_SILU}
 IN_LAYOUTS = {"tokens": RQ_MOE_IN_TOKENS, "permuted": RQ_MOE_IN_PERMUTED}
@@ -71,6 +72,13 @@ def _stream(t, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Allocate on ``stream``: buffers this module allocates (outputs, workspaces, debug
+    outputs) then belong to that stream in PyTorch's caching allocator, so a buffer freed
+    while the stream's kernels still use it is only reused by later work on the same stream."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _workspace(nbytes, device, workspace):
     if workspace is not None:
         return workspace
@@ -88,10 +96,11 @@ def quant_weights(w, w_q=None, w_scale=None, stream=None, wscale="channel"):
         raise ValueError("w must be [N, K] or [B, N, K]")
     b, n, k = (1,) + tuple(w.shape) if w.dim() == 2 else tuple(w.shape)
     lead = tuple(w.shape[:-2])
-    if w_q is None:
-        w_q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
-    if w_scale is None:
-        w_scale = torch.empty(scale_shape(lead, n, k, g), dtype=torch.float32, device=w.device)
+    with _on(stream):
+        if w_q is None:
+            w_q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+        if w_scale is None:
+            w_scale = torch.empty(scale_shape(lead, n, k, g), dtype=torch.float32, device=w.device)
     _dev(w_q, torch.uint8, "w_q")
     _dev(w_scale, torch.float32, "w_scale")
     _shape(w_q, w.shape, "w_q")
@@ -145,14 +154,14 @@ def linear(x, w_q, w_scale, act="none", out=None, workspace=None, debug=False, s
     if x.shape[1] != (2 * k if a == RQ_ACT_SILU_MUL else k):
         raise ValueError("x width %d does not match K=%d for act=%r" % (x.shape[1], k, act))
     n_out = n // 2 if a == RQ_ACT_GATE_SILU else n
-    if out is None:
-        out = torch.empty((m, n_out), dtype=torch.float16, device=x.device)
+    lib = _lib.load()
+    with _on(stream):
+        if out is None:
+            out = torch.empty((m, n_out), dtype=torch.float16, device=x.device)
+        ws = _workspace(lib.rq_fp8_linear_workspace_size(m, k, a), x.device, workspace)
+        dbg, dbg_s = _debug(debug, m, m, k, a, x.device)
     _dev(out, torch.float16, "out")
     _shape(out, (m, n_out), "out")
-    lib = _lib.load()
-    ws_bytes = lib.rq_fp8_linear_workspace_size(m, k, a)
-    ws = _workspace(ws_bytes, x.device, workspace)
-    dbg, dbg_s = _debug(debug, m, m, k, a, x.device)
     _shape(w_scale, scale_shape((), n, k, g), "w_scale")
     st = lib.rq_fp8_linear_ex(_ptr(x), m, k, a, f, _ptr(w_q), _ptr(w_scale), g, n, _ptr(out), _ptr(ws),
                               ws.numel(), ctypes.byref(dbg_s) if dbg_s is not None else None,
@@ -191,15 +200,15 @@ def moe_grouped_linear(x, topk_ids, w_q, w_scale, in_layout="tokens", act="none"
     rows = t if il == RQ_MOE_IN_TOKENS else r
     if tuple(x.shape) != (rows, 2 * k if a == RQ_ACT_SILU_MUL else k):
         raise ValueError("x shape %r does not match the layout" % (tuple(x.shape),))
-    if out is None:
-        out = torch.empty((t if ol == RQ_MOE_OUT_COMBINED else r, n // 2 if a == RQ_ACT_GATE_SILU else n),
-                          dtype=torch.float16, device=x.device)
-    _dev(out, torch.float16, "out")
-    _shape(out, (t if ol == RQ_MOE_OUT_COMBINED else r, n // 2 if a == RQ_ACT_GATE_SILU else n), "out")
+    out_shape = (t if ol == RQ_MOE_OUT_COMBINED else r, n // 2 if a == RQ_ACT_GATE_SILU else n)
     lib = _lib.load()
-    ws_bytes = lib.rq_fp8_moe_workspace_size(t, top_k, e, n, k, il, a, ol)
-    ws = _workspace(ws_bytes, x.device, workspace)
-    dbg, dbg_s = _debug(debug, r, rows, k, a, x.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty(out_shape, dtype=torch.float16, device=x.device)
+        ws = _workspace(lib.rq_fp8_moe_workspace_size(t, top_k, e, n, k, il, a, ol), x.device, workspace)
+        dbg, dbg_s = _debug(debug, r, rows, k, a, x.device)
+    _dev(out, torch.float16, "out")
+    _shape(out, out_shape, "out")
     _shape(w_scale, scale_shape((e,), n, k, g), "w_scale")
     st = lib.rq_fp8_moe_grouped_linear_ex(
         _ptr(x), il, a, f, _ptr(topk_ids), _ptr(topk_w), t, top_k, _ptr(w_q), _ptr(w_scale), g, e, n, k,
@@ -219,15 +228,16 @@ def router_topk(x, w_gate, top_k=2, topk_ids=None, topk_w=None, logits=False, st
         raise ValueError("x [T, K] and w_gate [E, K] must share K")
     t, k = x.shape
     e = w_gate.shape[0]
-    if topk_ids is None:
-        topk_ids = torch.empty((t, top_k), dtype=torch.int32, device=x.device)
-    if topk_w is None:
-        topk_w = torch.empty((t, top_k), dtype=torch.float16, device=x.device)
+    with _on(stream):
+        if topk_ids is None:
+            topk_ids = torch.empty((t, top_k), dtype=torch.int32, device=x.device)
+        if topk_w is None:
+            topk_w = torch.empty((t, top_k), dtype=torch.float16, device=x.device)
+        lg = torch.empty((t, e), dtype=torch.float32, device=x.device) if logits else None
     _dev(topk_ids, torch.int32, "topk_ids")
     _dev(topk_w, torch.float16, "topk_w")
     _shape(topk_ids, (t, top_k), "topk_ids")
     _shape(topk_w, (t, top_k), "topk_w")
-    lg = torch.empty((t, e), dtype=torch.float32, device=x.device) if logits else None
     st = _lib.load().rq_moe_router_topk(_ptr(x), t, k, _ptr(w_gate), e, top_k, _ptr(topk_ids), _ptr(topk_w),
                                         _ptr(lg), _stream(x, stream))
     _lib.check("rq_moe_router_topk", st)
@@ -241,12 +251,23 @@ def attention_core(qkv, requests, length, heads, head_dim=128, out=None, stream=
     hidden = heads * head_dim
     _shape(qkv, (requests * length, 3 * hidden), "qkv")
     if out is None:
-        out = torch.empty((requests * length, hidden), dtype=torch.float16, device=qkv.device)
+        with _on(stream):
+            out = torch.empty((requests * length, hidden), dtype=torch.float16, device=qkv.device)
     _dev(out, torch.float16, "out")
     _shape(out, (requests * length, hidden), "out")
     st = _lib.load().rq_attention_core(_ptr(qkv), requests, length, heads, head_dim, _ptr(out), _stream(qkv, stream))
     _lib.check("rq_attention_core", st)
     return out
+
+
+def debug_flag(clear=False):
+    """The current device's error word (waits for all work on the device): bit
+    ``RQ_FLAG_EXPERT_ID`` is set once a routing id outside [0, E) reached
+    ``moe_grouped_linear``.  ``clear=True`` resets it."""
+    v = _lib.load().rq_debug_flag(1 if clear else 0)
+    if v < 0:
+        raise RqError("rq_debug_flag", _lib.RQ_ERR_HIP)
+    return v
 
 
 def interleave_gate_up(w_gu, block=32):

@@ -10,12 +10,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "librq_fp8.so")
 
 RQ_OK = 0
+RQ_ERR_HIP = 6
 RQ_ACT_NONE, RQ_ACT_SILU_MUL, RQ_ACT_GATE_SILU = 0, 1, 2
 RQ_MOE_IN_TOKENS, RQ_MOE_IN_PERMUTED = 0, 1
 RQ_MOE_OUT_PERMUTED, RQ_MOE_OUT_COMBINED = 0, 1
 RQ_KERNEL_QUANT, RQ_KERNEL_GEMM, RQ_KERNEL_COMBINE, RQ_KERNEL_ROUTER, RQ_KERNEL_ATTENTION = 0, 1, 2, 3, 4
 RQ_WSCALE_CHANNEL, RQ_WSCALE_TENSOR, RQ_WSCALE_BLOCK128 = 0, 1, 2
 RQ_FP8_E4M3, RQ_FP8_E5M2 = 0, 1
+RQ_FLAG_EXPERT_ID = 1
 
 # Every symbol the header declares, with (restype, argtypes).
 _P = ctypes.c_void_p
@@ -46,6 +48,7 @@ SIGNATURES = {
     "rq_time_next_kernel": (_I, [_I, _P, _P]),
     "rq_status_string": (ctypes.c_char_p, [_I]),
     "rq_device_supported": (_I, [_I]),
+    "rq_debug_flag": (_I, [_I]),
 }
 
 _lib = None

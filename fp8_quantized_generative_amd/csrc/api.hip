@@ -109,6 +109,12 @@ int rq_time_next_kernel(int kernel, void* start_event, void* stop_event) {
   return RQ_OK;
 }
 
+int rq_debug_flag(int clear) {
+  unsigned int flags = 0;
+  if (rq::read_error_flags(&flags, clear != 0) != hipSuccess) return -1;
+  return (int)(flags & 0x7FFFFFFFu);
+}
+
 int rq_device_supported(int device) {
   if (device < 0) return -1;
   if (device < kMaxDevices) {

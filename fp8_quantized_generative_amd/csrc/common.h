@@ -130,6 +130,12 @@ hipError_t launch_attention_core(const uint16_t* qkv, int64_t requests, int leng
 int attention_head_dim();
 int attention_max_len();
 
+// Bits of the device error word (the values of the C ABI's RQ_FLAG_*).
+enum : unsigned { kErrExpertId = 1u };
+
+// Wait for all work on the current device, then read (and optionally clear) its error word.
+hipError_t read_error_flags(unsigned int* flags, bool clear);
+
 hipError_t launch_moe_combine(const uint16_t* y_perm, const int32_t* pos, const uint16_t* topk_w,
                               int64_t T, int top_k, int64_t N, uint16_t* out, hipStream_t stream);
 

@@ -54,6 +54,7 @@
 // permuted output rows.  The device-side tile total bounds the walk, so the host never
 // needs the per-expert counts.
 
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 #include <type_traits>
@@ -697,22 +698,26 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
 }
 
 // Workgroups of this kernel the device keeps resident at once (all CUs), cached per device.
+// The cache is read and filled with atomic operations, so concurrent calls from several
+// host threads are safe: two threads may both compute the value, and both store the same one.
 template <class C, bool GROUPED, bool GATE, bool BLK, bool A5>
 int resident_workgroups() {
   constexpr int kDevices = 64;
-  static int cache[kDevices] = {};
+  static std::atomic<int> cache[kDevices];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
   const int slot = dev < kDevices ? dev : kDevices - 1;
-  if (cache[slot] > 0) return cache[slot];
+  const int known = cache[slot].load(std::memory_order_relaxed);
+  if (known > 0) return known;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_fp8_kernel<C, GROUPED, GATE, BLK, A5>, C::NT, 0) !=
           hipSuccess ||
       per_cu <= 0)
     per_cu = 1;
-  cache[slot] = cus * per_cu;
-  return cache[slot];
+  const int value = cus * per_cu;
+  if (dev < kDevices) cache[slot].store(value, std::memory_order_relaxed);  // devices past the table: no cache
+  return value;
 }
 
 // RQ_GEMM_GRID=n caps the number of persistent workgroups (tests use it to give small

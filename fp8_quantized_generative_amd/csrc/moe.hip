@@ -27,10 +27,22 @@ namespace {
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
 
-__device__ __forceinline__ int expert_of(const int32_t* ids, int64_t j, int E) {
+// Device error word of this GPU (each device holds its own copy): the routing-plan kernels
+// set kErrExpertId when an expert id lies outside [0, E).  Host code reads and clears it with
+// read_error_flags (rq_debug_flag in the C ABI).
+__device__ unsigned int g_error_flags;
+
+// The expert of slot j.  An id outside [0, E) breaks the caller's contract: it is reported
+// in the error word (report = true in the one kernel that reads every slot first) and mapped
+// into [0, E) so that every index the plan produces stays inside the workspace; the rows of
+// such slots are then meaningless, but no kernel reads or writes out of bounds.
+__device__ __forceinline__ int expert_of(const int32_t* ids, int64_t j, int E, bool report) {
   int e = ids[j];
-  e = e < 0 ? 0 : e;
-  return e >= E ? E - 1 : e;
+  if (e < 0 || e >= E) {
+    if (report) atomicOr(&g_error_flags, (unsigned)kErrExpertId);
+    e = e < 0 ? 0 : E - 1;
+  }
+  return e;
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_hist(const int32_t* __restrict__ ids, int64_t R, int E,
@@ -39,7 +51,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_hist(const int32_t* __restr
   for (int e = threadIdx.x; e < E; e += kPlanThreads) hist[e] = 0;
   __syncthreads();
   const int64_t j = (int64_t)blockIdx.x * kPlanThreads + threadIdx.x;
-  if (j < R) atomicAdd(&hist[expert_of(ids, j, E)], 1);
+  if (j < R) atomicAdd(&hist[expert_of(ids, j, E, true)], 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kPlanThreads) block_hist[(int64_t)blockIdx.x * E + e] = hist[e];
 }
@@ -161,7 +173,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_scatter(const int32_t* __re
   const int wave = threadIdx.x >> 6;
   const int64_t j = (int64_t)blockIdx.x * kPlanThreads + threadIdx.x;
   const bool valid = j < R;
-  const int e = valid ? expert_of(ids, j, E) : 0;
+  const int e = valid ? expert_of(ids, j, E, false) : 0;
   uint64_t peers = __ballot(valid);
   for (int b = 0; b < nbits; ++b) {
     const uint64_t m = __ballot(((e >> b) & 1) != 0);
@@ -239,6 +251,15 @@ hipError_t launch_moe_plan(const int32_t* ids, int64_t T, int top_k, int64_t E, 
   plan_scatter<<<dim3(nb), dim3(kPlanThreads), kPlanWaves * e * sizeof(int32_t), stream>>>(
       ids, R, e, nbits, block_hist, perm, pos);
   return hipGetLastError();
+}
+
+hipError_t read_error_flags(unsigned int* flags, bool clear) {
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return e;
+  e = hipMemcpyFromSymbol(flags, HIP_SYMBOL(g_error_flags), sizeof(unsigned int), 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess || !clear) return e;
+  const unsigned int zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_error_flags), &zero, sizeof(unsigned int), 0, hipMemcpyHostToDevice);
 }
 
 hipError_t launch_moe_combine(const uint16_t* y_perm, const int32_t* pos, const uint16_t* topk_w,

@@ -134,7 +134,10 @@ size_t rq_fp8_moe_workspace_size(int64_t T, int top_k, int64_t E, int64_t N, int
  * input here).
  *
  * Routing: slot j = t * top_k + k of token t goes to expert topk_ids[t][k] (int32,
- * must lie in [0, E); out-of-range ids are clamped into that range).  The canonical
+ * must lie in [0, E)).  The ids live on the device, so the host cannot check them: a
+ * routing-plan kernel sets RQ_FLAG_EXPERT_ID in the device error word (rq_debug_flag) for
+ * an id outside [0, E) and maps it into that range so that no kernel reads or writes out of
+ * bounds; the outputs of that call are then unspecified.  The canonical
  * permuted order sorts the R = T * top_k slots by (expert, j) ascending; expert e owns
  * permuted rows [offset_e, offset_e + count_e).
  *
@@ -259,6 +262,15 @@ enum {
   RQ_KERNEL_KINDS = 5
 };
 int rq_time_next_kernel(int kernel, void* start_event, void* stop_event);
+
+/* Device error word (one per GPU).  Bits: */
+enum { RQ_FLAG_EXPERT_ID = 1 /* a routing id outside [0, E) reached rq_fp8_moe_grouped_linear */ };
+
+/* Diagnostic read of the current device's error word: waits for all work on the device
+ * (hipDeviceSynchronize), returns the word (>= 0) and, if `clear` is non-zero, resets it to
+ * 0.  Returns -1 if a HIP call fails.  Not meant for the hot path: it blocks the host.
+ * The word accumulates over calls until it is cleared. */
+int rq_debug_flag(int clear);
 
 /* Static description of a status code ("ok", "null pointer", ...). */
 const char* rq_status_string(int status);

@@ -66,3 +66,9 @@ def test_algorithmic_bytes_of_the_largest_quantizer_call():
 def test_more_than_one_gpu_exits_with_a_message():
     p = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True)
     assert p.returncode == 2 and "one GPU" in p.stderr
+
+
+def test_stats_us_percentiles():
+    st = bench.stats_us([i / 1000.0 for i in range(1, 101)])  # 1..100 us given in ms
+    assert st["n"] == 100 and st["median"] == 50.5 and st["mean"] == 50.5
+    assert st["p10"] == pytest.approx(10.9) and st["p90"] == pytest.approx(90.1)

@@ -8,8 +8,8 @@ the debug outputs) must equal the oracle's bit for bit; FP16 outputs must lie wi
 of the oracle's exactly accumulated result (``oracle.linear.check``).  Small shapes span
 several 128-wide tiles with ragged M, N and K tails; the full-size workloads (dense 64 x
 512 x 512, attention QKV/O at 4096 tokens, the FFN at 4096 tokens) are checked on every
-quantized byte and on sampled output rows, in the same launch configuration the
-benchmark uses.
+quantized byte and every output row, in the launch configuration and (for the FFN) the
+gated formulation the benchmark times.
 """
 
 import numpy as np
@@ -18,6 +18,7 @@ import torch
 
 import workloads
 from oracle import ffn, linear, quant
+from tests import parity
 from tests.gpu_util import case, dev, host, require_gpu, ulp_diff16
 
 pytestmark = pytest.mark.gpu
@@ -100,39 +101,21 @@ def test_merged_qkv_equals_split():
     assert np.array_equal(merged, np.concatenate(parts, axis=1))
 
 
-def _sample(m, rng, count=48):
-    r = rng.choice(m, size=count, replace=False)
-    return np.sort(np.concatenate([r, [0, m - 1]]))
-
-
 @pytest.mark.slow
 def test_attention_full_size():
-    case("workload 2: attention 4096 tokens, QKV 6144 and O 2048")
+    rq = require_gpu()
     d = workloads.make(2)
-    rng = np.random.default_rng(2)
-    _check(d["x"], d["w_qkv"], sample_rows=_sample(4096, rng))
-    _check(d["attn_out"], d["w_o"], sample_rows=_sample(4096, rng))
+    parity.linear_all_rows(rq, d["x"], d["w_qkv"], "workload 2: QKV 4096 x 6144 x 2048, every row")
+    parity.linear_all_rows(rq, d["attn_out"], d["w_o"], "workload 2: O 4096 x 2048 x 2048, every row")
 
 
 @pytest.mark.slow
 def test_ffn_full_size_chain():
+    """The dense FFN at 4096 tokens as the benchmark runs it (gated gate/up, down over
+    K = 8192), every row, plus the unfused formulation bit for bit."""
     rq = require_gpu()
-    case("workload 3: FFN 4096 tokens, gate/up 16384, down 2048 over K = 8192")
     d = workloads.make(3)
-    rng = np.random.default_rng(3)
-    rows = _sample(4096, rng, 32)
-    _check(d["x"], d["w_gu"], sample_rows=rows)
-    # down projection over the GPU's own gate/up output
-    wgu_q, wgu_s = rq.quant_weights(dev(d["w_gu"]))
-    gu = rq.linear(dev(d["x"]), wgu_q, wgu_s)
-    wdn_q, wdn_s = rq.quant_weights(dev(d["w_dn"]))
-    y, dbg = rq.linear(gu, wdn_q, wdn_s, act="silu_mul", debug=True)
-    gu_h, h, aq, a_s, y = host(gu), host(dbg["h"]), host(dbg["a_q"]), host(dbg["a_scale"]), host(y)
-    assert ulp_diff16(h[rows], ffn.silu_mul(gu_h[rows], 8192)).max() <= 1
-    hq, hs = quant.quantize_rows(h)
-    assert np.array_equal(aq, hq) and np.array_equal(a_s.view(np.uint32), hs.view(np.uint32))
-    ok, ratio, _ = linear.check(y[rows], hq[rows], hs[rows], host(wdn_q), host(wdn_s))
-    assert ok, ratio
+    parity.dense_ffn_gated(rq, d["x"], d["w_gu"], d["w_dn"], "workload 3: FFN 4096 tokens, F = 8192")
 
 
 def test_determinism():

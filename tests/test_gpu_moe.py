@@ -5,7 +5,7 @@ permuted GEMM row is within the linear tolerance of the oracle evaluated on the 
 quantized operand; the SiLU rows are within 1 FP16 ulp; the combined output is within 1
 FP16 ulp of the oracle's combine of the GPU's permuted rows.  Ragged expert loads include
 empty experts; the full-size Zipf workload (16384 tokens, top-2 of 32 experts) is checked
-on sampled rows.
+on every row, in the gated formulation the benchmark times.
 """
 
 import numpy as np
@@ -14,6 +14,7 @@ import torch
 
 import workloads
 from oracle import ffn, linear, moe, quant
+from tests import parity
 from tests.gpu_util import case, dev, host, require_gpu, ulp_diff16
 
 pytestmark = pytest.mark.gpu
@@ -120,15 +121,14 @@ def test_moe_determinism():
 
 
 @pytest.mark.slow
-def test_moe_full_size_sampled():
-    case("workload 4: MoE 16384 tokens, top-2 of 32, F = 4096")
+def test_moe_full_size_every_row():
+    """16384 tokens, top-2 of 32 Zipf-loaded experts, F = 4096, as the benchmark runs it
+    (gated gate/up, down with the combine), every permuted row checked expert by expert."""
+    rq = require_gpu()
     d = workloads.make(4)
-    rng = np.random.default_rng(4)
-    counts, offsets, _, _ = moe.plan(d["ids"], 32)
-    sample = [int(offsets[ex]) for ex in range(32) if counts[ex] > 0]          # first row of each expert
-    sample += [int(offsets[ex + 1]) - 1 for ex in range(32) if counts[ex] > 0]  # last row of each expert
-    sample += list(rng.choice(32768, size=64, replace=False))
-    _expert_ffn(d, 16384, 2048, 4096, 32, 2, sample=np.unique(np.array(sample)))
+    counts, r_gu, r_dn = parity.moe_ffn_gated(rq, d["x"], d["ids"], d["topk_w"], d["w_gu"], d["w_dn"],
+                                              "workload 4: MoE 16384 tokens, top-2 of 32, F = 4096")
+    assert (counts == 0).any()
 
 
 @pytest.mark.parametrize("grid", [None, "5", "16"])

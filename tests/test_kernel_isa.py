@@ -2,7 +2,8 @@
 
 The direct-to-LDS loads are inline asm that writes m0 (listed as clobbered).  That is only safe
 while no compiler-generated instruction in the translation unit relies on m0; this test
-compiles gemm.hip and checks that every m0 reference sits inside one of those asm blocks.
+compiles gemm.hip with exactly the flags the shipped library is built with (``build.FLAGS``)
+and checks that every m0 reference sits inside one of those asm blocks.
 """
 
 import os
@@ -11,6 +12,8 @@ import subprocess
 
 import pytest
 
+from fp8_quantized_generative_amd import build as lib_build
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "fp8_quantized_generative_amd", "csrc")
 
@@ -18,8 +21,7 @@ CSRC = os.path.join(ROOT, "fp8_quantized_generative_amd", "csrc")
 @pytest.mark.skipif(shutil.which("hipcc") is None, reason="hipcc not available")
 def test_gemm_m0_only_in_lds_dma_asm(tmp_path):
     asm = str(tmp_path / "gemm.s")
-    subprocess.check_call(["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
-                           "-Wno-inline-asm", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    subprocess.check_call([lib_build.HIPCC, *lib_build.FLAGS, "-Wno-inline-asm",
                            "-S", "--cuda-device-only", "-o", asm, os.path.join(CSRC, "gemm.hip")],
                           stderr=subprocess.DEVNULL)
     inside = outside = 0
