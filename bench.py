@@ -63,6 +63,10 @@ def parse():
     ap.add_argument("--traffic-summary", nargs=3, default=None, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of a bench command with "
                          "--calibrate-copy-mb, write the dominant kernel's HBM traffic per launch to OUT (json)")
+    ap.add_argument("--pmc-summary", default=None, metavar="PATH",
+                    help="print FP8 MFMA counts, MFMA busy fraction and clock per GEMM call from a rocprofv3 "
+                         "--pmc database (SQ_INSTS_VALU_MFMA_MOPS_F8 SQ_INSTS_VALU_MFMA_F8 SQ_VALU_MFMA_BUSY_CYCLES "
+                         "SQ_INSTS_VALU GRBM_GUI_ACTIVE) and exit")
     ap.add_argument("--steps-in-profile", type=int, default=None,
                     help="with --rocprof-summary / --traffic-summary: steps (warmup + timed) the profiled "
                          "command ran")
@@ -112,7 +116,7 @@ class Flush:
         self.mib = mib
 
     def __call__(self):
-        self.torch.sum(self.buf, dtype=self.torch.float32, out=self.out)
+        self.torch.sum(self.buf, dim=0, out=self.out)
 
 
 class Hip:
@@ -575,6 +579,64 @@ def _pmc_rows(path, counter):
     return [per[d] for d in sorted(per)]
 
 
+def _pmc_db(path):
+    """{dispatch_id: (kernel name, duration ns, {counter: value summed over instances})} from a
+    rocprofv3 --pmc database."""
+    import sqlite3
+    path = _find(path, ["*_results.db"])
+    db = sqlite3.connect(path)
+    per = {}
+    q = ("select dispatch_id, kernel_name, max(duration), counter_name, sum(value) from counters_collection "
+         "group by dispatch_id, counter_name")
+    for d, name, dur, cn, v in db.execute(q):
+        e = per.setdefault(int(d), [name, int(dur), {}])
+        e[2][cn] = float(v)
+    return path, per
+
+
+XCDS, SIMDS = 8, 1024  # MI355X: GRBM_GUI_ACTIVE is summed over the 8 XCDs; 256 CUs x 4 SIMDs
+
+
+def pmc_summary(path, only=None, steps=None):
+    """Per call of the step: FP8 MFMA instructions and flops executed (against the algorithmic
+    flops), the MFMA pipe's busy fraction and the engine clock, from a --pmc run with
+    SQ_INSTS_VALU_MFMA_MOPS_F8, SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE."""
+    import workloads
+    src, per = _pmc_db(path)
+    ids = sorted(per)
+    names = [per[d][0] for d in ids]
+    aligned, nsteps = _align_steps(names, only, steps)
+    flops = {}
+    for wl, label, shapes in (("attention", ("qkv", "o"), workloads.gemm_shapes(2)),
+                              ("ffn", ("gate_up", "down"), workloads.gemm_shapes(3)),
+                              ("moe", ("gate_up", "down"), workloads.gemm_shapes(4)),
+                              ("layer_small_m", ("qkv", "o", "gate_up", "down", "moe_gate_up", "moe_down"),
+                               workloads.gemm_shapes(5))):
+        for lb, (m, n, k) in zip(label, shapes):
+            flops["%s %s" % (wl, lb)] = 2 * m * n * k
+    groups = {}
+    for idx, label, kind in aligned:
+        if kind == "gemm":
+            groups.setdefault(label, []).append(per[ids[idx]])
+    print("# rocprofv3 --pmc: %s (%d steps matched)" % (os.path.basename(src), nsteps))
+    print("# %-26s %8s %9s %10s %8s %7s %9s %7s %8s" % (
+        "call", "avg_us", "clock_GHz", "mfma_f8", "exec/alg", "busy", "TFLOP/s", "frac5P", "valu/mfma"))
+    for label, recs in groups.items():
+        dur = np.mean([r[1] for r in recs])
+        c = {k: np.mean([r[2].get(k, np.nan) for r in recs]) for k in recs[0][2]}
+        ghz = c.get("GRBM_GUI_ACTIVE", np.nan) / XCDS / dur
+        executed = c.get("SQ_INSTS_VALU_MFMA_MOPS_F8", np.nan) * 512
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", np.nan) / (SIMDS * c.get("GRBM_GUI_ACTIVE", np.nan) / XCDS)
+        alg = flops.get(label, np.nan)
+        valu = (c.get("SQ_INSTS_VALU", np.nan) - c.get("SQ_INSTS_VALU_MFMA_F8", 0)) / c.get("SQ_INSTS_VALU_MFMA_F8", np.nan)
+        print("  %-26s %8.1f %9.3f %10.0f %8.3f %7.3f %9.1f %7.3f %8.2f" % (
+            label, dur / 1e3, ghz, c.get("SQ_INSTS_VALU_MFMA_F8", np.nan), executed / alg, busy,
+            alg / dur / 1e3, alg / dur / 1e3 / FP8_PEAK_TFLOPS, valu))
+    print("# clock = GRBM_GUI_ACTIVE / %d XCDs / duration; exec/alg = MOPS_F8 * 512 / (2 M N K over real rows); "
+          "busy = SQ_VALU_MFMA_BUSY_CYCLES / (%d SIMDs * GRBM_GUI_ACTIVE / %d); valu/mfma = non-MFMA VALU "
+          "instructions per FP8 MFMA" % (XCDS, SIMDS, XCDS))
+
+
 def source_hash(files):
     """Hash of a kernel's sources: stored traffic counters are valid only for this code."""
     import hashlib
@@ -696,6 +758,9 @@ def main():
     if args.rocprof_summary:
         rocprof_summary(args.rocprof_summary, args.only, args.steps_in_profile)
         return
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary, args.only, args.steps_in_profile)
+        return
     if args.traffic_summary:
         fetch_dir, write_dir, out = args.traffic_summary
         gemm, qnt = traffic_summary(fetch_dir, write_dir, out, args.only, args.steps_in_profile)
@@ -809,14 +874,15 @@ def main():
                                                  "before each of %d repetitions; GB/s from the median" % reps,
                                        "instances": targets}
     # the small dense linear (quantizer + GEMM) and the small-M layer as a whole, flushed
-    fl1, fn1 = path.c1
-    c1_call = stats_us(timer.sequence([fn1], reps))
-    result["dense_small"] = {"workload": "64 x 512 x 512 dense linear (quantizer + GEMM)", "call_us": c1_call,
-                             "gemm_us": stats_us(timer.kernel(fn1, _lib.RQ_KERNEL_GEMM, reps)),
-                             "quant_us": stats_us(timer.kernel(fn1, _lib.RQ_KERNEL_QUANT, reps)),
-                             "timing": "flushed before each repetition; launch-latency bound"}
     layer = [c for c in path.calls if c[0] == "layer_small_m"]
-    if layer:
+    if not args.no_kernels:
+        fl1, fn1 = path.c1
+        c1_call = stats_us(timer.sequence([fn1], reps))
+        result["dense_small"] = {"workload": "64 x 512 x 512 dense linear (quantizer + GEMM)", "call_us": c1_call,
+                                 "gemm_us": stats_us(timer.kernel(fn1, _lib.RQ_KERNEL_GEMM, reps)),
+                                 "quant_us": stats_us(timer.kernel(fn1, _lib.RQ_KERNEL_QUANT, reps)),
+                                 "timing": "flushed before each repetition; launch-latency bound"}
+    if layer and not args.no_kernels:
         lay = stats_us(timer.sequence([c[5] for c in layer], reps))
         lay_bytes = sum(c[4] for c in layer)
         result["layer_small_m"] = {
