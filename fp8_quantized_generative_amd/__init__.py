@@ -7,6 +7,7 @@ PyTorch provides device memory and the current stream.
 * ``quant_weights(w, wscale=...)``            offline E4M3 weight quantization (scales per
                                                output channel, per tensor or per 128x128 block)
 * ``linear(x, w_q, w_scale, act=...)``         per-token quantization + FP8 GEMM + FP16 epilogue
+* ``linear_noalloc(x, w_q, w_scale, out)``     the same without allocating (static device scratch)
 * ``moe_grouped_linear(x, ids, w_q, w_scale, ...)``  routing plan + grouped GEMM (+ combine)
 * ``attention_core(qkv, requests, length, heads)``  FP16 causal short-context attention (QKV -> O input)
 * ``router_topk(x, w_gate, top_k)``            FP16 MoE gate logits -> top-k expert ids and weights
@@ -168,6 +169,30 @@ def linear(x, w_q, w_scale, act="none", out=None, workspace=None, debug=False, s
                               _stream(x, stream))
     _lib.check("rq_fp8_linear_ex", st)
     return (out, dbg) if debug else out
+
+
+def linear_noalloc(x, w_q, w_scale, out, act="none", stream=None):
+    """``linear`` without any allocation: the caller passes ``out`` (FP16 [M, N], or
+    [M, N/2] for ``act='gate_silu'``) and the quantized activations live in the library's
+    static device buffer (``RQ_STATIC_SCRATCH_BYTES`` per GPU; calls that overlap on one GPU
+    race on it).  E4M3 activations, per-channel weight scales."""
+    a = _code(ACTS, act, "act")
+    _dev(x, torch.float16, "x")
+    _dev(w_q, torch.uint8, "w_q")
+    _dev(w_scale, torch.float32, "w_scale")
+    _dev(out, torch.float16, "out")
+    if x.dim() != 2 or w_q.dim() != 2:
+        raise ValueError("x and w_q must be 2-D")
+    m = x.shape[0]
+    n, k = w_q.shape
+    if x.shape[1] != (2 * k if a == RQ_ACT_SILU_MUL else k):
+        raise ValueError("x width %d does not match K=%d for act=%r" % (x.shape[1], k, act))
+    _shape(out, (m, n // 2 if a == RQ_ACT_GATE_SILU else n), "out")
+    _shape(w_scale, (n,), "w_scale")
+    st = _lib.load().rq_fp8_linear_noalloc(_ptr(x), m, k, a, _ptr(w_q), _ptr(w_scale), n, _ptr(out),
+                                           _stream(x, stream))
+    _lib.check("rq_fp8_linear_noalloc", st)
+    return out
 
 
 def moe_grouped_linear(x, topk_ids, w_q, w_scale, in_layout="tokens", act="none",

@@ -18,6 +18,8 @@ RQ_KERNEL_QUANT, RQ_KERNEL_GEMM, RQ_KERNEL_COMBINE, RQ_KERNEL_ROUTER, RQ_KERNEL_
 RQ_WSCALE_CHANNEL, RQ_WSCALE_TENSOR, RQ_WSCALE_BLOCK128 = 0, 1, 2
 RQ_FP8_E4M3, RQ_FP8_E5M2 = 0, 1
 RQ_FLAG_EXPERT_ID = 1
+RQ_ERR_SCRATCH = 8
+RQ_STATIC_SCRATCH_BYTES = 40 << 20
 
 # Every symbol the header declares, with (restype, argtypes).
 _P = ctypes.c_void_p
@@ -49,6 +51,7 @@ SIGNATURES = {
     "rq_status_string": (ctypes.c_char_p, [_I]),
     "rq_device_supported": (_I, [_I]),
     "rq_debug_flag": (_I, [_I]),
+    "rq_fp8_linear_noalloc": (_I, [_P, _I64, _I64, _I, _P, _P, _I64, _P, _P]),
 }
 
 _lib = None

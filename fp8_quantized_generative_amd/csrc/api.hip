@@ -3,6 +3,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "rq_fp8.h"
 #include "common.h"
@@ -83,6 +84,39 @@ MoeLayout moe_layout(int64_t T, int top_k, int64_t E, int64_t N, int64_t K, int 
   return l;
 }
 
+// Device scratch of the allocation-free linear (rq_fp8_linear_noalloc): the quantized
+// activation rows and their scales.  Each GPU the library runs on holds its own copy, for the
+// life of the process.  In host code `scratch` is only a host-side stand-in for the symbol:
+// its device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[RQ_STATIC_SCRATCH_BYTES];
+
+// Per-device address of `scratch` (resolved on a call's first use of a device, with that
+// device current).  g_scratch_state: 0 not resolved, 1 resolved, 2 failed.
+std::mutex g_scratch_mutex;
+std::atomic<int> g_scratch_state[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+
+int static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return RQ_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return RQ_ERR_UNSUPPORTED;
+  int state = g_scratch_state[dev].load(std::memory_order_acquire);
+  if (state == 0) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    state = g_scratch_state[dev].load(std::memory_order_relaxed);
+    if (state == 0) {
+      void* ptr = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      g_scratch_ptr[dev] = ptr;
+      state = (e == hipSuccess && ptr != nullptr) ? 1 : 2;
+      g_scratch_state[dev].store(state, std::memory_order_release);
+    }
+  }
+  if (state != 1) return RQ_ERR_HIP;
+  *out = g_scratch_ptr[dev];
+  return RQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -97,6 +131,7 @@ const char* rq_status_string(int status) {
     case RQ_ERR_UNSUPPORTED: return "device is not gfx950";
     case RQ_ERR_HIP: return "HIP runtime error";
     case RQ_ERR_ARG: return "invalid argument";
+    case RQ_ERR_SCRATCH: return "request exceeds the static scratch buffer";
     default: return "unknown status";
   }
 }
@@ -224,6 +259,21 @@ int rq_fp8_linear(const uint16_t* x, int64_t M, int64_t K, int act, const uint8_
                   size_t workspace_bytes, const rq_debug_out* dbg, void* stream) {
   return rq_fp8_linear_ex(x, M, K, act, RQ_FP8_E4M3, w_q, w_scale, RQ_WSCALE_CHANNEL, N, y, workspace,
                           workspace_bytes, dbg, stream);
+}
+
+int rq_fp8_linear_noalloc(const uint16_t* x, int64_t M, int64_t K, int act, const uint8_t* w_q,
+                          const float* w_scale, int64_t N, uint16_t* y, void* stream) {
+  if (M < 0 || K <= 0 || N <= 0) return RQ_ERR_SHAPE;
+  if (M == 0)  // validates the remaining arguments and enqueues nothing
+    return rq_fp8_linear_ex(x, M, K, act, RQ_FP8_E4M3, w_q, w_scale, RQ_WSCALE_CHANNEL, N, y, nullptr, 0,
+                            nullptr, stream);
+  if (K > kMaxK || M > (int64_t)1 << 31) return RQ_ERR_SHAPE;
+  if (rq_fp8_linear_workspace_size(M, K, act) > (size_t)RQ_STATIC_SCRATCH_BYTES) return RQ_ERR_SCRATCH;
+  void* ptr = nullptr;
+  const int st = static_scratch(&ptr);
+  if (st != RQ_OK) return st;
+  return rq_fp8_linear_ex(x, M, K, act, RQ_FP8_E4M3, w_q, w_scale, RQ_WSCALE_CHANNEL, N, y, ptr,
+                          (size_t)RQ_STATIC_SCRATCH_BYTES, nullptr, stream);
 }
 
 size_t rq_fp8_moe_workspace_size(int64_t T, int top_k, int64_t E, int64_t N, int64_t K,

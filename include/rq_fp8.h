@@ -60,7 +60,8 @@ typedef enum {
   RQ_ERR_WORKSPACE = 4,   /* workspace smaller than the *_workspace_size result */
   RQ_ERR_UNSUPPORTED = 5, /* the current device is not gfx950 */
   RQ_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed */
-  RQ_ERR_ARG = 7          /* an unknown act / layout / a_fmt / w_gran value, or a missing topk_w */
+  RQ_ERR_ARG = 7,         /* an unknown act / layout / a_fmt / w_gran value, or a missing topk_w */
+  RQ_ERR_SCRATCH = 8      /* rq_fp8_linear_noalloc: the call needs more than RQ_STATIC_SCRATCH_BYTES */
 } rq_status;
 
 /* Activation applied to the FP16 input rows before they are quantized.
@@ -124,7 +125,30 @@ int rq_fp8_linear(const uint16_t* x, int64_t M, int64_t K, int act,
                   uint16_t* y, void* workspace, size_t workspace_bytes,
                   const rq_debug_out* dbg, void* stream);
 
-/* Bytes of workspace rq_fp8_moe_grouped_linear needs.  E <= 1024, 1 <= top_k <= E. */
+/* rq_fp8_linear for callers that cannot allocate memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same operation with act
+ * RQ_ACT_NONE, RQ_ACT_SILU_MUL or RQ_ACT_GATE_SILU, E4M3 activations and per-channel weight
+ * scales, and the same kernels, but the quantized activation rows and scales live in a
+ * static device buffer of RQ_STATIC_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on until the process ends, so the call itself calls no allocator.  The caller still
+ * owns x, w_q, w_scale and y.
+ * Limit: rq_fp8_linear_workspace_size(M, K, act) <= RQ_STATIC_SCRATCH_BYTES (for example
+ * M = 4096 rows of K = 8192), else RQ_ERR_SCRATCH before anything is enqueued.
+ * Every call on one GPU shares that GPU's buffer, which keeps the last call's contents (the
+ * quantizer rewrites every byte the GEMM then reads, so nothing needs clearing): calls that
+ * overlap on one GPU (concurrent streams, or host threads) race on it and must be ordered
+ * by the caller.  The buffer's device address is resolved on the first call on each
+ * device. */
+#define RQ_STATIC_SCRATCH_BYTES (40u << 20)
+int rq_fp8_linear_noalloc(const uint16_t* x, int64_t M, int64_t K, int act,
+                          const uint8_t* w_q, const float* w_scale, int64_t N,
+                          uint16_t* y, void* stream);
+
+/* Bytes of workspace rq_fp8_moe_grouped_linear needs.  E <= 1024, 1 <= top_k <= E.
+ * Besides the row counts and widths (T, top_k, E, K) and the input layout and activation,
+ * it takes N and out_layout: with RQ_MOE_OUT_COMBINED the permuted GEMM output
+ * [T * top_k][N (N / 2 for RQ_ACT_GATE_SILU)] FP16 also lives in the workspace until the
+ * combine has read it. */
 size_t rq_fp8_moe_workspace_size(int64_t T, int top_k, int64_t E, int64_t N, int64_t K,
                                  int in_layout, int act, int out_layout);
 

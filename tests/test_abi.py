@@ -151,3 +151,21 @@ def test_quant_weights_rejects(kw, code):
 def test_quant_weights_zero_rows_is_noop():
     lib = lib_mod.load()
     assert lib.rq_fp8_quant_weights(None, 0, 64, 64, None, None, None) == 0
+
+
+def test_noalloc_validates_on_the_host():
+    """rq_fp8_linear_noalloc rejects bad shapes and requests beyond its static buffer before
+    any device query (no GPU here)."""
+    lib = lib_mod.load()
+    k = 8192
+    m = lib_mod.RQ_STATIC_SCRATCH_BYTES // k
+    call = lambda m_, k_, n_, act=0: lib.rq_fp8_linear_noalloc(FAKE, m_, k_, act, FAKE, FAKE, n_, FAKE, None)  # noqa: E731
+    assert call(m, k, 16) == lib_mod.RQ_ERR_SCRATCH
+    assert call(1 << 20, 2048, 16) == lib_mod.RQ_ERR_SCRATCH
+    assert call(-1, 64, 16) == RQ_ERR_SHAPE
+    assert call(4, 0, 16) == RQ_ERR_SHAPE
+    assert call(4, 64, 0) == RQ_ERR_SHAPE
+    assert call(0, 64, 16) == 0            # zero rows: a validated no-op
+    assert call(0, 24, 16) == RQ_ERR_ALIGN
+    assert call(0, 64, 16, act=9) == RQ_ERR_ARG
+    assert lib.rq_status_string(lib_mod.RQ_ERR_SCRATCH) == b"request exceeds the static scratch buffer"
