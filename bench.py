@@ -74,8 +74,8 @@ def parse():
 
 
 # Calls of one step, in launch order: (workload, call, kind).  "linear" launches the row
-# quantizer and the GEMM; "moe" the three routing-plan kernels, the quantizer and the
-# grouped GEMM; "moe_combined" also the weighted combine.
+# quantizer and the GEMM; "moe" the routing-plan kernel (one workgroup at these sizes), the
+# quantizer and the grouped GEMM; "moe_combined" also the weighted combine.
 STEP = [
     ("attention", "qkv", "linear"), ("attention", "o", "linear"),
     ("ffn", "gate_up", "linear"), ("ffn", "down", "linear"),
@@ -85,9 +85,10 @@ STEP = [
     ("layer_small_m", "moe_gate_up", "moe"), ("layer_small_m", "moe_down", "moe_combined"),
 ]
 DOMINANT = ("moe", "gate_up")
-KERNELS = {"linear": ["quant", "gemm"], "moe": ["plan_hist", "plan_scan", "plan_scatter", "quant", "gemm"],
-           "moe_combined": ["plan_hist", "plan_scan", "plan_scatter", "quant", "gemm", "combine"]}
-OUR_KERNELS = ("quant_rows", "gemm_fp8_kernel", "plan_hist", "plan_scan", "plan_scatter", "combine_kernel")
+KERNELS = {"linear": ["quant", "gemm"], "moe": ["plan", "quant", "gemm"],
+           "moe_combined": ["plan", "quant", "gemm", "combine"]}
+OUR_KERNELS = ("quant_rows", "gemm_fp8_kernel", "plan_single", "plan_hist", "plan_scan", "plan_scatter",
+               "combine_kernel")
 
 
 def step_dispatches(only):
@@ -170,7 +171,7 @@ class Path:
             m = x.shape[0]
             n, k = wq.shape
             out = torch.empty((m, n // 2 if act == "gate_silu" else n), dtype=torch.float16, device="cuda")
-            ws_t = torch.empty(max(rq.linear_workspace_size(m, k, act), 1), dtype=torch.uint8, device="cuda")
+            ws_t = torch.empty(max(rq.linear_workspace_size(m, k, act, n=n), 1), dtype=torch.uint8, device="cuda")
             fl = 2 * m * n * k
             # bytes that must cross HBM at least once: activations in, weights, output
             by = x.numel() * 2 + wq.numel() + out.numel() * 2
@@ -207,7 +208,7 @@ class Path:
         w1 = qw(d1["w"])
         x1 = dev(d1["x"])
         y1 = torch.empty((64, 512), dtype=torch.float16, device="cuda")
-        ws1 = torch.empty(rq.linear_workspace_size(64, 512), dtype=torch.uint8, device="cuda")
+        ws1 = torch.empty(rq.linear_workspace_size(64, 512, n=512), dtype=torch.uint8, device="cuda")
         self.c1 = (2 * 64 * 512 * 512, lambda: rq.linear(x1, *w1, out=y1, workspace=ws1))
         self.config = {}
         if "attention" in want:
@@ -511,8 +512,7 @@ def _rocprof_rows(path):
     return path, [r[1:] for r in rows]
 
 
-_KIND_TOKEN = {"quant": "quant_rows", "gemm": "gemm_fp8_kernel", "plan_hist": "plan_hist",
-               "plan_scan": "plan_scan", "plan_scatter": "plan_scatter", "combine": "combine_kernel"}
+_KIND_TOKEN = {"quant": "quant_rows", "gemm": "gemm_fp8_kernel", "plan": "plan_single", "combine": "combine_kernel"}
 
 
 def _align_steps(names, only, steps):

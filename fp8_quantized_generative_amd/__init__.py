@@ -111,8 +111,13 @@ def quant_weights(w, w_q=None, w_scale=None, stream=None, wscale="channel"):
     return w_q, w_scale
 
 
-def linear_workspace_size(m, k, act="none"):
-    return int(_lib.load().rq_fp8_linear_workspace_size(m, k, _code(ACTS, act, "act")))
+def linear_workspace_size(m, k, act="none", n=None):
+    """Workspace bytes of ``linear``; with ``n`` given, the size that also lets the call split
+    K (small M, see ``rq_fp8_linear_workspace_size_ex``)."""
+    a = _code(ACTS, act, "act")
+    if n is None:
+        return int(_lib.load().rq_fp8_linear_workspace_size(m, k, a))
+    return int(_lib.load().rq_fp8_linear_workspace_size_ex(m, n, k, a))
 
 
 def moe_workspace_size(t, top_k, e, n, k, in_layout="tokens", act="none", out_layout="permuted"):
@@ -159,7 +164,7 @@ def linear(x, w_q, w_scale, act="none", out=None, workspace=None, debug=False, s
     with _on(stream):
         if out is None:
             out = torch.empty((m, n_out), dtype=torch.float16, device=x.device)
-        ws = _workspace(lib.rq_fp8_linear_workspace_size(m, k, a), x.device, workspace)
+        ws = _workspace(lib.rq_fp8_linear_workspace_size_ex(m, n, k, a), x.device, workspace)
         dbg, dbg_s = _debug(debug, m, m, k, a, x.device)
     _dev(out, torch.float16, "out")
     _shape(out, (m, n_out), "out")

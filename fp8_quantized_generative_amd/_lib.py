@@ -36,6 +36,7 @@ class DebugOut(ctypes.Structure):
 SIGNATURES = {
     "rq_fp8_quant_weights": (_I, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "rq_fp8_linear_workspace_size": (_SZ, [_I64, _I64, _I]),
+    "rq_fp8_linear_workspace_size_ex": (_SZ, [_I64, _I64, _I64, _I]),
     "rq_fp8_linear": (_I, [_P, _I64, _I64, _I, _P, _P, _I64, _P, _P, _SZ, ctypes.POINTER(DebugOut), _P]),
     "rq_fp8_moe_workspace_size": (_SZ, [_I64, _I, _I64, _I64, _I64, _I, _I, _I]),
     "rq_fp8_moe_grouped_linear": (_I, [_P, _I, _I, _P, _P, _I64, _I, _P, _P, _I64, _I64, _I64,

@@ -198,6 +198,11 @@ size_t rq_fp8_linear_workspace_size(int64_t M, int64_t K, int act) {
   return align_up((size_t)(M * K)) + align_up((size_t)M * sizeof(float));
 }
 
+size_t rq_fp8_linear_workspace_size_ex(int64_t M, int64_t N, int64_t K, int act) {
+  if (M < 0 || K <= 0 || N <= 0) return 0;
+  return rq_fp8_linear_workspace_size(M, K, act) + align_up(rq::dense_partial_bytes(M, N, K, act, RQ_WSCALE_CHANNEL));
+}
+
 int rq_fp8_linear_ex(const uint16_t* x, int64_t M, int64_t K, int act, int a_fmt, const uint8_t* w_q,
                      const float* w_scale, int w_gran, int64_t N, uint16_t* y, void* workspace,
                      size_t workspace_bytes, const rq_debug_out* dbg, void* stream) {
@@ -228,6 +233,11 @@ int rq_fp8_linear_ex(const uint16_t* x, int64_t M, int64_t K, int act, int a_fmt
   Carve c{reinterpret_cast<uint8_t*>(workspace)};
   uint8_t* xq = dq ? dq : c.take<uint8_t>((size_t)(M * K));
   float* sx = ds ? ds : c.take<float>((size_t)M * sizeof(float));
+  // split-K partial sums when the workspace holds them (see rq_fp8_linear_workspace_size_ex)
+  const size_t part_bytes = rq::dense_partial_bytes(M, N, K, act, w_gran);
+  float* partial = nullptr;
+  if (part_bytes > 0 && workspace != nullptr && workspace_bytes >= c.used + part_bytes)
+    partial = c.take<float>(part_bytes);
   hipStream_t s = (hipStream_t)stream;
   {
     Hook hook(RQ_KERNEL_QUANT, s);
@@ -250,6 +260,8 @@ int rq_fp8_linear_ex(const uint16_t* x, int64_t M, int64_t K, int act, int a_fmt
   g.gate = act == RQ_ACT_GATE_SILU ? 1 : 0;
   g.b_gran = w_gran;
   g.a_fmt = a_fmt;
+  g.splits = partial != nullptr ? rq::dense_splits(M, N, K, act, w_gran) : 1;
+  g.partial = partial;
   Hook hook(RQ_KERNEL_GEMM, s);
   return rq::launch_gemm_dense(g, s) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
@@ -357,6 +369,7 @@ int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act, int 
   g.a_rows = (int32_t)R;
   g.N = (int32_t)N;
   g.K = (int32_t)K;
+  g.splits = 1;
   g.tile_start = tile_start;
   g.tile_table = tile_table;
   g.E = (int32_t)E;

@@ -100,6 +100,11 @@ struct GemmArgs {
   int32_t gate;               // 1: gated SiLU output (see rq_fp8.h, RQ_ACT_GATE_SILU), y is [rows][N/2]
   int32_t b_gran;             // kScaleChannel, kScaleTensor or kScaleBlock128 (layout of b_scale)
   int32_t a_fmt;              // kFmtE4M3 or kFmtE5M2 (the bytes of a)
+  // split-K (dense only): the K range is cut into `splits` equal parts; part s of every tile
+  // writes its FP32 sum to partial [splits][M][N] and a reduce kernel adds the parts in order
+  // and applies the epilogue
+  int32_t splits;             // 1: no split
+  float* partial;
 };
 
 // GEMM tile shapes (rows x columns of output per workgroup).
@@ -107,6 +112,9 @@ enum { kTileBig = 0, kTileWide, kTileSmall, kTileThin, kTileThinWide, kTileKinds
 constexpr int kMinTileRows = 64;  // fewest rows of any tile shape (sizes the MoE tile table)
 
 hipError_t launch_gemm_dense(const GemmArgs& g, hipStream_t stream);
+// K parts of a dense M x N x K GEMM (1 = no split) and the FP32 partial-sum bytes they need.
+int dense_splits(int64_t M, int64_t N, int64_t K, int act, int w_gran);
+size_t dense_partial_bytes(int64_t M, int64_t N, int64_t K, int act, int w_gran);
 hipError_t launch_gemm_grouped(const GemmArgs& g, int kind, hipStream_t stream);
 int pick_grouped(int64_t R, int64_t E, int64_t N);  // tile shape for R routed rows over E experts
 int tile_rows(int kind);                       // M rows of a tile shape

@@ -236,13 +236,20 @@ struct TileInfo {
   int row_end;    // one past the last valid row
   int n0;         // first output column
   int expert;
+  int part;       // split-K: the K part this work item sums (0 without split)
 };
 
 // Logical tile L -> rows and columns: groups of kGroupM M-tiles walked column by column.  In
 // grouped mode expert e owns logical tiles [tile_start[e], tile_start[e + 1]) * n_tiles and
 // its M-tiles are grouped on their own.
 template <int BM, int BN, bool GROUPED>
-__device__ __forceinline__ TileInfo tile_info(const GemmArgs& p, int L, int m_tiles, int n_tiles) {
+__device__ __forceinline__ TileInfo tile_info(const GemmArgs& p, int L, int m_tiles, int n_tiles,
+                                              int tiles_per_part = 0) {
+  int part = 0;
+  if (tiles_per_part > 0) {  // split-K: work item L is part L / tiles of tile L % tiles
+    part = L / tiles_per_part;
+    L -= part * tiles_per_part;
+  }
   int base = 0;
   if (GROUPED) {  // the expert whose M-tiles hold L: largest e with tile_start[e] * n_tiles <= L
     int lo = 0, hi = p.E;
@@ -261,6 +268,7 @@ __device__ __forceinline__ TileInfo tile_info(const GemmArgs& p, int L, int m_ti
   const int in_group = L - group * per_group;
   const int mt = base + first_m + in_group % gm;
   TileInfo t;
+  t.part = part;
   t.n0 = (in_group / gm) * BN;
   if (GROUPED) {
     const int32_t* ent = p.tile_table + 4 * (int64_t)mt;
@@ -285,19 +293,24 @@ struct TileDesc2 {
 // memory).
 __device__ __forceinline__ v4i pick(bool c, v4i x, v4i y) { return c ? x : y; }
 
+// Split-K: the descriptors start at the part's first K byte (kl bytes per part), so the K
+// loop runs over the part as over a whole row; the row stride stays K.
 template <int BN>
-__device__ __forceinline__ TileDesc2 tile_descs(const GemmArgs& p, const TileInfo& t) {
+__device__ __forceinline__ TileDesc2 tile_descs(const GemmArgs& p, const TileInfo& t, int kl = 0) {
   TileDesc2 d;
-  d.a = make_desc(p.a + (int64_t)t.row_begin * p.K, (uint32_t)((t.row_end - t.row_begin) * p.K));
-  d.b = make_desc(p.b + ((int64_t)t.expert * p.N + t.n0) * p.K, (uint32_t)(min(BN, p.N - t.n0) * p.K));
+  const int k0 = t.part * kl;
+  d.a = make_desc(p.a + (int64_t)t.row_begin * p.K + k0, (uint32_t)((t.row_end - t.row_begin) * p.K - k0));
+  d.b = make_desc(p.b + ((int64_t)t.expert * p.N + t.n0) * p.K + k0, (uint32_t)(min(BN, p.N - t.n0) * p.K - k0));
   return d;
 }
 
-template <class C, bool GROUPED, bool GATE, bool BLK, bool A5>
+template <class C, bool GROUPED, bool GATE, bool BLK, bool A5, bool SPLITK>
 __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles, int n_tiles) {
   // operand formats of the MFMA: the weight fragment (first operand) is E4M3, the activation
   // fragment (second) E4M3 or, with A5, E5M2 (format code 1 of the f8f6f4 instruction)
   constexpr int kFmtB = A5 ? 1 : 0;
+  static_assert(!SPLITK || (!GROUPED && !GATE && !BLK && !C::SPLIT),
+                "split-K: dense, plain output, per-channel or per-tensor scales, every wave stores");
   static_assert(!BLK || (C::WN <= kScaleBlock && kScaleBlock % C::WN == 0),
                 "a wave's columns lie in one 128-column scale block");
   static_assert(!GATE || C::TJ % 2 == 0, "gated output pairs 32-column gate and up blocks in a wave");
@@ -307,7 +320,8 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
   // Workgroup ids go round-robin over the 8 XCDs; each XCD's workgroups share a contiguous
   // slice of the logical order.  In grouped mode the real M-tile count is on the device.
   if (GROUPED) m_tiles = load_uniform(p.tile_start + p.E);
-  const int total = m_tiles * n_tiles;
+  const int tiles_pp = SPLITK ? m_tiles * n_tiles : 0;  // split-K: tiles per K part
+  const int total = m_tiles * n_tiles * (SPLITK ? p.splits : 1);
   int first, stride, last;
   {
     const int bid = (int)blockIdx.x;
@@ -338,11 +352,12 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
   // MFMAs.
   const bool loader = wave < C::LOADERS;                  // every wave unless SPLIT
   const bool storer = !C::SPLIT || wave >= C::LOADERS;    // every wave unless SPLIT
-  const int K = p.K;
+  const int K = p.K;    // row stride of both operands
   const int N = p.N;
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  const int ktiles = (K + BK - 1) / BK;
-  const int full_slabs = K / BK;
+  const int KL = SPLITK ? K / p.splits : K;  // K bytes one work item sums (a multiple of BK when split)
+  const int ktiles = (KL + BK - 1) / BK;
+  const int full_slabs = KL / BK;
 
   // ---- direct-to-LDS loads.  Load i of loader w fills slab rows [row0, row0 + 16) with
   // row0 = 16 (i * LOADERS + w); lane l writes 16 bytes at row row0 + l / 4, physical
@@ -370,13 +385,13 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
   // Any slab, including the ragged last one: granules past K read zero.
   auto issue_one = [&](const TileDesc2& d, int slab, uint32_t lds, int i) {
     const uint32_t k0 = (uint32_t)slab * BK;
-    const bool kin = (int)k0 + 16 * gran < K;
+    const bool kin = (int)k0 + 16 * gran < KL;
     load_lds_16(i < C::A_LOADS ? d.a : d.b, kin ? voff[i] + k0 : kOutOfRange, 0u, lds, 16 * BK * C::LOADERS * i);
   };
   // The tile's BM row scales and BN column scales into scale area `region` (0 or 1);
   // entries past the tile's rows or columns read zero and are never used.
   auto issue_scales = [&](const TileInfo& t, int region) {
-    if (!loader) return;
+    if (!loader || SPLITK) return;  // split-K parts are scaled by the reduce kernel
     const uint32_t base = smem_lds + C::SCALE_OFF + region * C::SCALE_BYTES;
     for (int q = wave; q < C::SCALE_LOADS; q += C::LOADERS) {
       const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane((int)(base + 256 * q));
@@ -429,8 +444,8 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
   uint4 fa[2 * C::TI], fb0[2 * C::TJ], fb1[2 * C::TJ];
 
   // ---- current and next tile
-  TileInfo cur = tile_info<C::BM, C::BN, GROUPED>(p, first, m_tiles, n_tiles);
-  TileDesc2 dc = tile_descs<C::BN>(p, cur);
+  TileInfo cur = tile_info<C::BM, C::BN, GROUPED>(p, first, m_tiles, n_tiles, tiles_pp);
+  TileDesc2 dc = tile_descs<C::BN>(p, cur, SPLITK ? KL : 0);
   int rb = 0;  // ring buffer that holds slab 0 of the current tile
 
   // A tile's scales and slabs 0..min(S, ktiles)-1 into ring buffers 0.., then (after the
@@ -468,8 +483,8 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
     TileInfo nxt = cur;
     TileDesc2 dn = dc;
     if (has_next) {
-      nxt = tile_info<C::BM, C::BN, GROUPED>(p, L + stride, m_tiles, n_tiles);
-      dn = tile_descs<C::BN>(p, nxt);
+      nxt = tile_info<C::BM, C::BN, GROUPED>(p, L + stride, m_tiles, n_tiles, tiles_pp);
+      dn = tile_descs<C::BN>(p, nxt, SPLITK ? KL : 0);
     }
     // With K of at least S slabs the last S steps fetch slabs 0..S-1 of the next tile.
     const bool pre = has_next && ktiles >= C::S;
@@ -610,7 +625,28 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
     // SPLIT, loaders stage each 32-row block in an LDS strip shared with their storer; after
     // a barrier the storer reads it back as 16-byte chunks along the rows (whole 128-byte
     // row segments per store) and stores it; a second barrier frees the strip.
-    {
+    if constexpr (SPLITK) {
+      // FP32 part sums straight from registers: register group g of tile (i, jj) holds 4
+      // consecutive columns of one row, one 16-byte store
+      float* pt = p.partial + ((int64_t)cur.part * p.M + cur.row_begin) * N + cur.n0;
+      const int rows = cur.row_end - cur.row_begin;
+      const int erow = lane & 31, ehalf = lane >> 5;
+#pragma unroll
+      for (int i = 0; i < C::TI; ++i) {
+        const int lrow = wm * C::WM + 32 * i + erow;
+#pragma unroll
+        for (int jj = 0; jj < C::TJ; ++jj)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = wn * C::WN + 32 * jj + 8 * g + 4 * ehalf;
+            if (lrow < rows && cur.n0 + col < N) {
+              const v16f& a = acc[i][jj];
+              *reinterpret_cast<v4f*>(pt + (int64_t)lrow * N + col) =
+                  (v4f){a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+            }
+          }
+      }
+    } else {
       constexpr int kOutTJ = GATE ? C::TJ / 2 : C::TJ;  // 32-column output blocks per wave
       constexpr int kOutWN = 32 * kOutTJ;               // output columns per wave
       const int NO = GATE ? N / 2 : N;                   // output row length
@@ -700,7 +736,7 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
 // Workgroups of this kernel the device keeps resident at once (all CUs), cached per device.
 // The cache is read and filled with atomic operations, so concurrent calls from several
 // host threads are safe: two threads may both compute the value, and both store the same one.
-template <class C, bool GROUPED, bool GATE, bool BLK, bool A5>
+template <class C, bool GROUPED, bool GATE, bool BLK, bool A5, bool SPLITK>
 int resident_workgroups() {
   constexpr int kDevices = 64;
   static std::atomic<int> cache[kDevices];
@@ -711,8 +747,8 @@ int resident_workgroups() {
   if (known > 0) return known;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_fp8_kernel<C, GROUPED, GATE, BLK, A5>, C::NT, 0) !=
-          hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_fp8_kernel<C, GROUPED, GATE, BLK, A5, SPLITK>,
+                                                    C::NT, 0) != hipSuccess ||
       per_cu <= 0)
     per_cu = 1;
   const int value = cus * per_cu;
@@ -729,16 +765,78 @@ int64_t grid_cap_override() {
   return v > 0 ? (int64_t)v : 0;
 }
 
-template <class C, bool GROUPED, bool GATE, bool BLK, bool A5>
+template <class C, bool GROUPED, bool GATE, bool BLK, bool A5, bool SPLITK = false>
 hipError_t launch_one(const GemmArgs& g, int m_tiles, hipStream_t stream) {
   const int n_tiles = (int)((g.N + C::BN - 1) / C::BN);
-  const int64_t tiles = (int64_t)m_tiles * n_tiles;  // grouped: the worst case
-  int64_t cap = resident_workgroups<C, GROUPED, GATE, BLK, A5>();
+  // work items: tiles (grouped: the worst case), times the K parts with split-K
+  const int64_t tiles = (int64_t)m_tiles * n_tiles * (SPLITK ? g.splits : 1);
+  int64_t cap = resident_workgroups<C, GROUPED, GATE, BLK, A5, SPLITK>();
   const int64_t forced = grid_cap_override();
   if (forced > 0 && forced < cap) cap = forced;
   const int64_t want = (tiles + 7) / 8 * 8;
   const int64_t grid = want < cap ? want : cap;
-  gemm_fp8_kernel<C, GROUPED, GATE, BLK, A5><<<dim3((unsigned)grid), dim3(C::NT), 0, stream>>>(g, m_tiles, n_tiles);
+  gemm_fp8_kernel<C, GROUPED, GATE, BLK, A5, SPLITK>
+      <<<dim3((unsigned)grid), dim3(C::NT), 0, stream>>>(g, m_tiles, n_tiles);
+  return hipGetLastError();
+}
+
+// Split-K reduce: adds the K parts of each output in part order (FP32) and applies the GEMM
+// kernel's epilogue, y = fl16(fl32(fl32(acc * s_a[m]) * s_b[n])) with the same roundings, or
+// with GATE h = silu_mul of the FP16 gate and up values (output block o of 32 features takes
+// gate columns [64 o, 64 o + 32) and up columns [64 o + 32, 64 o + 64)).  One thread per 8
+// output values: 16-byte loads of each part, one 16-byte store.
+template <bool GATE>
+__global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ partial, int splits, int M, int N,
+                                                     const float* __restrict__ a_scale,
+                                                     const float* __restrict__ b_scale, int b_gran,
+                                                     uint16_t* __restrict__ y) {
+  const int NO = GATE ? N / 2 : N;
+  const int per_row = NO / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)M * per_row) return;
+  const int m = (int)(idx / per_row);
+  const int c = 8 * (int)(idx % per_row);  // first output column
+  const int64_t part_stride = (int64_t)M * N;
+  const float sa = a_scale[m];
+  // FP16 of the 8 columns starting at column n0 of the GEMM output
+  auto columns = [&](int n0, uint32_t (&out)[4]) {
+    const float* src = partial + (int64_t)m * N + n0;
+    v4f lo = *reinterpret_cast<const v4f*>(src), hi = *reinterpret_cast<const v4f*>(src + 4);
+    for (int s = 1; s < splits; ++s) {
+      lo += *reinterpret_cast<const v4f*>(src + s * part_stride);
+      hi += *reinterpret_cast<const v4f*>(src + s * part_stride + 4);
+    }
+    float sb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sb[i] = b_gran == kScaleTensor ? b_scale[0] : b_scale[n0 + i];
+    out[0] = pack_half2((lo[0] * sa) * sb[0], (lo[1] * sa) * sb[1]);
+    out[1] = pack_half2((lo[2] * sa) * sb[2], (lo[3] * sa) * sb[3]);
+    out[2] = pack_half2((hi[0] * sa) * sb[4], (hi[1] * sa) * sb[5]);
+    out[3] = pack_half2((hi[2] * sa) * sb[6], (hi[3] * sa) * sb[7]);
+  };
+  uint32_t v[4];
+  if constexpr (GATE) {
+    const int gcol = 64 * (c / 32) + c % 32;
+    uint32_t g[4], u[4];
+    columns(gcol, g);
+    columns(gcol + 32, u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = silu_mul_pair(g[i], u[i]);
+  } else {
+    columns(c, v);
+  }
+  *reinterpret_cast<uint4*>(y + (int64_t)m * NO + c) = make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+hipError_t launch_splitk_reduce(const GemmArgs& g, hipStream_t stream) {
+  const int64_t threads = (int64_t)g.M * ((g.gate ? g.N / 2 : g.N) / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (g.gate)
+    splitk_reduce<true><<<grid, dim3(256), 0, stream>>>(g.partial, g.splits, g.M, g.N, g.a_scale, g.b_scale,
+                                                        g.b_gran, g.y);
+  else
+    splitk_reduce<false><<<grid, dim3(256), 0, stream>>>(g.partial, g.splits, g.M, g.N, g.a_scale, g.b_scale,
+                                                         g.b_gran, g.y);
   return hipGetLastError();
 }
 
@@ -810,7 +908,20 @@ int pick_dense(int64_t M, int64_t N, bool gate) {
 
 template <class C>
 hipError_t launch_dense(const GemmArgs& g, hipStream_t stream) {
-  return launch<C, false>(g, (int)((g.M + C::BM - 1) / C::BM), stream);
+  const int m_tiles = (int)((g.M + C::BM - 1) / C::BM);
+  if constexpr (!C::SPLIT) {
+    // split-K: the GEMM writes FP32 part sums (plain output, the operand format picks the
+    // instantiation), then the reduce kernel applies the epilogue
+    if (g.splits > 1 && g.partial != nullptr && g.b_gran != kScaleBlock128) {
+      const hipError_t e = g.a_fmt == kFmtE5M2 ? launch_one<C, false, false, false, true, true>(g, m_tiles, stream)
+                                               : launch_one<C, false, false, false, false, true>(g, m_tiles, stream);
+      if (e != hipSuccess) return e;
+      return launch_splitk_reduce(g, stream);
+    }
+  }
+  GemmArgs one = g;
+  one.splits = 1;
+  return launch<C, false>(one, m_tiles, stream);
 }
 
 }  // namespace
@@ -832,6 +943,29 @@ int pick_grouped(int64_t R, int64_t E, int64_t N) {
 }
 
 int tile_rows(int kind) { return kTiles[kind].bm; }
+
+// Split-K for small M (the weight-streaming regime): a GEMM with few tiles keeps only part of
+// the 256 CUs streaming weights, each over a long K loop.  Cutting K into s equal parts (s a
+// power of two up to 8) multiplies the work items while the 64 x 128 tile count stays within
+// three per CU and every part keeps at least 32 slabs of 64 bytes: the FP32 part sums cost
+// 8 s M N bytes of traffic (written, then read by the reduce), which only a long K loop
+// repays (measured on the 512-row layer: K = 8192 gains 34%, K = 2048 loses 20-60%).  It
+// depends on M, N and K only - not on the output form - so the gated and the plain gate/up
+// linear sum K the same way.
+int dense_splits(int64_t M, int64_t N, int64_t K, int act, int w_gran) {
+  (void)act;
+  if (w_gran == kScaleBlock128 || M > 1024 || K % BK != 0) return 1;
+  const int64_t base = ((M + 63) / 64) * ((N + 127) / 128);
+  const int64_t slabs = K / BK;
+  int s = 1;
+  while (s < 8 && base * s * 2 <= 3 * 256 && slabs % (2 * s) == 0 && slabs / (2 * s) >= 32) s *= 2;
+  return s;
+}
+
+size_t dense_partial_bytes(int64_t M, int64_t N, int64_t K, int act, int w_gran) {
+  const int s = dense_splits(M, N, K, act, w_gran);
+  return s > 1 ? (size_t)s * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
 
 int64_t grouped_max_mtiles(int64_t R, int64_t E, int tile_m) { return (R + tile_m - 1) / tile_m + E; }
 

@@ -6,7 +6,9 @@
 // its top-k expert ids and weights are inputs here.
 //
 // Plan: slot j = t * top_k + k goes to expert ids[j].  The canonical permuted order sorts
-// slots by (expert, j) - a stable counting sort - computed without any host round trip:
+// slots by (expert, j) - a stable counting sort - computed without any host round trip.  Up to
+// 32768 slots (and 256 experts) one workgroup does it all in a single launch (plan_single);
+// beyond, three kernels:
 //   1. plan_hist:    per block of 1024 slots, a histogram over experts (LDS atomics on
 //                    integer counts, so the result is deterministic);
 //   2. plan_scan:    one workgroup turns the block histograms into per-expert offsets,
@@ -36,13 +38,16 @@ __device__ unsigned int g_error_flags;
 // in the error word (report = true in the one kernel that reads every slot first) and mapped
 // into [0, E) so that every index the plan produces stays inside the workspace; the rows of
 // such slots are then meaningless, but no kernel reads or writes out of bounds.
-__device__ __forceinline__ int expert_of(const int32_t* ids, int64_t j, int E, bool report) {
-  int e = ids[j];
+__device__ __forceinline__ int checked_expert(int e, int E, bool report) {
   if (e < 0 || e >= E) {
     if (report) atomicOr(&g_error_flags, (unsigned)kErrExpertId);
     e = e < 0 ? 0 : E - 1;
   }
   return e;
+}
+
+__device__ __forceinline__ int expert_of(const int32_t* ids, int64_t j, int E, bool report) {
+  return checked_expert(ids[j], E, report);
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_hist(const int32_t* __restrict__ ids, int64_t R, int E,
@@ -199,6 +204,116 @@ __global__ __launch_bounds__(kPlanThreads) void plan_scatter(const int32_t* __re
   }
 }
 
+// The whole plan in one workgroup (one launch instead of three) for up to
+// kSinglePlanMaxRows slots and kSinglePlanMaxExperts experts: each thread loads its IPT slot
+// ids (slots tid, tid + 1024, ...) into registers at once, so the kernel waits for global
+// memory a single time; then the expert histogram (LDS integer atomics), the scans and the
+// M-tile table as in plan_scan, and the stable scatter over chunks of 1024 slots taken in slot
+// order, each ranked like plan_scatter and placed after the rows of earlier chunks.
+constexpr int64_t kSinglePlanMaxRows = 32768;
+constexpr int64_t kSinglePlanMaxExperts = 256;  // keeps its LDS (19 E + 1 words) under 20 KB
+
+template <int IPT>
+__global__ __launch_bounds__(kPlanThreads) void plan_single(const int32_t* __restrict__ ids, int R, int E,
+                                                            int nbits, int tile_m, int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ tile_start,
+                                                            int32_t* __restrict__ tile_table,
+                                                            int32_t* __restrict__ perm, int32_t* __restrict__ pos) {
+  extern __shared__ int32_t sh[];
+  int32_t* base = sh;                  // [E] rows per expert, then the next free row of each expert
+  int32_t* s_off = sh + E;             // [E] first row of each expert
+  int32_t* s_tstart = sh + 2 * E;      // [E + 1] first M-tile of each expert
+  int32_t* wcount = sh + 3 * E + 1;    // [kPlanWaves][E] per-wave counts of a chunk, then their prefix
+  __shared__ int wave_sums[kPlanWaves + 1];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int ex[IPT];  // experts of slots tid + 1024 c (0 past R: never used)
+#pragma unroll
+  for (int c = 0; c < IPT; ++c) {
+    const int j = c * kPlanThreads + tid;
+    ex[c] = j < R ? ids[j] : 0;
+  }
+  for (int e = tid; e < E; e += kPlanThreads) base[e] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < IPT; ++c) {
+    const int j = c * kPlanThreads + tid;
+    if (j < R) {
+      ex[c] = checked_expert(ex[c], E, true);
+      atomicAdd(&base[ex[c]], 1);
+    }
+  }
+  __syncthreads();
+  // offsets and M-tile prefix (E <= kPlanThreads: one expert per thread)
+  const int count = tid < E ? base[tid] : 0;
+  int total_rows, total_tiles;
+  const int off = block_exclusive_scan(count, wave_sums, total_rows);
+  __syncthreads();
+  const int tstart = block_exclusive_scan(tid < E ? (count + tile_m - 1) / tile_m : 0, wave_sums, total_tiles);
+  if (tid < E) {
+    offsets[tid] = off;
+    tile_start[tid] = tstart;
+    s_off[tid] = off;
+    s_tstart[tid] = tstart;
+    base[tid] = off;
+  }
+  if (tid == 0) {
+    offsets[E] = total_rows;
+    tile_start[E] = total_tiles;
+    s_tstart[E] = total_tiles;
+  }
+  __syncthreads();
+  for (int t = tid; t < total_tiles; t += kPlanThreads) {
+    int lo = 0, hi = E - 1;  // largest x with s_tstart[x] <= t
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_tstart[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int first = s_off[lo] + (t - s_tstart[lo]) * tile_m;
+    const int end_e = lo + 1 < E ? s_off[lo + 1] : total_rows;
+    int32_t* ent = tile_table + 4 * (int64_t)t;
+    ent[0] = lo;
+    ent[1] = first;
+    ent[2] = first + tile_m < end_e ? first + tile_m : end_e;
+    ent[3] = 0;
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int c = 0; c < IPT; ++c) {
+    if (c * kPlanThreads >= R) break;  // uniform
+    const int j = c * kPlanThreads + tid;
+    const bool valid = j < R;
+    const int e = ex[c];
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const uint64_t m = __ballot(((e >> b) & 1) != 0);
+      peers &= ((e >> b) & 1) ? m : ~m;
+    }
+    const int rank = __popcll(peers & below);
+    for (int i = tid; i < kPlanWaves * E; i += kPlanThreads) wcount[i] = 0;
+    __syncthreads();
+    if (valid && rank == 0) wcount[wave * E + e] = __popcll(peers);
+    __syncthreads();
+    int chunk_rows = 0;
+    if (tid < E) {
+      for (int w = 0; w < kPlanWaves; ++w) {
+        const int n = wcount[w * E + tid];
+        wcount[w * E + tid] = chunk_rows;
+        chunk_rows += n;
+      }
+    }
+    __syncthreads();
+    if (valid) {
+      const int row = base[e] + wcount[wave * E + e] + rank;
+      perm[row] = j;
+      pos[j] = row;
+    }
+    __syncthreads();
+    if (tid < E) base[tid] += chunk_rows;
+  }
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y_perm,
                                                       const int32_t* __restrict__ pos,
                                                       const uint16_t* __restrict__ topk_w, int top_k,
@@ -239,6 +354,16 @@ hipError_t launch_moe_plan(const int32_t* ids, int64_t T, int top_k, int64_t E, 
   const int e = (int)E;
   int nbits = 0;
   while ((1 << nbits) < e) ++nbits;
+  if (R <= kSinglePlanMaxRows && E <= kSinglePlanMaxExperts) {
+    const size_t lds = (size_t)(3 * e + 1 + kPlanWaves * e) * sizeof(int32_t);
+    const dim3 g1(1), blk(kPlanThreads);
+    const int r = (int)R, per = (int)((R + kPlanThreads - 1) / kPlanThreads);  // ids per thread
+    if (per <= 1) plan_single<1><<<g1, blk, lds, stream>>>(ids, r, e, nbits, tile_m, offsets, tile_start, tile_table, perm, pos);
+    else if (per <= 4) plan_single<4><<<g1, blk, lds, stream>>>(ids, r, e, nbits, tile_m, offsets, tile_start, tile_table, perm, pos);
+    else if (per <= 8) plan_single<8><<<g1, blk, lds, stream>>>(ids, r, e, nbits, tile_m, offsets, tile_start, tile_table, perm, pos);
+    else plan_single<32><<<g1, blk, lds, stream>>>(ids, r, e, nbits, tile_m, offsets, tile_start, tile_table, perm, pos);
+    return hipGetLastError();
+  }
   if (nb > 0) {
     plan_hist<<<dim3(nb), dim3(kPlanThreads), e * sizeof(int32_t), stream>>>(ids, R, e, block_hist);
     hipError_t err = hipGetLastError();

@@ -112,6 +112,17 @@ int rq_fp8_quant_weights(const uint16_t* w, int64_t B, int64_t N, int64_t K,
  * (the quantized activation bytes and scales, each region 256-byte aligned). */
 size_t rq_fp8_linear_workspace_size(int64_t M, int64_t K, int act);
 
+/* Bytes of workspace with which rq_fp8_linear (and rq_fp8_linear_ex with per-channel or
+ * per-tensor weight scales) may also split K: the quantized activations as above plus, for few
+ * rows (M <= 1024, the weight-streaming regime), FP32 partial sums [parts][M][N].  With such a
+ * workspace a linear whose 64 x 128 tile count would leave most of the 256 compute units idle
+ * cuts K into 2, 4 or 8 equal parts (each at least 2048 bytes of K), runs them as separate
+ * work items and adds the parts in a fixed order in a second kernel that applies the
+ * epilogue: outputs stay deterministic, and the part count depends only on M, N and K (the
+ * gated and the plain gate/up linear sum alike).  With a smaller workspace (at least
+ * rq_fp8_linear_workspace_size) the call does not split.  Returns 0 for invalid sizes. */
+size_t rq_fp8_linear_workspace_size_ex(int64_t M, int64_t N, int64_t K, int act);
+
 /* W8A8 FP8 linear (pages: "Quantized Inference for OneRec-V2", section 关键证据;
  * "FP8量化在生成式推荐系统OneRec-V2中的优化实践", §2.3 and Fig. 2).
  * x [M][K] FP16 (or [M][2K] with RQ_ACT_SILU_MUL) is quantized per token into the
@@ -119,7 +130,8 @@ size_t rq_fp8_linear_workspace_size(int64_t M, int64_t K, int act);
  * dequantized with w_scale [N] into y [M][N] FP16.
  * With RQ_ACT_GATE_SILU, y is [M][N / 2] (see above).
  * Two kernels on `stream`: the row quantizer, then the FP8 MFMA GEMM with the
- * scale/FP16 epilogue.  dbg may be NULL. */
+ * scale/FP16 epilogue (three with split-K: the GEMM writes FP32 part sums and a reduce kernel
+ * applies the epilogue; see rq_fp8_linear_workspace_size_ex).  dbg may be NULL. */
 int rq_fp8_linear(const uint16_t* x, int64_t M, int64_t K, int act,
                   const uint8_t* w_q, const float* w_scale, int64_t N,
                   uint16_t* y, void* workspace, size_t workspace_bytes,
@@ -134,8 +146,11 @@ int rq_fp8_linear(const uint16_t* x, int64_t M, int64_t K, int act,
  * owns x, w_q, w_scale and y.
  * Limit: rq_fp8_linear_workspace_size(M, K, act) <= RQ_STATIC_SCRATCH_BYTES (for example
  * M = 4096 rows of K = 8192), else RQ_ERR_SCRATCH before anything is enqueued.
+ * The call splits K as rq_fp8_linear does with a workspace of
+ * rq_fp8_linear_workspace_size_ex bytes whenever the partial sums fit in the buffer too.
  * Every call on one GPU shares that GPU's buffer, which keeps the last call's contents (the
- * quantizer rewrites every byte the GEMM then reads, so nothing needs clearing): calls that
+ * quantizer rewrites every byte the GEMM then reads, and the GEMM every partial sum the
+ * reduce reads, so nothing needs clearing): calls that
  * overlap on one GPU (concurrent streams, or host threads) race on it and must be ordered
  * by the caller.  The buffer's device address is resolved on the first call on each
  * device. */

@@ -49,6 +49,17 @@ def test_workspace_sizes():
     assert lib.rq_fp8_linear_workspace_size(4096, 2048, 0) == 4096 * 2048 + 4096 * 4
     assert lib.rq_fp8_linear_workspace_size(3, 16, 0) == 256 + 256
     assert lib.rq_fp8_linear_workspace_size(-1, 16, 0) == 0
+    # split-K partial sums only for few rows and long K: 512 x 2048 x 8192 splits K in 4,
+    # 300 x 6144 x 4096 in 2; K = 2048 and 4096 rows do not split
+    assert lib.rq_fp8_linear_workspace_size_ex(512, 2048, 8192, 2) == 512 * 8192 + 2048 + 4 * 512 * 2048 * 4
+    assert lib.rq_fp8_linear_workspace_size_ex(300, 6144, 4096, 0) == \
+        300 * 4096 + 1280 + 2 * 300 * 6144 * 4
+    assert lib.rq_fp8_linear_workspace_size_ex(512, 2048, 2048, 0) == lib.rq_fp8_linear_workspace_size(512, 2048, 0)
+    assert lib.rq_fp8_linear_workspace_size_ex(512, 16384, 2048, 0) == lib.rq_fp8_linear_workspace_size(512, 2048, 0)
+    assert lib.rq_fp8_linear_workspace_size_ex(4096, 2048, 8192, 0) == lib.rq_fp8_linear_workspace_size(4096, 8192, 0)
+    assert lib.rq_fp8_linear_workspace_size_ex(64, 512, 512, 0) == lib.rq_fp8_linear_workspace_size(64, 512, 0)
+    assert lib.rq_fp8_linear_workspace_size_ex(512, 2048, 2048 + 16, 0) == lib.rq_fp8_linear_workspace_size(512, 2064, 0)
+    assert lib.rq_fp8_linear_workspace_size_ex(512, 0, 2048, 0) == 0
     a = lib.rq_fp8_moe_workspace_size(16384, 2, 32, 8192, 2048, 0, 0, 0)
     b = lib.rq_fp8_moe_workspace_size(16384, 2, 32, 2048, 4096, 1, 1, 1)
     assert a >= 16384 * 2048 and b >= 32768 * 4096 + 32768 * 2048 * 2

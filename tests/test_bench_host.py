@@ -12,18 +12,17 @@ import bench
 
 def _names(only=None, steps=2, prefix=("quant_rows_regs<4, false>", "at::native::fill")):
     tok = {"quant": "void rq::quant_rows_regs<8, false>(...)", "gemm": "void rq::gemm_fp8_kernel<Cfg>(...)",
-           "plan_hist": "rq::plan_hist(...)", "plan_scan": "rq::plan_scan(...)",
-           "plan_scatter": "rq::plan_scatter(...)", "combine": "rq::combine_kernel(...)"}
+           "plan": "rq::plan_single(...)", "combine": "rq::combine_kernel(...)"}
     seq = [tok[k] for _, k in bench.step_dispatches(only)]
     return list(prefix) + seq * steps + ["at::native::vectorized_elementwise_kernel (copy)"]
 
 
 def test_step_table_matches_workloads():
     seq = bench.step_dispatches(None)
-    # 8 linears x 2 kernels, 2 uncombined MoE calls x 5, 2 combined x 6
-    assert len(seq) == 8 * 2 + 2 * 5 + 2 * 6
+    # 8 linears x 2 kernels, 2 uncombined MoE calls x 3, 2 combined x 4
+    assert len(seq) == 8 * 2 + 2 * 3 + 2 * 4
     assert ("moe gate_up", "gemm") in seq
-    assert len(bench.step_dispatches("moe")) == 11
+    assert len(bench.step_dispatches("moe")) == 7
 
 
 def test_align_finds_every_step_and_labels():
@@ -37,7 +36,7 @@ def test_align_finds_every_step_and_labels():
 
 
 def test_align_rejects_a_foreign_sequence():
-    names = ["rq::plan_scan(...)"] * 5
+    names = ["rq::plan_single(...)"] * 5
     with pytest.raises(SystemExit):
         bench._align_steps(names, None, None)
 

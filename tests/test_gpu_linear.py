@@ -188,3 +188,58 @@ def test_gated_needs_64_column_blocks():
     with pytest.raises(rq.RqError):
         rq.linear(torch.zeros((4, 64), dtype=torch.float16, device="cuda"), wq,
                   torch.ones(96, device="cuda"), act="gate_silu")
+
+
+def _splits(m, n, k):
+    from fp8_quantized_generative_amd import _lib
+    lib = _lib.load()
+    extra = lib.rq_fp8_linear_workspace_size_ex(m, n, k, 0) - lib.rq_fp8_linear_workspace_size(m, k, 0)
+    return (extra // 256 * 256) // (4 * m * n) if extra else 1
+
+
+@pytest.mark.parametrize("m,n,k", [(512, 2048, 8192), (300, 6144, 4096), (64, 256, 4096), (1, 512, 8192),
+                                   (1000, 1040, 4096)])
+def test_split_k_small_m(m, n, k):
+    """Few rows and a long K: the linear splits K into 2-8 parts whose FP32 sums a reduce kernel adds in
+    order.  Every row within the oracle's tolerance; bit-identical on a second run; the
+    unsplit call (smaller workspace) within the tolerance too."""
+    rq = require_gpu()
+    case("split-K linear m=%d n=%d k=%d" % (m, n, k))
+    assert _splits(m, n, k) > 1
+    rng = np.random.default_rng(m + n + k)
+    x16, w16 = workloads.acts_student_t(rng, m, k), workloads.weights(rng, (n, k))
+    ratio = _check(x16, w16)
+    assert ratio <= 1
+    wq, ws = rq.quant_weights(dev(w16))
+    x = dev(x16)
+    a, b = host(rq.linear(x, wq, ws)), host(rq.linear(x, wq, ws))
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    plain = torch.empty(rq.linear_workspace_size(m, k), dtype=torch.uint8, device="cuda")
+    y1 = host(rq.linear(x, wq, ws, workspace=plain))
+    xq, xs = quant.quantize_rows(x16)
+    ok, r1, _ = linear.check(y1, xq, xs, host(wq), host(ws))
+    assert ok, r1
+
+
+@pytest.mark.parametrize("m,f,k", [(512, 512, 4096), (96, 1024, 8192)])
+def test_split_k_gated_equals_unfused(m, f, k):
+    """The gated gate/up linear splits K exactly as the plain one (the part count depends on
+    M, N and K only), so its h equals the unfused path's bit for bit."""
+    rq = require_gpu()
+    case("split-K gated m=%d f=%d k=%d" % (m, f, k))
+    assert _splits(m, 2 * f, k) > 1
+    rng = np.random.default_rng(m * f + k)
+    x = dev(workloads.acts_channel_lognormal(rng, m, k))
+    w = workloads.weights(rng, (2 * f, k))
+    wq, ws = rq.quant_weights(dev(w))
+    order = torch.from_numpy(ffn.gate_up_order(f)).cuda()
+    h = host(rq.linear(x, wq[order].contiguous(), ws[order].contiguous(), act="gate_silu"))
+    gu = rq.linear(x, wq, ws)
+    _, dbg = rq.linear(gu, torch.zeros((16, f), dtype=torch.uint8, device="cuda"), torch.ones(16, device="cuda"),
+                       act="silu_mul", debug=True)
+    assert np.array_equal(h.view(np.uint16), host(dbg["h"]).view(np.uint16))
+    assert ulp_diff16(h, ffn.silu_mul(host(gu), f)).max() <= 1
+    # and the gate/up output itself against the oracle
+    xq, xs = quant.quantize_rows(host(x))
+    ok, r, _ = linear.check(host(gu), xq, xs, host(wq), host(ws))
+    assert ok, r

@@ -27,7 +27,8 @@ def _stream():
 
 
 def _reference(lib, x, m, k, act, wq, ws, n, y):
-    need = lib.rq_fp8_linear_workspace_size(m, k, act)
+    # the workspace that lets rq_fp8_linear split K as the static buffer does
+    need = lib.rq_fp8_linear_workspace_size_ex(m, n, k, act)
     wsp = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     st = lib.rq_fp8_linear(_p(x), m, k, act, _p(wq), _p(ws), n, _p(y), _p(wsp), wsp.numel(), None, _stream())
     assert st == 0, st
@@ -39,8 +40,9 @@ def test_noalloc_matches_linear(act):
     rq = require_gpu()
     from fp8_quantized_generative_amd import _lib
     lib = _lib.load()
-    # the larger call first, then a smaller ragged one that reuses (part of) the same buffer
-    for m, k, n, seed in ((2048, 2048, 2048, 1), (130, 528, 320, 2)):
+    # the larger call first, then smaller ones that reuse (part of) the same buffer: 512 rows
+    # split K (partial sums in the buffer too), the ragged one does not
+    for m, k, n, seed in ((2048, 2048, 2048, 1), (512, 8192, 2048, 3), (130, 528, 320, 2)):
         case("noalloc act=%d m=%d k=%d n=%d" % (act, m, k, n))
         rng = np.random.default_rng(seed + 10 * act)
         xw = 2 * k if act == 1 else k
