@@ -33,8 +33,9 @@
 //
 // Memory: each lane owns 16-byte chunks of the row (8 FP16 values), held in registers
 // between the amax reduction and the cast, so the input is read from HBM once; loads and
-// stores are 16- and 8-byte vectors, contiguous across the wave.  A row is one wavefront's,
-// or is split over 2 or 4 wavefronts when there are few rows.
+// stores are 16- and 8-byte vectors, contiguous across the wave (each load instruction covers
+// 1 KB of a row; pairing adjacent chunks per lane for 16-byte stores measured 20-55% slower).
+// A row is one wavefront's, or is split over 2 or 4 wavefronts.
 // Rows wider than 8192 values fall back to a two-pass loop that re-reads the row.
 
 #include "common.h"
@@ -252,10 +253,13 @@ hipError_t launch_impl(const uint16_t* x, int64_t rows, int64_t K, uint8_t* q, f
     quant_rows_loop<SILU, E5><<<grid, dim3(64 * kRowsPerBlock), 0, stream>>>(x, rows, K, q, scale, h, pos, fanout);
     return hipGetLastError();
   }
-  // Wavefronts per row: split long rows while the launch would hold fewer than 8192
-  // wavefronts (32 per CU), keeping at least 4 chunks per lane.
+  // Wavefronts per row: split long rows while the launch would hold fewer than 65536
+  // wavefronts, keeping at least 2 chunks per lane.  Measured on MI355X with L2 and the
+  // last-level cache flushed: 4096 x 8192 rows 25.1 -> 22.9 us (4 wavefronts per row),
+  // 16384 x 2048 rows with two output copies 30.2 -> 28.1 us and 32768 x 4096 rows
+  // 68.4 -> 65.7 us (2 per row), against one or two per row under an 8192-wavefront rule.
   int split = 1;
-  while (split < 4 && rows * split < 8192 && nchunk >= 64 * 4 * 2 * split) split *= 2;
+  while (split < 4 && rows * split < 65536 && nchunk >= 64 * 2 * 2 * split) split *= 2;
   const int64_t per_lane = (nchunk + 64 * split - 1) / (64 * split);
   if (per_lane <= 1) return launch_split<1, SILU, E5>(split, x, rows, k, q, scale, h, pos, fanout, stream);
   if (per_lane <= 2) return launch_split<2, SILU, E5>(split, x, rows, k, q, scale, h, pos, fanout, stream);
