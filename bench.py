@@ -155,6 +155,7 @@ class Path:
         self.variants = []
         self.router = None  # (bytes per launch, fn) of the MoE router, timed apart from the step
         self.attention = None  # the same for the attention core
+        self.beam = []         # (label, bytes per call, fn, torch.topk of the same rows) of the beam top-k workloads
         self.flops = 0
         want = set(only.split(",")) if only else {"attention", "ffn", "moe", "layer_small_m"}
 
@@ -210,6 +211,19 @@ class Path:
         y1 = torch.empty((64, 512), dtype=torch.float16, device="cuda")
         ws1 = torch.empty(rq.linear_workspace_size(64, 512, n=512), dtype=torch.uint8, device="cuda")
         self.c1 = (2 * 64 * 512 * 512, lambda: rq.linear(x1, *w1, out=y1, workspace=ws1))
+        if variants:
+            # beam top-k: 32 requests x (16 beams | 512 beams) x 512 codes, keep 16 | 512
+            for beams, keep in ((16, 16), (512, 512)):
+                sc = dev(workloads.beam_scores(np.random.default_rng(3000 + beams), 32, beams, 512))
+                n = beams * 512
+                ti = torch.empty((32, keep), dtype=torch.int32, device="cuda")
+                tv = torch.empty((32, keep), dtype=torch.float16, device="cuda")
+                tw = torch.empty(max(rq.topk_workspace_size(32, n, keep), 1), dtype=torch.uint8, device="cuda")
+                self.beam.append(("32 requests x %d beams x 512 codes, keep %d" % (beams, keep),
+                                  32 * n * 2 + 32 * keep * 6,
+                                  lambda sc=sc, keep=keep, ti=ti, tv=tv, tw=tw: rq.topk(sc, keep, idx=ti, vals=tv,
+                                                                                       workspace=tw),
+                                  lambda sc=sc, keep=keep: torch.topk(sc, keep, dim=1)))
         self.config = {}
         if "attention" in want:
             d = workloads.make(2)
@@ -480,6 +494,19 @@ def cpu_attention(requests=128):
             "sample": "%d requests x 32 positions, 16 heads of 128" % requests}
 
 
+def cpu_beam_topk():
+    """The oracle top-k on the larger beam workload (32 x 262144, keep 512), in GB/s."""
+    import workloads
+    from oracle import topk
+    s = workloads.beam_scores(np.random.default_rng(3512), 32, 512, 512)
+    t0 = time.perf_counter()
+    topk.topk(s, 512)
+    dt = time.perf_counter() - t0
+    by = s.size * 2 + 32 * 512 * 6
+    return {"value": round(by / dt / 1e9, 3), "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle", "seconds": round(dt, 3), "sample": "32 requests x 512 beams x 512 codes, keep 512"}
+
+
 def _find(path, patterns):
     import glob
     if not os.path.isdir(path):
@@ -737,7 +764,8 @@ def kernel_stats(path):
     with open(src) as f:
         for r in csv.DictReader(f):
             name = r["Name"]
-            if not any(k in name for k in OUR_KERNELS + ("router_topk", "attention_core", "quant_blocks", "tensor_")):
+            if not any(k in name for k in OUR_KERNELS + ("router_topk", "attention_core", "topk_segment", "splitk_reduce",
+                                                       "quant_blocks", "tensor_")):
                 continue
             short = name.replace("rq::(anonymous namespace)::", "").replace("void ", "")
             short = short.split("(")[0] if "(" in short else short
@@ -877,11 +905,13 @@ def main():
     layer = [c for c in path.calls if c[0] == "layer_small_m"]
     if not args.no_kernels:
         fl1, fn1 = path.c1
-        c1_call = stats_us(timer.sequence([fn1], reps))
-        result["dense_small"] = {"workload": "64 x 512 x 512 dense linear (quantizer + GEMM)", "call_us": c1_call,
-                                 "gemm_us": stats_us(timer.kernel(fn1, _lib.RQ_KERNEL_GEMM, reps)),
-                                 "quant_us": stats_us(timer.kernel(fn1, _lib.RQ_KERNEL_QUANT, reps)),
-                                 "timing": "flushed before each repetition; launch-latency bound"}
+        g1 = stats_us(timer.kernel(fn1, _lib.RQ_KERNEL_GEMM, reps))
+        q1 = stats_us(timer.kernel(fn1, _lib.RQ_KERNEL_QUANT, reps))
+        result["dense_small"] = {"workload": "64 x 512 x 512 dense linear (quantizer + GEMM)",
+                                 "kernels_us": round(g1["median"] + q1["median"], 2), "gemm_us": g1, "quant_us": q1,
+                                 "call_us_with_host_dispatch": stats_us(timer.sequence([fn1], reps)),
+                                 "timing": "HIP events around each kernel, flushed before each repetition; the whole "
+                                           "call timed from Python includes the binding's host dispatch"}
     if layer and not args.no_kernels:
         lay = stats_us(timer.sequence([c[5] for c in layer], reps))
         lay_bytes = sum(c[4] for c in layer)
@@ -907,13 +937,25 @@ def main():
                        "achieved_gbs": round(by / (st["median"] * 1e-6) / 1e9, 1),
                        "frac_hbm": round(by / (st["median"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                        "timing": "flushed before each repetition"}
+    if path.beam:
+        rows = []
+        for what, by, fn, default in path.beam:
+            st = stats_us(timer.kernel(fn, _lib.RQ_KERNEL_TOPK, reps))
+            rows.append({"workload": what, "us": st, "bytes_per_call": by,
+                         "achieved_gbs": round(by / (st["median"] * 1e-6) / 1e9, 1),
+                         "frac_hbm": round(by / (st["median"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "torch_topk_us": stats_us(timer.sequence([default], reps))["median"]})
+        result["beam_topk"] = {"timing": "HIP events around all kernels of the call (every stage), flushed before "
+                                         "each repetition; bytes = FP16 scores read + int32 index and FP16 score of "
+                                         "each pick written",
+                               "workloads": rows}
     del flush, timer
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         del path
         torch.cuda.empty_cache()
         result["cpu_baseline"] = cpu_baseline()
-        for key, fn in (("router", cpu_router), ("attention_core", cpu_attention)):
+        for key, fn in (("router", cpu_router), ("attention_core", cpu_attention), ("beam_topk", cpu_beam_topk)):
             if key in result:
                 result[key]["cpu_oracle"] = fn()
     print(json.dumps(result), flush=True)

@@ -11,6 +11,7 @@ PyTorch provides device memory and the current stream.
 * ``moe_grouped_linear(x, ids, w_q, w_scale, ...)``  routing plan + grouped GEMM (+ combine)
 * ``attention_core(qkv, requests, length, heads)``  FP16 causal short-context attention (QKV -> O input)
 * ``router_topk(x, w_gate, top_k)``            FP16 MoE gate logits -> top-k expert ids and weights
+* ``topk(scores, k)``                          batched top-k of FP16 candidate rows (beam search)
 * ``linear_workspace_size`` / ``moe_workspace_size``  scratch sizes for caller-held workspaces
 """
 
@@ -288,6 +289,34 @@ def attention_core(qkv, requests, length, heads, head_dim=128, out=None, stream=
     st = _lib.load().rq_attention_core(_ptr(qkv), requests, length, heads, head_dim, _ptr(out), _stream(qkv, stream))
     _lib.check("rq_attention_core", st)
     return out
+
+
+def topk_workspace_size(rows, n, k):
+    return int(_lib.load().rq_topk_workspace_size(rows, n, k))
+
+
+def topk(scores, k, idx=None, vals=None, workspace=None, stream=None):
+    """Batched top-k of FP16 rows [rows, n]: ``(idx int32 [rows, k], vals FP16 [rows, k])``,
+    ranked by score (larger first, -0 below +0), equal scores by lower index."""
+    _dev(scores, torch.float16, "scores")
+    if scores.dim() != 2:
+        raise ValueError("scores must be [rows, n]")
+    rows, n = scores.shape
+    lib = _lib.load()
+    with _on(stream):
+        if idx is None:
+            idx = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+        if vals is None:
+            vals = torch.empty((rows, k), dtype=torch.float16, device=scores.device)
+        need = lib.rq_topk_workspace_size(rows, n, k) if 1 <= k <= n else 0
+        ws = _workspace(need, scores.device, workspace)
+    _dev(idx, torch.int32, "idx")
+    _dev(vals, torch.float16, "vals")
+    _shape(idx, (rows, k), "idx")
+    _shape(vals, (rows, k), "vals")
+    st = lib.rq_topk(_ptr(scores), rows, n, k, _ptr(idx), _ptr(vals), _ptr(ws), ws.numel(), _stream(scores, stream))
+    _lib.check("rq_topk", st)
+    return idx, vals
 
 
 def debug_flag(clear=False):

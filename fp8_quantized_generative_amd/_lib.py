@@ -14,7 +14,8 @@ RQ_ERR_HIP = 6
 RQ_ACT_NONE, RQ_ACT_SILU_MUL, RQ_ACT_GATE_SILU = 0, 1, 2
 RQ_MOE_IN_TOKENS, RQ_MOE_IN_PERMUTED = 0, 1
 RQ_MOE_OUT_PERMUTED, RQ_MOE_OUT_COMBINED = 0, 1
-RQ_KERNEL_QUANT, RQ_KERNEL_GEMM, RQ_KERNEL_COMBINE, RQ_KERNEL_ROUTER, RQ_KERNEL_ATTENTION = 0, 1, 2, 3, 4
+RQ_KERNEL_QUANT, RQ_KERNEL_GEMM, RQ_KERNEL_COMBINE, RQ_KERNEL_ROUTER, RQ_KERNEL_ATTENTION, RQ_KERNEL_TOPK = \
+    0, 1, 2, 3, 4, 5
 RQ_WSCALE_CHANNEL, RQ_WSCALE_TENSOR, RQ_WSCALE_BLOCK128 = 0, 1, 2
 RQ_FP8_E4M3, RQ_FP8_E5M2 = 0, 1
 RQ_FLAG_EXPERT_ID = 1
@@ -52,6 +53,8 @@ SIGNATURES = {
     "rq_status_string": (ctypes.c_char_p, [_I]),
     "rq_device_supported": (_I, [_I]),
     "rq_debug_flag": (_I, [_I]),
+    "rq_topk_workspace_size": (_SZ, [_I64, _I64, _I]),
+    "rq_topk": (_I, [_P, _I64, _I64, _I, _P, _P, _P, _SZ, _P]),
     "rq_fp8_linear_noalloc": (_I, [_P, _I64, _I64, _I, _P, _P, _I64, _P, _P]),
 }
 

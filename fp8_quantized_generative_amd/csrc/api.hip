@@ -2,6 +2,7 @@
 // launch sequence of each entry point.  The operations are specified in rq_fp8.h.
 
 #include <atomic>
+#include <climits>
 #include <cstring>
 #include <mutex>
 
@@ -426,6 +427,30 @@ int rq_attention_core(const uint16_t* qkv, int64_t requests, int length, int hea
   return rq::launch_attention_core(qkv, requests, length, heads, out, (hipStream_t)stream) == hipSuccess
              ? RQ_OK
              : RQ_ERR_HIP;
+}
+
+size_t rq_topk_workspace_size(int64_t rows, int64_t n, int k) {
+  if (rows < 0 || n < 1 || k < 1 || k > rq::topk_max_k() || k > n) return 0;
+  const int64_t pairs = rq::topk_pairs_per_buffer(rows, n, k);
+  return pairs > 0 ? 2 * align_up((size_t)pairs * sizeof(int2)) : 0;
+}
+
+int rq_topk(const uint16_t* scores, int64_t rows, int64_t n, int k, int32_t* idx, uint16_t* vals, void* workspace,
+            size_t workspace_bytes, void* stream) {
+  if (rows < 0 || n < 1 || n > INT32_MAX || rows > 65535 || k < 1 || k > rq::topk_max_k() || k > n)
+    return RQ_ERR_SHAPE;
+  if (rows > 0 && (!scores || !idx || !vals)) return RQ_ERR_NULL;
+  if (!aligned(scores, 16) || !aligned(idx, 4) || !aligned(vals, 2) || !aligned(workspace, 16)) return RQ_ERR_ALIGN;
+  if (rows == 0) return RQ_OK;
+  const size_t need = rq_topk_workspace_size(rows, n, k);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return RQ_ERR_WORKSPACE;
+  const int dev = check_device();
+  if (dev != RQ_OK) return dev;
+  int2* b0 = need > 0 ? reinterpret_cast<int2*>(workspace) : nullptr;
+  int2* b1 = need > 0 ? reinterpret_cast<int2*>(reinterpret_cast<uint8_t*>(workspace) + need / 2) : nullptr;
+  Hook hook(RQ_KERNEL_TOPK, (hipStream_t)stream);
+  return rq::launch_topk(scores, rows, n, k, idx, vals, b0, b1, (hipStream_t)stream) == hipSuccess ? RQ_OK
+                                                                                                   : RQ_ERR_HIP;
 }
 
 int rq_fp8_moe_grouped_linear(const uint16_t* x, int in_layout, int act, const int32_t* topk_ids,

@@ -138,6 +138,14 @@ hipError_t launch_attention_core(const uint16_t* qkv, int64_t requests, int leng
 int attention_head_dim();
 int attention_max_len();
 
+// Batched top-k of FP16 rows (k <= topk_max_k()): idx [rows][k] int32 and vals [rows][k] FP16
+// in rank order; buf0 / buf1 hold topk_pairs_per_buffer() (key, index) pairs each (unused
+// when a row fits one segment).
+hipError_t launch_topk(const uint16_t* scores, int64_t rows, int64_t n, int k, int32_t* idx, uint16_t* vals,
+                       int2* buf0, int2* buf1, hipStream_t stream);
+int topk_max_k();
+int64_t topk_pairs_per_buffer(int64_t rows, int64_t n, int k);
+
 // Bits of the device error word (the values of the C ABI's RQ_FLAG_*).
 enum : unsigned { kErrExpertId = 1u };
 

@@ -285,6 +285,21 @@ int rq_moe_router_topk(const uint16_t* x, int64_t T, int64_t K, const uint16_t* 
 int rq_attention_core(const uint16_t* qkv, int64_t requests, int length, int heads, int head_dim,
                       uint16_t* out, void* stream);
 
+/* Batched top-k of FP16 candidate rows, for beam search (page "FP8量化在生成式推荐系统OneRec-V2
+ * 中的优化实践", §3.2: a RadixSelect TopK run batched with zero copies; §5.3: TopK results kept
+ * in FP16).  scores [rows][n] FP16.  For each row the k candidates ranked first by score -
+ * larger first in the IEEE total order (-0 below +0), equal scores ranking the lower index
+ * first - go to idx [rows][k] (int32 indices into the row) and vals [rows][k] (their FP16
+ * scores), in rank order.  The result is unique, so it is exact.  NaN scores are outside the
+ * contract.  Limits: 1 <= k <= min(n, 1024), n <= 2^31 - 1, rows <= 65535 (RQ_ERR_SHAPE).
+ * A radix select over the 16-bit score keys in 16384-score segments, one workgroup each;
+ * rows longer than one segment run in stages through the workspace (a segment's top k holds
+ * every member of the row's top k that lies in it).  The workspace (16-byte aligned) must
+ * hold rq_topk_workspace_size bytes (0 when n <= 16384). */
+size_t rq_topk_workspace_size(int64_t rows, int64_t n, int k);
+int rq_topk(const uint16_t* scores, int64_t rows, int64_t n, int k, int32_t* idx, uint16_t* vals,
+            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Kernel-level timing for benchmarks and profilers.  After this call, the next kernel
  * of the given kind that the calling thread enqueues (through any entry point above) is
  * bracketed by hipEventRecord(start_event) just before its launch and
@@ -298,7 +313,8 @@ enum {
   RQ_KERNEL_COMBINE = 2,
   RQ_KERNEL_ROUTER = 3,
   RQ_KERNEL_ATTENTION = 4,
-  RQ_KERNEL_KINDS = 5
+  RQ_KERNEL_TOPK = 5,     /* all kernels of one rq_topk call (every stage) */
+  RQ_KERNEL_KINDS = 6
 };
 int rq_time_next_kernel(int kernel, void* start_event, void* stop_event);
 

@@ -180,3 +180,18 @@ def test_noalloc_validates_on_the_host():
     assert call(0, 24, 16) == RQ_ERR_ALIGN
     assert call(0, 64, 16, act=9) == RQ_ERR_ARG
     assert lib.rq_status_string(lib_mod.RQ_ERR_SCRATCH) == b"request exceeds the static scratch buffer"
+
+
+def test_topk_validates_on_the_host():
+    lib = lib_mod.load()
+    call = lambda rows, n, k, ws=FAKE, nb=1 << 30: lib.rq_topk(FAKE, rows, n, k, FAKE, FAKE, ws, nb, None)  # noqa: E731
+    assert call(4, 100, 0) == RQ_ERR_SHAPE
+    assert call(4, 100, 101) == RQ_ERR_SHAPE
+    assert call(4, 5000, 1025) == RQ_ERR_SHAPE
+    assert call(-1, 100, 5) == RQ_ERR_SHAPE
+    assert call(70000, 100, 5) == RQ_ERR_SHAPE
+    assert call(0, 100, 5) == 0                                   # zero rows: a validated no-op
+    assert call(4, 100000, 16, ws=None, nb=0) == RQ_ERR_WORKSPACE  # two stages need the workspace
+    assert lib.rq_topk_workspace_size(4, 16384, 16) == 0           # one segment: none
+    assert lib.rq_topk_workspace_size(32, 262144, 512) == 2 * 32 * 16 * 512 * 8
+    assert lib.rq_topk_workspace_size(4, 100, 101) == 0

@@ -106,6 +106,17 @@ def zipf_routing(rng, tokens, experts, top_k=2, alpha=1.1, empty_last=True):
 
 # ------------------------------------------------------------------------- workloads
 
+def beam_scores(rng, requests, beams, codes):
+    """Beam-search candidate scores [requests, beams * codes] FP16: each beam's running
+    log-probability (sorted, the best beam first) plus a log-softmax over ``codes`` next
+    semantic-ID codes, as a decoding step of a generative recommender produces them."""
+    running = -np.sort(rng.exponential(3.0, size=(requests, beams)), axis=1)
+    logits = rng.standard_normal((requests, beams, codes)) * 2.0
+    m = logits.max(axis=2, keepdims=True)
+    logp = logits - m - np.log(np.exp(logits - m).sum(axis=2, keepdims=True))
+    return (running[:, :, None] + logp).reshape(requests, beams * codes).astype(np.float16)
+
+
 def _streams(seed, n):
     return [np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(n)]
 
