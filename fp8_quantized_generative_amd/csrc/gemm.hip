@@ -36,9 +36,9 @@
 //   Rows outside the tile and K past the end read as zero through the buffer range check.
 // * Tile order: the hardware hands consecutive workgroup ids to the 8 XCDs in turn; each
 //   XCD's workgroups share a contiguous slice of the logical order, and the logical order
-//   walks groups of 8 M-tiles across all N-tiles, so tiles that share A rows or B columns
+//   walks groups of 4 M-tiles across all N-tiles, so tiles that share A rows or B columns
 //   run on the same XCD at the same time and hit its L2.  In grouped mode the groups never
-//   straddle two experts (an expert's M-tiles are cut into groups of at most 8), so the
+//   straddle two experts (an expert's M-tiles are cut into groups of at most 4), so the
 //   tiles running together read one expert's weights rather than two.
 // * Epilogue: each lane scales its four-column groups (FP32 row and column scales read from
 //   LDS) and rounds them to FP16; column groups are paired across the two 32-lane halves
@@ -64,7 +64,10 @@
 namespace rq {
 namespace {
 
-constexpr int kGroupM = 8;
+// M-tiles per group of the tile walk.  A group's A rows stay in the XCD's L2 while its tiles
+// walk the N-tiles; measured on MI355X (GEMM kernel time, caches flushed, interleaved runs):
+// groups of 4 beat 8 by 1-2% on the MoE and FFN GEMMs, 2 and 16 are slower.
+constexpr int kGroupM = 4;
 constexpr int BK = 64;          // K bytes per slab
 constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset that always reads zero
 
