@@ -67,6 +67,8 @@ def parse():
                     help="print FP8 MFMA counts, MFMA busy fraction and clock per GEMM call from a rocprofv3 "
                          "--pmc database (SQ_INSTS_VALU_MFMA_MOPS_F8 SQ_INSTS_VALU_MFMA_F8 SQ_VALU_MFMA_BUSY_CYCLES "
                          "SQ_INSTS_VALU GRBM_GUI_ACTIVE) and exit")
+    ap.add_argument("--pmc-dump", nargs="+", default=None, metavar="PATH",
+                    help="print every counter of rocprofv3 --pmc databases per GEMM call of the step and exit")
     ap.add_argument("--steps-in-profile", type=int, default=None,
                     help="with --rocprof-summary / --traffic-summary: steps (warmup + timed) the profiled "
                          "command ran")
@@ -75,7 +77,8 @@ def parse():
 
 # Calls of one step, in launch order: (workload, call, kind).  "linear" launches the row
 # quantizer and the GEMM; "moe" the routing-plan kernel (one workgroup at these sizes), the
-# quantizer and the grouped GEMM; "moe_combined" also the weighted combine.
+# quantizer and the grouped GEMM; "moe_combined" (the down call, which reuses the gate/up call's
+# plan) the quantizer, the grouped GEMM and the weighted combine.
 STEP = [
     ("attention", "qkv", "linear"), ("attention", "o", "linear"),
     ("ffn", "gate_up", "linear"), ("ffn", "down", "linear"),
@@ -86,7 +89,7 @@ STEP = [
 ]
 DOMINANT = ("moe", "gate_up")
 KERNELS = {"linear": ["quant", "gemm"], "moe": ["plan", "quant", "gemm"],
-           "moe_combined": ["plan", "quant", "gemm", "combine"]}
+           "moe_combined": ["quant", "gemm", "combine"]}  # the down call reuses the gate/up call's plan
 OUR_KERNELS = ("quant_rows", "gemm_fp8_kernel", "plan_single", "plan_hist", "plan_scan", "plan_scatter",
                "combine_kernel")
 
@@ -163,6 +166,13 @@ class Path:
             wq, ws = rq.quant_weights(dev(w16))
             return wq, ws
 
+        def ffn_workspace(t, e, f, k):
+            # one workspace for both calls of an expert FFN: the down call reuses the routing plan
+            # the gate/up call left at its front
+            size = max(rq.moe_workspace_size(t, 2, e, 2 * f, k, "tokens", "gate_silu", "permuted"),
+                       rq.moe_workspace_size(t, 2, e, k, f, "permuted", "none", "combined"))
+            return torch.empty(size, dtype=torch.uint8, device="cuda")
+
         def qw_gated(w16):
             # gate/up rows interleaved in blocks of 32 (offline, untimed): the gate/up GEMM
             # then writes h = silu(g) * u directly
@@ -183,20 +193,21 @@ class Path:
             self.flops += fl
             return out
 
-        def add_moe(work, label, x, ids, wq, ws, il, act, ol, topk_w=None):
+        def add_moe(work, label, x, ids, wq, ws, il, act, ol, topk_w=None, ws_t=None, plan_ready=False):
             t, top_k = ids.shape
             e, n, k = wq.shape
             r = t * top_k
             n_out = n // 2 if act == "gate_silu" else n
             out = torch.empty((t if ol == "combined" else r, n_out), dtype=torch.float16, device="cuda")
-            ws_t = torch.empty(rq.moe_workspace_size(t, top_k, e, n, k, il, act, ol), dtype=torch.uint8,
-                               device="cuda")
+            if ws_t is None:
+                ws_t = torch.empty(rq.moe_workspace_size(t, top_k, e, n, k, il, act, ol), dtype=torch.uint8,
+                                   device="cuda")
             fl = 2 * r * n * k
             touched = int(torch.unique(ids).numel())  # experts with rows: only their weights are read
             by = x.numel() * 2 + touched * n * k + (t if ol == "combined" else r) * n_out * 2
             self.calls.append((work, label, "moe", fl, by,
                                lambda: rq.moe_grouped_linear(x, ids, wq, ws, il, act, ol, topk_w=topk_w,
-                                                             out=out, workspace=ws_t)))
+                                                             out=out, workspace=ws_t, plan_ready=plan_ready)))
             # the row quantizer reads each input row once and writes one E4M3 row and scale per
             # routed slot
             self.qbytes.append(x.numel() * 2 + r * k + 4 * r)
@@ -272,9 +283,11 @@ class Path:
             wgu, wdn = qw_gated(d["w_gu"]), qw(d["w_dn"])
             ids, tw = dev(d["ids"].astype(np.int32)), dev(d["topk_w"])
             counts = np.bincount(d["ids"].reshape(-1), minlength=32)
-            h = add_moe("moe", "gate_up", dev(d["x"]), ids, *wgu, "tokens", "gate_silu", "permuted")
+            shared = ffn_workspace(16384, 32, 4096, 2048)
+            h = add_moe("moe", "gate_up", dev(d["x"]), ids, *wgu, "tokens", "gate_silu", "permuted", ws_t=shared)
             self.dominant = len(self.calls) - 1
-            add_moe("moe", "down", h, ids, *wdn, "permuted", "none", "combined", topk_w=tw)
+            add_moe("moe", "down", h, ids, *wdn, "permuted", "none", "combined", topk_w=tw, ws_t=shared,
+                    plan_ready=True)
             if variants:
                 # expert weights with one scale per 128 x 128 block
                 x4 = dev(d["x"])
@@ -313,10 +326,11 @@ class Path:
             h = add_linear("layer_small_m", "gate_up", dev(d["x_ffn"]), *qw_gated(d["w_gu"]), act="gate_silu")
             add_linear("layer_small_m", "down", h, *qw(d["w_dn"]))
             ids, tw = dev(d["ids"].astype(np.int32)), dev(d["topk_w"])
+            shared5 = ffn_workspace(512, 32, 4096, 2048)
             h2 = add_moe("layer_small_m", "moe_gate_up", dev(d["x_moe"]), ids, *qw_gated(d["w_gu_moe"]),
-                         "tokens", "gate_silu", "permuted")
+                         "tokens", "gate_silu", "permuted", ws_t=shared5)
             add_moe("layer_small_m", "moe_down", h2, ids, *qw(d["w_dn_moe"]), "permuted", "none",
-                    "combined", topk_w=tw)
+                    "combined", topk_w=tw, ws_t=shared5, plan_ready=True)
             self.config["layer_small_m"] = "512 rows (32 requests x 16 beams); one layer: QKV, O, FFN 8192, MoE 4096"
             del d
         if not hasattr(self, "dominant"):
@@ -664,6 +678,24 @@ def pmc_summary(path, only=None, steps=None):
           "instructions per FP8 MFMA" % (XCDS, SIMDS, XCDS))
 
 
+def pmc_dump(paths, only=None, steps=None):
+    """Every counter of one or more rocprofv3 --pmc databases, averaged per GEMM call of the
+    step (the same dispatch matching as --pmc-summary), with the GEMM's average duration."""
+    for path in paths:
+        src, per = _pmc_db(path)
+        ids = sorted(per)
+        aligned, nsteps = _align_steps([per[d][0] for d in ids], only, steps)
+        groups = {}
+        for idx, label, kind in aligned:
+            if kind == "gemm":
+                groups.setdefault(label, []).append(per[ids[idx]])
+        print("# rocprofv3 --pmc: %s (%d steps matched)" % (path, nsteps))
+        for label, recs in groups.items():
+            print("  %-26s avg_us %.1f" % (label, np.mean([r[1] for r in recs]) / 1e3))
+            for k in sorted(recs[0][2]):
+                print("    %-34s %16.0f" % (k, np.mean([r[2][k] for r in recs])))
+
+
 def source_hash(files):
     """Hash of a kernel's sources: stored traffic counters are valid only for this code."""
     import hashlib
@@ -788,6 +820,9 @@ def main():
         return
     if args.pmc_summary:
         pmc_summary(args.pmc_summary, args.only, args.steps_in_profile)
+        return
+    if args.pmc_dump:
+        pmc_dump(args.pmc_dump, args.only, args.steps_in_profile)
         return
     if args.traffic_summary:
         fetch_dir, write_dir, out = args.traffic_summary

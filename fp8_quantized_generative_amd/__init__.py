@@ -22,6 +22,7 @@ import torch
 
 from . import _lib
 from ._lib import (RQ_ACT_GATE_SILU, RQ_ACT_NONE, RQ_ACT_SILU_MUL, RQ_MOE_IN_PERMUTED, RQ_MOE_IN_TOKENS,  # noqa: F401
+                   RQ_MOE_PLAN_READY,
                    RQ_MOE_OUT_COMBINED, RQ_MOE_OUT_PERMUTED, RQ_WSCALE_BLOCK128, RQ_WSCALE_CHANNEL,
                    RQ_WSCALE_TENSOR, RQ_FP8_E4M3, RQ_FP8_E5M2, RQ_FLAG_EXPERT_ID, DebugOut, RqError)
 
@@ -203,13 +204,15 @@ def linear_noalloc(x, w_q, w_scale, out, act="none", stream=None):
 
 def moe_grouped_linear(x, topk_ids, w_q, w_scale, in_layout="tokens", act="none",
                        out_layout="permuted", topk_w=None, out=None, workspace=None,
-                       debug=False, stream=None, wscale="channel", afmt="e4m3"):
+                       debug=False, stream=None, wscale="channel", afmt="e4m3", plan_ready=False):
     """Expert grouped W8A8 linear.
 
     ``x``: FP16 [T, K*] (tokens) or [T*top_k, K*] (permuted), K* = 2K for ``silu_mul``;
     ``topk_ids``: int32 [T, top_k]; ``w_q``: uint8 [E, N, K]; ``w_scale``: FP32 [E, N] (or the
     ``wscale`` layout with E matrices, see ``quant_weights``);
     ``topk_w``: FP16 [T, top_k] for ``out_layout='combined'``.
+    ``plan_ready``: the ``workspace`` given already holds the routing plan of these ``topk_ids``
+    from an earlier call (permuted input only; see ``RQ_MOE_PLAN_READY``).
     Returns FP16 [T*top_k, N] (permuted) or [T, N] (combined), plus the debug dict when
     ``debug=True``: ``a_q`` / ``a_scale`` hold the GEMM operand, one row per routed slot in
     the permuted order; ``h`` (``silu_mul``) one row per input row.
@@ -241,8 +244,11 @@ def moe_grouped_linear(x, topk_ids, w_q, w_scale, in_layout="tokens", act="none"
     _dev(out, torch.float16, "out")
     _shape(out, out_shape, "out")
     _shape(w_scale, scale_shape((e,), n, k, g), "w_scale")
+    if plan_ready and workspace is None:
+        raise ValueError("plan_ready needs the workspace that holds the plan")
     st = lib.rq_fp8_moe_grouped_linear_ex(
-        _ptr(x), il, a, f, _ptr(topk_ids), _ptr(topk_w), t, top_k, _ptr(w_q), _ptr(w_scale), g, e, n, k,
+        _ptr(x), il | (RQ_MOE_PLAN_READY if plan_ready else 0), a, f, _ptr(topk_ids), _ptr(topk_w), t, top_k,
+        _ptr(w_q), _ptr(w_scale), g, e, n, k,
         _ptr(out), ol, _ptr(ws), ws.numel(), ctypes.byref(dbg_s) if dbg_s is not None else None,
         _stream(x, stream))
     _lib.check("rq_fp8_moe_grouped_linear_ex", st)

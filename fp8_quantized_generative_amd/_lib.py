@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(HERE, "librq_fp8.so")
 RQ_OK = 0
 RQ_ERR_HIP = 6
 RQ_ACT_NONE, RQ_ACT_SILU_MUL, RQ_ACT_GATE_SILU = 0, 1, 2
-RQ_MOE_IN_TOKENS, RQ_MOE_IN_PERMUTED = 0, 1
+RQ_MOE_IN_TOKENS, RQ_MOE_IN_PERMUTED, RQ_MOE_PLAN_READY = 0, 1, 4
 RQ_MOE_OUT_PERMUTED, RQ_MOE_OUT_COMBINED = 0, 1
 RQ_KERNEL_QUANT, RQ_KERNEL_GEMM, RQ_KERNEL_COMBINE, RQ_KERNEL_ROUTER, RQ_KERNEL_ATTENTION, RQ_KERNEL_TOPK = \
     0, 1, 2, 3, 4, 5

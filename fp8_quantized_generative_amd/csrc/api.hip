@@ -63,26 +63,37 @@ struct Carve {
   }
 };
 
+// MoE workspace: the routing plan first, at offsets that depend only on (T, top_k, E), so a
+// later call with the same routing can reuse it from the same workspace (RQ_MOE_PLAN_READY);
+// then the quantized GEMM operand and, for the combined output, the permuted GEMM output.
 struct MoeLayout {
-  size_t a_q, a_scale, offsets, tile_start, tile_table, perm, pos, block_hist, y_perm;
+  size_t offsets, tile_start[2], tile_table[2], perm, pos, block_hist;  // the plan
+  size_t a_q, a_scale, y_perm;
 };
 
-MoeLayout moe_layout(int64_t T, int top_k, int64_t E, int64_t N, int64_t K, int in_layout, int act,
-                     int out_layout) {
-  (void)in_layout;
+constexpr int kPlanTileRows[2] = {rq::kMinTileRows, 256};  // the grouped GEMM's tile heights
+
+MoeLayout moe_layout(int64_t T, int top_k, int64_t E, int64_t N, int64_t K, int act, int out_layout) {
   const int64_t R = T * top_k;
   MoeLayout l;
-  l.a_q = (size_t)(R * K);  // the GEMM operand: one quantized row per routed slot
-  l.a_scale = (size_t)R * sizeof(float);
   l.offsets = (size_t)(E + 1) * sizeof(int32_t);
-  l.tile_start = (size_t)(E + 1) * sizeof(int32_t);
-  l.tile_table = (size_t)rq::grouped_max_mtiles(R, E, rq::kMinTileRows) * 4 * sizeof(int32_t);
+  for (int i = 0; i < 2; ++i) {
+    l.tile_start[i] = (size_t)(E + 1) * sizeof(int32_t);
+    l.tile_table[i] = (size_t)rq::grouped_max_mtiles(R, E, kPlanTileRows[i]) * 4 * sizeof(int32_t);
+  }
   l.perm = (size_t)R * sizeof(int32_t);
   l.pos = (size_t)R * sizeof(int32_t);
   l.block_hist = (size_t)(rq::moe_plan_blocks(R) * E) * sizeof(int32_t);
+  l.a_q = (size_t)(R * K);  // the GEMM operand: one quantized row per routed slot
+  l.a_scale = (size_t)R * sizeof(float);
   const int64_t NO = act == RQ_ACT_GATE_SILU ? N / 2 : N;  // output row length
   l.y_perm = out_layout == RQ_MOE_OUT_COMBINED ? (size_t)(R * NO) * sizeof(uint16_t) : 0;
   return l;
+}
+
+size_t plan_bytes(const MoeLayout& l) {
+  return align_up(l.offsets) + align_up(l.tile_start[0]) + align_up(l.tile_start[1]) + align_up(l.tile_table[0]) +
+         align_up(l.tile_table[1]) + align_up(l.perm) + align_up(l.pos) + align_up(l.block_hist);
 }
 
 // Device scratch of the allocation-free linear (rq_fp8_linear_noalloc): the quantized
@@ -291,10 +302,10 @@ int rq_fp8_linear_noalloc(const uint16_t* x, int64_t M, int64_t K, int act, cons
 
 size_t rq_fp8_moe_workspace_size(int64_t T, int top_k, int64_t E, int64_t N, int64_t K,
                                  int in_layout, int act, int out_layout) {
+  (void)in_layout;
   if (T < 0 || top_k < 1 || E < 1 || N <= 0 || K <= 0) return 0;
-  const MoeLayout l = moe_layout(T, top_k, E, N, K, in_layout, act, out_layout);
-  return align_up(l.a_q) + align_up(l.a_scale) + align_up(l.offsets) + align_up(l.tile_start) +
-         align_up(l.tile_table) + align_up(l.perm) + align_up(l.pos) + align_up(l.block_hist) + align_up(l.y_perm);
+  const MoeLayout l = moe_layout(T, top_k, E, N, K, act, out_layout);
+  return plan_bytes(l) + align_up(l.a_q) + align_up(l.a_scale) + align_up(l.y_perm);
 }
 
 int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act, int a_fmt, const int32_t* topk_ids,
@@ -305,7 +316,12 @@ int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act, int 
   if (act != RQ_ACT_NONE && act != RQ_ACT_SILU_MUL && act != RQ_ACT_GATE_SILU) return RQ_ERR_ARG;
   if (w_gran != RQ_WSCALE_CHANNEL && w_gran != RQ_WSCALE_TENSOR && w_gran != RQ_WSCALE_BLOCK128) return RQ_ERR_ARG;
   if (a_fmt != RQ_FP8_E4M3 && a_fmt != RQ_FP8_E5M2) return RQ_ERR_ARG;
+  // RQ_MOE_PLAN_READY: reuse the plan in the workspace (permuted input only: a token input
+  // would scatter rows through the plan's slot positions)
+  const bool plan_ready = (in_layout & RQ_MOE_PLAN_READY) != 0;
+  in_layout &= ~RQ_MOE_PLAN_READY;
   if (in_layout != RQ_MOE_IN_TOKENS && in_layout != RQ_MOE_IN_PERMUTED) return RQ_ERR_ARG;
+  if (plan_ready && in_layout != RQ_MOE_IN_PERMUTED) return RQ_ERR_ARG;
   if (out_layout != RQ_MOE_OUT_PERMUTED && out_layout != RQ_MOE_OUT_COMBINED) return RQ_ERR_ARG;
   if (T < 0 || K <= 0 || N <= 0 || E < 1 || E > kMaxExperts || top_k < 1 || top_k > E)
     return RQ_ERR_SHAPE;
@@ -332,25 +348,31 @@ int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act, int 
 
   const int64_t R = T * top_k;
   const int64_t rows = in_layout == RQ_MOE_IN_TOKENS ? T : R;
-  const MoeLayout l = moe_layout(T, top_k, E, N, K, in_layout, act, out_layout);
+  const MoeLayout l = moe_layout(T, top_k, E, N, K, act, out_layout);
   Carve c{reinterpret_cast<uint8_t*>(workspace)};
-  uint8_t* aq = c.take<uint8_t>(l.a_q);
-  float* as = c.take<float>(l.a_scale);
   int32_t* offsets = c.take<int32_t>(l.offsets);
-  int32_t* tile_start = c.take<int32_t>(l.tile_start);
-  int32_t* tile_table = c.take<int32_t>(l.tile_table);
+  rq::TileTables tt;
+  for (int i = 0; i < 2; ++i) {
+    tt.rows[i] = kPlanTileRows[i];
+    tt.start[i] = c.take<int32_t>(l.tile_start[i]);
+  }
+  for (int i = 0; i < 2; ++i) tt.table[i] = c.take<int32_t>(l.tile_table[i]);
   int32_t* perm = c.take<int32_t>(l.perm);
   int32_t* pos = c.take<int32_t>(l.pos);
   int32_t* block_hist = c.take<int32_t>(l.block_hist);
+  uint8_t* aq = c.take<uint8_t>(l.a_q);
+  float* as = c.take<float>(l.a_scale);
   uint16_t* y_perm = out_layout == RQ_MOE_OUT_COMBINED ? c.take<uint16_t>(l.y_perm) : y;
   if (dq) aq = dq;
   if (ds) as = ds;
 
   hipStream_t s = (hipStream_t)stream;
   const int kind = rq::pick_grouped(R, E, N);
-  if (rq::launch_moe_plan(topk_ids, T, top_k, E, rq::tile_rows(kind), offsets, tile_start, tile_table,
-                          perm, pos, block_hist, s) != hipSuccess)
+  const int which = rq::tile_rows(kind) == kPlanTileRows[0] ? 0 : 1;
+  if (!plan_ready && rq::launch_moe_plan(topk_ids, T, top_k, E, offsets, tt, perm, pos, block_hist, s) != hipSuccess)
     return RQ_ERR_HIP;
+  int32_t* tile_start = tt.start[which];
+  int32_t* tile_table = tt.table[which];
   {
     Hook hook(RQ_KERNEL_QUANT, s);
     // per-token rows are written to each of the token's permuted slots

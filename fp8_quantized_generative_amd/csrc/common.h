@@ -120,9 +120,17 @@ int pick_grouped(int64_t R, int64_t E, int64_t N);  // tile shape for R routed r
 int tile_rows(int kind);                       // M rows of a tile shape
 int64_t grouped_max_mtiles(int64_t R, int64_t E, int tile_m);
 
-hipError_t launch_moe_plan(const int32_t* ids, int64_t T, int top_k, int64_t E, int tile_m,
-                           int32_t* offsets, int32_t* tile_start, int32_t* tile_table, int32_t* perm,
-                           int32_t* pos, int32_t* block_hist, hipStream_t stream);
+// The M-tile prefix and table of a routing plan for two tile heights (the 64- and the
+// 256-row tiles of the grouped GEMM), so a later call may reuse the plan with either.
+struct TileTables {
+  int rows[2];
+  int32_t* start[2];  // [E + 1]
+  int32_t* table[2];  // [grouped_max_mtiles(R, E, rows)][4]
+};
+
+hipError_t launch_moe_plan(const int32_t* ids, int64_t T, int top_k, int64_t E, int32_t* offsets,
+                           const TileTables& tt, int32_t* perm, int32_t* pos, int32_t* block_hist,
+                           hipStream_t stream);
 int64_t moe_plan_blocks(int64_t R);
 
 // MoE router: FP16 logits of T rows x [K] against E <= 32 gate rows, top_k <= router_max_topk()

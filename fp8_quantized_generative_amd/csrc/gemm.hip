@@ -247,7 +247,7 @@ struct TileInfo {
 // its M-tiles are grouped on their own.
 template <int BM, int BN, bool GROUPED>
 __device__ __forceinline__ TileInfo tile_info(const GemmArgs& p, int L, int m_tiles, int n_tiles,
-                                              int tiles_per_part = 0) {
+                                              int tiles_per_part = 0, int mt_cap = 0) {
   int part = 0;
   if (tiles_per_part > 0) {  // split-K: work item L is part L / tiles of tile L % tiles
     part = L / tiles_per_part;
@@ -267,17 +267,21 @@ __device__ __forceinline__ TileInfo tile_info(const GemmArgs& p, int L, int m_ti
   const int per_group = kGroupM * n_tiles;
   const int group = L / per_group;
   const int first_m = group * kGroupM;
-  const int gm = min(m_tiles - first_m, kGroupM);
+  const int gm = GROUPED ? max(min(m_tiles - first_m, kGroupM), 1) : min(m_tiles - first_m, kGroupM);
   const int in_group = L - group * per_group;
   const int mt = base + first_m + in_group % gm;
   TileInfo t;
   t.part = part;
   t.n0 = (in_group / gm) * BN;
   if (GROUPED) {
-    const int32_t* ent = p.tile_table + 4 * (int64_t)mt;
-    t.expert = load_uniform(ent);
-    t.row_begin = load_uniform(ent + 1);
-    t.row_end = load_uniform(ent + 2);
+    t.n0 = min(max(t.n0, 0), (n_tiles - 1) * BN);
+    // the plan may come from an earlier call (RQ_MOE_PLAN_READY): every value is clamped into
+    // range, so even a plan that does not belong to these ids cannot move an access outside the
+    // operands (it only gives wrong rows); for the plan the call builds itself these are no-ops
+    const int32_t* ent = p.tile_table + 4 * (int64_t)min(max(mt, 0), mt_cap - 1);
+    t.expert = min(max(load_uniform(ent), 0), p.E - 1);
+    t.row_begin = min(max(load_uniform(ent + 1), 0), p.a_rows);
+    t.row_end = min(max(load_uniform(ent + 2), t.row_begin), min(t.row_begin + BM, p.a_rows));
   } else {
     t.expert = 0;
     t.row_begin = mt * BM;
@@ -322,7 +326,9 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
   // ---- this workgroup's tiles: logical tiles first, first + stride, ... below last.
   // Workgroup ids go round-robin over the 8 XCDs; each XCD's workgroups share a contiguous
   // slice of the logical order.  In grouped mode the real M-tile count is on the device.
-  if (GROUPED) m_tiles = load_uniform(p.tile_start + p.E);
+  // grouped: the real M-tile count is on the device, at most the host's bound m_tiles
+  const int mt_cap = m_tiles;
+  if (GROUPED) m_tiles = min(max(load_uniform(p.tile_start + p.E), 0), mt_cap);
   const int tiles_pp = SPLITK ? m_tiles * n_tiles : 0;  // split-K: tiles per K part
   const int total = m_tiles * n_tiles * (SPLITK ? p.splits : 1);
   int first, stride, last;
@@ -447,7 +453,7 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
   uint4 fa[2 * C::TI], fb0[2 * C::TJ], fb1[2 * C::TJ];
 
   // ---- current and next tile
-  TileInfo cur = tile_info<C::BM, C::BN, GROUPED>(p, first, m_tiles, n_tiles, tiles_pp);
+  TileInfo cur = tile_info<C::BM, C::BN, GROUPED>(p, first, m_tiles, n_tiles, tiles_pp, mt_cap);
   TileDesc2 dc = tile_descs<C::BN>(p, cur, SPLITK ? KL : 0);
   int rb = 0;  // ring buffer that holds slab 0 of the current tile
 
@@ -486,7 +492,7 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
     TileInfo nxt = cur;
     TileDesc2 dn = dc;
     if (has_next) {
-      nxt = tile_info<C::BM, C::BN, GROUPED>(p, L + stride, m_tiles, n_tiles, tiles_pp);
+      nxt = tile_info<C::BM, C::BN, GROUPED>(p, L + stride, m_tiles, n_tiles, tiles_pp, mt_cap);
       dn = tile_descs<C::BN>(p, nxt, SPLITK ? KL : 0);
     }
     // With K of at least S slabs the last S steps fetch slabs 0..S-1 of the next tile.

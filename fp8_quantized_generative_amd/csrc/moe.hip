@@ -89,15 +89,48 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_sums, int& 
   return wave_sums[wave] + incl - v;
 }
 
+// M-tile prefix (tile_start [E + 1]) and table (tile_table, one {expert, first row, end row,
+// 0} entry per M-tile) for tiles of tile_m rows.  All lanes call it; lane e < E passes its
+// expert's row count; s_off holds every expert's first row, s_tstart is LDS scratch [E + 1].
+__device__ void tile_tables(int count, int E, int total_rows, int tile_m, int32_t* __restrict__ tile_start,
+                            int32_t* __restrict__ tile_table, int* s_tstart, const int* s_off, int* wave_sums) {
+  const int tid = threadIdx.x;
+  int total_tiles;
+  const int tstart = block_exclusive_scan(tid < E ? (count + tile_m - 1) / tile_m : 0, wave_sums, total_tiles);
+  if (tid < E) {
+    tile_start[tid] = tstart;
+    s_tstart[tid] = tstart;
+  }
+  if (tid == 0) {
+    tile_start[E] = total_tiles;
+    s_tstart[E] = total_tiles;
+  }
+  __syncthreads();
+  // the expert of tile t is found by binary search over the tile prefix
+  for (int t = tid; t < total_tiles; t += kPlanThreads) {
+    int lo = 0, hi = E - 1;  // largest x with s_tstart[x] <= t
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_tstart[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int first = s_off[lo] + (t - s_tstart[lo]) * tile_m;
+    const int end_e = lo + 1 < E ? s_off[lo + 1] : total_rows;
+    int32_t* ent = tile_table + 4 * (int64_t)t;
+    ent[0] = lo;
+    ent[1] = first;
+    ent[2] = first + tile_m < end_e ? first + tile_m : end_e;
+    ent[3] = 0;
+  }
+  __syncthreads();  // s_tstart is reused by the next call
+}
+
 // One workgroup turns the [nb][E] block histograms into per-expert offsets and M-tile
 // prefixes, the M-tile table, and per-(block, expert) base rows.  The blocks are split into
 // G contiguous segments (G groups of E threads, consecutive threads on consecutive experts
 // so every load is coalesced): each group sums its segment, the segment sums are scanned
 // per expert in LDS, and each group then rewrites its segment with running base rows.
 __global__ __launch_bounds__(kPlanThreads) void plan_scan(int32_t* __restrict__ block_hist, int nblocks, int E,
-                                                          int tile_m, int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ tile_start,
-                                                          int32_t* __restrict__ tile_table) {
+                                                          int32_t* __restrict__ offsets, TileTables tt) {
   __shared__ int wave_sums[kPlanWaves + 1];
   __shared__ int seg[kPlanThreads];        // [G][E] segment sums, then their exclusive scans
   __shared__ int s_tstart[kPlanThreads + 1];
@@ -123,23 +156,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_scan(int32_t* __restrict__ 
     }
   }
   __syncthreads();
-  int total_rows, total_tiles;
+  int total_rows;
   const int off = block_exclusive_scan(tid < E ? count : 0, wave_sums, total_rows);
-  __syncthreads();
-  const int tiles = tid < E ? (count + tile_m - 1) / tile_m : 0;
-  const int tstart = block_exclusive_scan(tiles, wave_sums, total_tiles);
   if (tid < E) {
     offsets[tid] = off;
-    tile_start[tid] = tstart;
-    s_tstart[tid] = tstart;
     s_off[tid] = off;
   }
-  if (tid == 0) {
-    offsets[E] = total_rows;
-    tile_start[E] = total_tiles;
-    s_tstart[E] = total_tiles;
-  }
+  if (tid == 0) offsets[E] = total_rows;
   __syncthreads();
+  // M-tile tables for both tile heights, so a later call may reuse the plan with either
+  tile_tables(count, E, total_rows, tt.rows[0], tt.start[0], tt.table[0], s_tstart, s_off, wave_sums);
+  tile_tables(count, E, total_rows, tt.rows[1], tt.start[1], tt.table[1], s_tstart, s_off, wave_sums);
   // base row of (block b, expert e) = offset of e + rows of e in earlier blocks
   if (active) {
     int run = s_off[e] + seg[tid];
@@ -148,23 +175,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_scan(int32_t* __restrict__ 
       block_hist[(int64_t)b * E + e] = run;
       run += c;
     }
-  }
-  // one {expert, first row, end row} entry per M-tile, so a GEMM tile finds its rows with
-  // one load; the expert of tile t is found by binary search over the tile prefix
-  for (int t = tid; t < total_tiles; t += kPlanThreads) {
-    int lo = 0, hi = E - 1;  // largest x with s_tstart[x] <= t
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_tstart[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    const int ex = lo;
-    const int first = s_off[ex] + (t - s_tstart[ex]) * tile_m;
-    const int end_e = ex + 1 < E ? s_off[ex + 1] : total_rows;
-    int32_t* ent = tile_table + 4 * (int64_t)t;
-    ent[0] = ex;
-    ent[1] = first;
-    ent[2] = first + tile_m < end_e ? first + tile_m : end_e;
-    ent[3] = 0;
   }
 }
 
@@ -215,9 +225,7 @@ constexpr int64_t kSinglePlanMaxExperts = 256;  // keeps its LDS (19 E + 1 words
 
 template <int IPT>
 __global__ __launch_bounds__(kPlanThreads) void plan_single(const int32_t* __restrict__ ids, int R, int E,
-                                                            int nbits, int tile_m, int32_t* __restrict__ offsets,
-                                                            int32_t* __restrict__ tile_start,
-                                                            int32_t* __restrict__ tile_table,
+                                                            int nbits, int32_t* __restrict__ offsets, TileTables tt,
                                                             int32_t* __restrict__ perm, int32_t* __restrict__ pos) {
   extern __shared__ int32_t sh[];
   int32_t* base = sh;                  // [E] rows per expert, then the next free row of each expert
@@ -245,39 +253,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_single(const int32_t* __res
     }
   }
   __syncthreads();
-  // offsets and M-tile prefix (E <= kPlanThreads: one expert per thread)
+  // offsets (E <= kPlanThreads: one expert per thread), then the M-tile tables of both heights
   const int count = tid < E ? base[tid] : 0;
-  int total_rows, total_tiles;
+  int total_rows;
   const int off = block_exclusive_scan(count, wave_sums, total_rows);
-  __syncthreads();
-  const int tstart = block_exclusive_scan(tid < E ? (count + tile_m - 1) / tile_m : 0, wave_sums, total_tiles);
   if (tid < E) {
     offsets[tid] = off;
-    tile_start[tid] = tstart;
     s_off[tid] = off;
-    s_tstart[tid] = tstart;
     base[tid] = off;
   }
-  if (tid == 0) {
-    offsets[E] = total_rows;
-    tile_start[E] = total_tiles;
-    s_tstart[E] = total_tiles;
-  }
+  if (tid == 0) offsets[E] = total_rows;
   __syncthreads();
-  for (int t = tid; t < total_tiles; t += kPlanThreads) {
-    int lo = 0, hi = E - 1;  // largest x with s_tstart[x] <= t
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_tstart[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    const int first = s_off[lo] + (t - s_tstart[lo]) * tile_m;
-    const int end_e = lo + 1 < E ? s_off[lo + 1] : total_rows;
-    int32_t* ent = tile_table + 4 * (int64_t)t;
-    ent[0] = lo;
-    ent[1] = first;
-    ent[2] = first + tile_m < end_e ? first + tile_m : end_e;
-    ent[3] = 0;
-  }
+  tile_tables(count, E, total_rows, tt.rows[0], tt.start[0], tt.table[0], s_tstart, s_off, wave_sums);
+  tile_tables(count, E, total_rows, tt.rows[1], tt.start[1], tt.table[1], s_tstart, s_off, wave_sums);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int c = 0; c < IPT; ++c) {
@@ -317,7 +305,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_single(const int32_t* __res
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y_perm,
                                                       const int32_t* __restrict__ pos,
                                                       const uint16_t* __restrict__ topk_w, int top_k,
-                                                      int64_t N, uint16_t* __restrict__ out) {
+                                                      int64_t N, int64_t R, uint16_t* __restrict__ out) {
   const int64_t t = blockIdx.x;
   const int64_t nchunk = N / 8;
   for (int64_t c = threadIdx.x; c < nchunk; c += blockDim.x) {
@@ -325,7 +313,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     for (int k = 0; k < top_k; ++k) {
       const int64_t slot = t * top_k + k;
       const float w = half_bits_to_float(topk_w[slot]);
-      const uint4 v = ld_global_16(y_perm + (int64_t)pos[slot] * N + 8 * c);
+      const int64_t row = min(max((int64_t)pos[slot], (int64_t)0), R - 1);  // a reused plan is clamped
+      const uint4 v = ld_global_16(y_perm + row * N + 8 * c);
       const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -346,9 +335,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 
 int64_t moe_plan_blocks(int64_t R) { return (R + kPlanThreads - 1) / kPlanThreads; }
 
-hipError_t launch_moe_plan(const int32_t* ids, int64_t T, int top_k, int64_t E, int tile_m,
-                           int32_t* offsets, int32_t* tile_start, int32_t* tile_table, int32_t* perm,
-                           int32_t* pos, int32_t* block_hist, hipStream_t stream) {
+hipError_t launch_moe_plan(const int32_t* ids, int64_t T, int top_k, int64_t E, int32_t* offsets,
+                           const TileTables& tt, int32_t* perm, int32_t* pos, int32_t* block_hist,
+                           hipStream_t stream) {
   const int64_t R = T * top_k;
   const int nb = (int)moe_plan_blocks(R);
   const int e = (int)E;
@@ -358,10 +347,10 @@ hipError_t launch_moe_plan(const int32_t* ids, int64_t T, int top_k, int64_t E, 
     const size_t lds = (size_t)(3 * e + 1 + kPlanWaves * e) * sizeof(int32_t);
     const dim3 g1(1), blk(kPlanThreads);
     const int r = (int)R, per = (int)((R + kPlanThreads - 1) / kPlanThreads);  // ids per thread
-    if (per <= 1) plan_single<1><<<g1, blk, lds, stream>>>(ids, r, e, nbits, tile_m, offsets, tile_start, tile_table, perm, pos);
-    else if (per <= 4) plan_single<4><<<g1, blk, lds, stream>>>(ids, r, e, nbits, tile_m, offsets, tile_start, tile_table, perm, pos);
-    else if (per <= 8) plan_single<8><<<g1, blk, lds, stream>>>(ids, r, e, nbits, tile_m, offsets, tile_start, tile_table, perm, pos);
-    else plan_single<32><<<g1, blk, lds, stream>>>(ids, r, e, nbits, tile_m, offsets, tile_start, tile_table, perm, pos);
+    if (per <= 1) plan_single<1><<<g1, blk, lds, stream>>>(ids, r, e, nbits, offsets, tt, perm, pos);
+    else if (per <= 4) plan_single<4><<<g1, blk, lds, stream>>>(ids, r, e, nbits, offsets, tt, perm, pos);
+    else if (per <= 8) plan_single<8><<<g1, blk, lds, stream>>>(ids, r, e, nbits, offsets, tt, perm, pos);
+    else plan_single<32><<<g1, blk, lds, stream>>>(ids, r, e, nbits, offsets, tt, perm, pos);
     return hipGetLastError();
   }
   if (nb > 0) {
@@ -369,8 +358,7 @@ hipError_t launch_moe_plan(const int32_t* ids, int64_t T, int top_k, int64_t E, 
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  plan_scan<<<dim3(1), dim3(kPlanThreads), 0, stream>>>(block_hist, nb, e, tile_m, offsets, tile_start,
-                                                        tile_table);
+  plan_scan<<<dim3(1), dim3(kPlanThreads), 0, stream>>>(block_hist, nb, e, offsets, tt);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nb == 0) return err;
   plan_scatter<<<dim3(nb), dim3(kPlanThreads), kPlanWaves * e * sizeof(int32_t), stream>>>(
@@ -390,7 +378,7 @@ hipError_t read_error_flags(unsigned int* flags, bool clear) {
 hipError_t launch_moe_combine(const uint16_t* y_perm, const int32_t* pos, const uint16_t* topk_w,
                               int64_t T, int top_k, int64_t N, uint16_t* out, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  combine_kernel<<<dim3((unsigned)T), dim3(256), 0, stream>>>(y_perm, pos, topk_w, top_k, N, out);
+  combine_kernel<<<dim3((unsigned)T), dim3(256), 0, stream>>>(y_perm, pos, topk_w, top_k, N, T * top_k, out);
   return hipGetLastError();
 }
 

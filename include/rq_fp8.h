@@ -81,8 +81,16 @@ enum { RQ_ACT_NONE = 0, RQ_ACT_SILU_MUL = 1, RQ_ACT_GATE_SILU = 2 };
  * N must be a multiple of 64 (RQ_ERR_ALIGN otherwise). */
 
 /* MoE input rows: one per token (quantized once, before dispatch) or one per routed
- * slot in the canonical permuted order (see rq_fp8_moe_grouped_linear). */
-enum { RQ_MOE_IN_TOKENS = 0, RQ_MOE_IN_PERMUTED = 1 };
+ * slot in the canonical permuted order (see rq_fp8_moe_grouped_linear).
+ * RQ_MOE_PLAN_READY, OR'ed into RQ_MOE_IN_PERMUTED, skips building the routing plan: the
+ * workspace already holds the plan of these same topk_ids (T, top_k, E), written by an
+ * earlier call with the same workspace pointer on the same stream - the usual case being the
+ * down-projection call of an expert FFN after its gate/up call.  The plan sits at the front
+ * of the workspace at offsets that depend only on (T, top_k, E), so pass the larger of the
+ * two calls' workspace sizes to both.  A plan that does not belong to the ids gives wrong
+ * rows but no out-of-bounds access (every plan value is clamped where it is used).
+ * RQ_ERR_ARG with RQ_MOE_IN_TOKENS. */
+enum { RQ_MOE_IN_TOKENS = 0, RQ_MOE_IN_PERMUTED = 1, RQ_MOE_PLAN_READY = 4 };
 
 /* MoE output rows: one per routed slot in the canonical permuted order, or one per
  * token after the routing-weighted combine. */

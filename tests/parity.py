@@ -6,7 +6,8 @@ few GB at the full workload sizes.  The chains run exactly as the benchmark runs
 * dense FFN: the gate/up linear on interleaved weights writes h = silu(g) * u from its
   epilogue (``act='gate_silu'``), the down linear quantizes h per token;
 * expert FFN: the grouped gate/up call (TOKENS, GATE_SILU, PERMUTED) and the grouped down
-  call (PERMUTED, NONE, COMBINED).
+  call (PERMUTED, NONE, COMBINED) on the same workspace, reusing the gate/up call's routing
+  plan.
 
 Each gated call is also compared bit for bit with the unfused formulation (plain gate/up
 output, then the SiLU*up input transform of the down call), whose intermediate the oracle
@@ -144,7 +145,11 @@ def moe_ffn_gated(rq, x16, ids, topk_w, w_gu16, w_dn16, label):
     order = torch.from_numpy(ffn.gate_up_order(f)).cuda()
     wgi_q, wgi_s = rq.quant_weights(dev(rq.interleave_gate_up(w_gu16)))
     assert torch.equal(wgi_q, wgu_q[:, order]) and torch.equal(wgi_s, wgu_s[:, order])
-    h = rq.moe_grouped_linear(x, ids_d, wgi_q, wgi_s, "tokens", "gate_silu", "permuted")
+    # as timed: one workspace for both calls, the down call reusing the gate/up call's plan
+    shared = torch.empty(max(rq.moe_workspace_size(t, top_k, e, f2, k, "tokens", "gate_silu", "permuted"),
+                             rq.moe_workspace_size(t, top_k, e, k, f, "permuted", "none", "combined")),
+                         dtype=torch.uint8, device="cuda")
+    h = rq.moe_grouped_linear(x, ids_d, wgi_q, wgi_s, "tokens", "gate_silu", "permuted", workspace=shared)
     case(label + ": expert down, unfused and gated")
     wdn_q, wdn_s = rq.quant_weights(dev(w_dn16))
     out_u, dbg_u = rq.moe_grouped_linear(gu, ids_d, wdn_q, wdn_s, "permuted", "silu_mul", "combined",
@@ -153,7 +158,7 @@ def moe_ffn_gated(rq, x16, ids, topk_w, w_gu16, w_dn16, label):
     assert np.array_equal(h_h.view(np.uint16), host(dbg_u["h"]).view(np.uint16)), "gated h != unfused h"
     assert ulp_diff16(h_h, ffn.silu_mul(gu_h, f)).max() <= 1
     out, dbg2 = rq.moe_grouped_linear(h, ids_d, wdn_q, wdn_s, "permuted", "none", "combined",
-                                      topk_w=tw, debug=True)
+                                      topk_w=tw, debug=True, workspace=shared, plan_ready=True)
     out_h = host(out)
     assert np.array_equal(out_h.view(np.uint16), host(out_u).view(np.uint16)), "gated FFN != unfused FFN"
     wdn_qh, wdn_sh = host(wdn_q), host(wdn_s)

@@ -195,3 +195,17 @@ def test_topk_validates_on_the_host():
     assert lib.rq_topk_workspace_size(4, 16384, 16) == 0           # one segment: none
     assert lib.rq_topk_workspace_size(32, 262144, 512) == 2 * 32 * 16 * 512 * 8
     assert lib.rq_topk_workspace_size(4, 100, 101) == 0
+
+
+def test_plan_ready_only_with_permuted_input():
+    lib = lib_mod.load()
+    ready = lib_mod.RQ_MOE_PLAN_READY
+    call = lambda il, T: lib.rq_fp8_moe_grouped_linear(FAKE, il, 0, FAKE, FAKE, T, 2, FAKE, FAKE, 8, 64, 64,  # noqa: E731
+                                                       FAKE, 0, FAKE, 1 << 30, None, None)
+    assert call(0 | ready, 4) == RQ_ERR_ARG          # token input cannot reuse a plan
+    assert call(1 | ready, 0) == 0                   # permuted input: a validated no-op at T = 0
+    assert call(2 | ready, 0) == RQ_ERR_ARG          # unknown layout bits stay errors
+    # the plan sits first at offsets fixed by (T, top_k, E): the larger call's workspace serves both
+    a = lib.rq_fp8_moe_workspace_size(16384, 2, 32, 8192, 2048, 0, 2, 0)
+    b = lib.rq_fp8_moe_workspace_size(16384, 2, 32, 2048, 4096, 1, 0, 1)
+    assert a > 0 and b > 0

@@ -19,10 +19,11 @@ def _names(only=None, steps=2, prefix=("quant_rows_regs<4, false>", "at::native:
 
 def test_step_table_matches_workloads():
     seq = bench.step_dispatches(None)
-    # 8 linears x 2 kernels, 2 uncombined MoE calls x 3, 2 combined x 4
-    assert len(seq) == 8 * 2 + 2 * 3 + 2 * 4
-    assert ("moe gate_up", "gemm") in seq
-    assert len(bench.step_dispatches("moe")) == 7
+    # 8 linears x 2 kernels, 2 gate/up MoE calls x 3 (plan, quantizer, GEMM), 2 down calls x 3
+    # (they reuse the plan: quantizer, GEMM, combine)
+    assert len(seq) == 8 * 2 + 2 * 3 + 2 * 3
+    assert ("moe gate_up", "gemm") in seq and ("moe down", "plan") not in seq
+    assert len(bench.step_dispatches("moe")) == 6
 
 
 def test_align_finds_every_step_and_labels():

@@ -171,3 +171,29 @@ def test_gated_expert_ffn(monkeypatch, tile, t, k, f, e):
     assert np.array_equal(host(h).view(np.uint16), host(dbg["h"]).view(np.uint16))
     out = rq.moe_grouped_linear(h, ids, wdn_q, wdn_s, "permuted", "none", "combined", topk_w=tw)
     assert np.array_equal(host(out).view(np.uint16), host(out_plain).view(np.uint16))
+
+
+@pytest.mark.parametrize("t,k,f,e", [(512, 2048, 4096, 32), (600, 320, 160, 6), (3000, 256, 128, 8)])
+def test_plan_reuse_equals_fresh_plan(t, k, f, e):
+    """The down call with RQ_MOE_PLAN_READY on the gate/up call's workspace gives the bytes of a
+    down call that builds its own plan (the 512-token case: gate/up on 64-row tiles, down on
+    256-row tiles, so the reused plan serves the other tile height)."""
+    rq = require_gpu()
+    case("moe plan reuse t=%d k=%d f=%d e=%d" % (t, k, f, e))
+    d = workloads.make(4, t=t, k=k, f=f, e=e)
+    ids, tw, x = dev(d["ids"].astype(np.int32)), dev(d["topk_w"]), dev(d["x"])
+    wgu = rq.quant_weights(dev(rq.interleave_gate_up(d["w_gu"])))
+    wdn = rq.quant_weights(dev(d["w_dn"]))
+    size = max(rq.moe_workspace_size(t, 2, e, 2 * f, k, "tokens", "gate_silu", "permuted"),
+               rq.moe_workspace_size(t, 2, e, k, f, "permuted", "none", "combined"))
+    shared = torch.empty(size, dtype=torch.uint8, device="cuda")
+    h = rq.moe_grouped_linear(x, ids, *wgu, "tokens", "gate_silu", "permuted", workspace=shared)
+    reused = host(rq.moe_grouped_linear(h, ids, *wdn, "permuted", "none", "combined", topk_w=tw,
+                                        workspace=shared, plan_ready=True))
+    fresh = host(rq.moe_grouped_linear(h, ids, *wdn, "permuted", "none", "combined", topk_w=tw))
+    assert np.array_equal(reused.view(np.uint16), fresh.view(np.uint16))
+    # and the permuted output too (the GEMM's tile table alone)
+    yp_r = host(rq.moe_grouped_linear(h, ids, *wdn, "permuted", "none", "permuted", workspace=shared,
+                                      plan_ready=True))
+    yp_f = host(rq.moe_grouped_linear(h, ids, *wdn, "permuted", "none", "permuted"))
+    assert np.array_equal(yp_r.view(np.uint16), yp_f.view(np.uint16))
