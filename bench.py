@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--kernel-stats", default=None, metavar="PATH",
                     help="print this library's kernels from a rocprofv3 --stats output (*_kernel_stats.csv, or a "
                          "directory holding one): calls and average duration per kernel instantiation, and exit")
+    ap.add_argument("--wlayout", default="slabs", choices=["slabs", "rows"],
+                    help="byte layout of the quantized weights, chosen offline: the slab layout of "
+                         "rq_fp8_pack_weights (default) or the plain [N][K] rows")
     ap.add_argument("--only", default=None,
                     help="comma list of attention,ffn,moe,layer_small_m to restrict the step (profiling)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0, metavar="MB",
@@ -147,7 +150,7 @@ class Hip:
 class Path:
     """Device-resident inputs, quantized weights, outputs and workspaces of one step."""
 
-    def __init__(self, rq, torch, only=None, variants=True):
+    def __init__(self, rq, torch, only=None, variants=True, wlayout="slabs"):
         import workloads
         self.rq, self.torch = rq, torch
         dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
@@ -162,8 +165,13 @@ class Path:
         self.flops = 0
         want = set(only.split(",")) if only else {"attention", "ffn", "moe", "layer_small_m"}
 
-        def qw(w16):
-            wq, ws = rq.quant_weights(dev(w16))
+        self.wlayout = wlayout
+
+        def qw(w16, wscale="channel"):
+            # offline (untimed): quantize, then repack into the layout the step uses
+            wq, ws = rq.quant_weights(dev(w16), wscale=wscale)
+            if wlayout == "slabs":
+                wq = rq.pack_weights(wq)
             return wq, ws
 
         def ffn_workspace(t, e, f, k):
@@ -187,7 +195,7 @@ class Path:
             # bytes that must cross HBM at least once: activations in, weights, output
             by = x.numel() * 2 + wq.numel() + out.numel() * 2
             self.calls.append((work, label, "linear", fl, by,
-                               lambda: rq.linear(x, wq, ws, act=act, out=out, workspace=ws_t)))
+                               lambda: rq.linear(x, wq, ws, act=act, out=out, workspace=ws_t, wlayout=wlayout)))
             # the row quantizer: FP16 rows in, E4M3 rows and FP32 scales out
             self.qbytes.append(x.numel() * 2 + m * k + 4 * m)
             self.flops += fl
@@ -207,7 +215,8 @@ class Path:
             by = x.numel() * 2 + touched * n * k + (t if ol == "combined" else r) * n_out * 2
             self.calls.append((work, label, "moe", fl, by,
                                lambda: rq.moe_grouped_linear(x, ids, wq, ws, il, act, ol, topk_w=topk_w,
-                                                             out=out, workspace=ws_t, plan_ready=plan_ready)))
+                                                             out=out, workspace=ws_t, plan_ready=plan_ready,
+                                                             wlayout=wlayout)))
             # the row quantizer reads each input row once and writes one E4M3 row and scale per
             # routed slot
             self.qbytes.append(x.numel() * 2 + r * k + 4 * r)
@@ -221,7 +230,7 @@ class Path:
         x1 = dev(d1["x"])
         y1 = torch.empty((64, 512), dtype=torch.float16, device="cuda")
         ws1 = torch.empty(rq.linear_workspace_size(64, 512, n=512), dtype=torch.uint8, device="cuda")
-        self.c1 = (2 * 64 * 512 * 512, lambda: rq.linear(x1, *w1, out=y1, workspace=ws1))
+        self.c1 = (2 * 64 * 512 * 512, lambda: rq.linear(x1, *w1, out=y1, workspace=ws1, wlayout=wlayout))
         if variants:
             # beam top-k: 32 requests x (16 beams | 512 beams) x 512 codes, keep 16 | 512
             for beams, keep in ((16, 16), (512, 512)):
@@ -257,8 +266,8 @@ class Path:
             if variants:
                 # the dense FFN with one scale per weight tensor
                 x3 = dev(d["x"])
-                tgu = rq.quant_weights(dev(rq.interleave_gate_up(d["w_gu"])), wscale="tensor")
-                tdn = rq.quant_weights(dev(d["w_dn"]), wscale="tensor")
+                tgu = qw(rq.interleave_gate_up(d["w_gu"]), wscale="tensor")
+                tdn = qw(d["w_dn"], wscale="tensor")
                 h_t = torch.empty_like(h)
                 y_t = torch.empty((4096, 2048), dtype=torch.float16, device="cuda")
                 ws_gu = torch.empty(rq.linear_workspace_size(4096, 2048), dtype=torch.uint8, device="cuda")
@@ -266,17 +275,19 @@ class Path:
                 n0 = len(self.calls)
                 self.variants.append(("ffn", "gate_up", "tensor", self.calls[n0 - 2][3], n0 - 2,
                                       lambda x3=x3, tgu=tgu, h_t=h_t, ws_gu=ws_gu: rq.linear(
-                                          x3, *tgu, act="gate_silu", out=h_t, workspace=ws_gu, wscale="tensor")))
+                                          x3, *tgu, act="gate_silu", out=h_t, workspace=ws_gu, wscale="tensor",
+                                          wlayout=wlayout)))
                 self.variants.append(("ffn", "down", "tensor", self.calls[n0 - 1][3], n0 - 1,
                                       lambda h_t=h_t, tdn=tdn, y_t=y_t, ws_dn=ws_dn: rq.linear(
-                                          h_t, *tdn, out=y_t, workspace=ws_dn, wscale="tensor")))
+                                          h_t, *tdn, out=y_t, workspace=ws_dn, wscale="tensor", wlayout=wlayout)))
                 # the dense FFN with E5M2 activations (per-channel E4M3 weights)
                 self.variants.append(("ffn", "gate_up", "e5m2 activations", self.calls[n0 - 2][3], n0 - 2,
                                       lambda x3=x3, w=wgu, h_t=h_t, ws_gu=ws_gu: rq.linear(
-                                          x3, *w, act="gate_silu", out=h_t, workspace=ws_gu, afmt="e5m2")))
+                                          x3, *w, act="gate_silu", out=h_t, workspace=ws_gu, afmt="e5m2",
+                                          wlayout=wlayout)))
                 self.variants.append(("ffn", "down", "e5m2 activations", self.calls[n0 - 1][3], n0 - 1,
                                       lambda h_t=h_t, w=wdn, y_t=y_t, ws_dn=ws_dn: rq.linear(
-                                          h_t, *w, out=y_t, workspace=ws_dn, afmt="e5m2")))
+                                          h_t, *w, out=y_t, workspace=ws_dn, afmt="e5m2", wlayout=wlayout)))
             self.config["ffn"] = "4096 tokens x 2048; gate/up 2x8192, down K=8192"
         if "moe" in want:
             d = workloads.make(4)
@@ -291,8 +302,8 @@ class Path:
             if variants:
                 # expert weights with one scale per 128 x 128 block
                 x4 = dev(d["x"])
-                bgu = rq.quant_weights(dev(rq.interleave_gate_up(d["w_gu"])), wscale="block128")
-                bdn = rq.quant_weights(dev(d["w_dn"]), wscale="block128")
+                bgu = qw(rq.interleave_gate_up(d["w_gu"]), wscale="block128")
+                bdn = qw(d["w_dn"], wscale="block128")
                 h_b = torch.empty_like(h)
                 y_b = torch.empty((16384, 2048), dtype=torch.float16, device="cuda")
                 ws_gu = torch.empty(rq.moe_workspace_size(16384, 2, 32, 8192, 2048, "tokens", "gate_silu", "permuted"),
@@ -310,11 +321,12 @@ class Path:
                 self.variants.append(("moe", "gate_up", "block128", self.calls[n0 - 2][3], n0 - 2,
                                       lambda x4=x4, ids=ids, bgu=bgu, h_b=h_b, ws_gu=ws_gu: rq.moe_grouped_linear(
                                           x4, ids, *bgu, "tokens", "gate_silu", "permuted", out=h_b, workspace=ws_gu,
-                                          wscale="block128")))
+                                          wscale="block128", wlayout=wlayout)))
                 self.variants.append(("moe", "down", "block128", self.calls[n0 - 1][3], n0 - 1,
                                       lambda h_b=h_b, ids=ids, bdn=bdn, tw=tw, y_b=y_b, ws_dn=ws_dn:
                                       rq.moe_grouped_linear(h_b, ids, *bdn, "permuted", "none", "combined", topk_w=tw,
-                                                            out=y_b, workspace=ws_dn, wscale="block128")))
+                                                            out=y_b, workspace=ws_dn, wscale="block128",
+                                                            wlayout=wlayout)))
             self.config["moe"] = ("16384 tokens x 2048; top-2 of 32 experts (Zipf 1.1; max %d, min nonzero %d, "
                                   "%d empty rows of 32768); gate/up 2x4096, down K=4096"
                                   % (counts.max(), counts[counts > 0].min(), int((counts == 0).sum())))
@@ -843,7 +855,7 @@ def main():
     torch.cuda.set_device(0)
     hip = Hip()
     print("[bench] building inputs", file=sys.stderr, flush=True)
-    path = Path(rq, torch, args.only, variants=not args.no_variants)
+    path = Path(rq, torch, args.only, variants=not args.no_variants, wlayout=args.wlayout)
     print("[bench] %d calls per step, %.1f GFLOP" % (len(path.calls), path.flops / 1e9), file=sys.stderr, flush=True)
 
     for _ in range(args.warmup):
@@ -901,7 +913,9 @@ def main():
         "data": "synthetic",
         "frac_fp8_peak": round(value / FP8_PEAK_TFLOPS, 4),
         "config": {"workload": "+".join(path.config) + " (full-size W8A8 FP8 linears, one step each)",
-                   **path.config, "gflop_per_step": round(path.flops / 1e9, 2)},
+                   **path.config, "gflop_per_step": round(path.flops / 1e9, 2),
+                   "weight_layout": ("slabs [K/64][N][64] (rq_fp8_pack_weights, offline)"
+                                     if path.wlayout == "slabs" else "rows [N][K]")},
         "roofline": roofline,
         "quant_roofline": quant_roofline,
     }

@@ -6,6 +6,8 @@ PyTorch provides device memory and the current stream.
 
 * ``quant_weights(w, wscale=...)``            offline E4M3 weight quantization (scales per
                                                output channel, per tensor or per 128x128 block)
+* ``pack_weights(w_q)``                        offline repacking into the slab layout
+                                               (``wlayout="slabs"`` in the linears)
 * ``linear(x, w_q, w_scale, act=...)``         per-token quantization + FP8 GEMM + FP16 epilogue
 * ``linear_noalloc(x, w_q, w_scale, out)``     the same without allocating (static device scratch)
 * ``moe_grouped_linear(x, ids, w_q, w_scale, ...)``  routing plan + grouped GEMM (+ combine)
@@ -24,13 +26,15 @@ from . import _lib
 from ._lib import (RQ_ACT_GATE_SILU, RQ_ACT_NONE, RQ_ACT_SILU_MUL, RQ_MOE_IN_PERMUTED, RQ_MOE_IN_TOKENS,  # noqa: F401
                    RQ_MOE_PLAN_READY,
                    RQ_MOE_OUT_COMBINED, RQ_MOE_OUT_PERMUTED, RQ_WSCALE_BLOCK128, RQ_WSCALE_CHANNEL,
-                   RQ_WSCALE_TENSOR, RQ_FP8_E4M3, RQ_FP8_E5M2, RQ_FLAG_EXPERT_ID, DebugOut, RqError)
+                   RQ_WSCALE_TENSOR, RQ_WLAYOUT_SLABS, RQ_FP8_E4M3, RQ_FP8_E5M2, RQ_FLAG_EXPERT_ID, DebugOut,
+                   RqError)
 
 ACTS = {"none": RQ_ACT_NONE, "silu_mul": RQ_ACT_SILU_MUL, "gate_silu": RQ_ACT_GATE_SILU}
 IN_LAYOUTS = {"tokens": RQ_MOE_IN_TOKENS, "permuted": RQ_MOE_IN_PERMUTED}
 OUT_LAYOUTS = {"permuted": RQ_MOE_OUT_PERMUTED, "combined": RQ_MOE_OUT_COMBINED}
 WSCALES = {"channel": RQ_WSCALE_CHANNEL, "tensor": RQ_WSCALE_TENSOR, "block128": RQ_WSCALE_BLOCK128}
 AFMTS = {"e4m3": RQ_FP8_E4M3, "e5m2": RQ_FP8_E5M2}
+WLAYOUTS = {"rows": 0, "slabs": RQ_WLAYOUT_SLABS}
 
 
 def scale_shape(lead, n, k, wscale):
@@ -113,6 +117,24 @@ def quant_weights(w, w_q=None, w_scale=None, stream=None, wscale="channel"):
     return w_q, w_scale
 
 
+def pack_weights(w_q, out=None, stream=None):
+    """E4M3 weights [N, K] or [B, N, K] (row layout) -> the same bytes in the slab layout
+    [B, K/64, N, 64] (``rq_fp8_pack_weights``; K % 64 == 0), returned as a tensor of the input's
+    shape that the linears take with ``wlayout="slabs"``."""
+    _dev(w_q, torch.uint8, "w_q")
+    if w_q.dim() not in (2, 3):
+        raise ValueError("w_q must be [N, K] or [B, N, K]")
+    b, n, k = (1,) + tuple(w_q.shape) if w_q.dim() == 2 else tuple(w_q.shape)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(w_q)
+    _dev(out, torch.uint8, "out")
+    _shape(out, w_q.shape, "out")
+    st = _lib.load().rq_fp8_pack_weights(_ptr(w_q), b, n, k, _ptr(out), _stream(w_q, stream))
+    _lib.check("rq_fp8_pack_weights", st)
+    return out
+
+
 def linear_workspace_size(m, k, act="none", n=None):
     """Workspace bytes of ``linear``; with ``n`` given, the size that also lets the call split
     K (small M, see ``rq_fp8_linear_workspace_size_ex``)."""
@@ -139,7 +161,7 @@ def _debug(debug, q_rows, h_rows, k, act, device):
 
 
 def linear(x, w_q, w_scale, act="none", out=None, workspace=None, debug=False, stream=None, wscale="channel",
-           afmt="e4m3"):
+           afmt="e4m3", wlayout="rows"):
     """W8A8 FP8 linear: FP16 x [M, K] (or [M, 2K] for ``act='silu_mul'``) -> FP16 y [M, N]
     (or h [M, N/2] for ``act='gate_silu'``, whose weight rows interleave 32 gate and 32 up
     features; see ``interleave_gate_up``).
@@ -147,10 +169,11 @@ def linear(x, w_q, w_scale, act="none", out=None, workspace=None, debug=False, s
     With ``debug=True`` returns ``(y, {"a_q", "a_scale", "h"})``: the quantized GEMM input
     (and the SiLU*up rows).  ``wscale`` names the granularity of ``w_scale`` (see
     ``quant_weights``); ``afmt`` the format the activations are quantized to ("e4m3" or
-    "e5m2").
+    "e5m2"); ``wlayout`` the byte layout of ``w_q`` ("rows", or "slabs" from ``pack_weights``).
     """
     a = _code(ACTS, act, "act")
     g = _code(WSCALES, wscale, "wscale")
+    wl = _code(WLAYOUTS, wlayout, "wlayout")
     f = _code(AFMTS, afmt, "afmt")
     _dev(x, torch.float16, "x")
     _dev(w_q, torch.uint8, "w_q")
@@ -171,7 +194,7 @@ def linear(x, w_q, w_scale, act="none", out=None, workspace=None, debug=False, s
     _dev(out, torch.float16, "out")
     _shape(out, (m, n_out), "out")
     _shape(w_scale, scale_shape((), n, k, g), "w_scale")
-    st = lib.rq_fp8_linear_ex(_ptr(x), m, k, a, f, _ptr(w_q), _ptr(w_scale), g, n, _ptr(out), _ptr(ws),
+    st = lib.rq_fp8_linear_ex(_ptr(x), m, k, a, f, _ptr(w_q), _ptr(w_scale), g | wl, n, _ptr(out), _ptr(ws),
                               ws.numel(), ctypes.byref(dbg_s) if dbg_s is not None else None,
                               _stream(x, stream))
     _lib.check("rq_fp8_linear_ex", st)
@@ -204,7 +227,8 @@ def linear_noalloc(x, w_q, w_scale, out, act="none", stream=None):
 
 def moe_grouped_linear(x, topk_ids, w_q, w_scale, in_layout="tokens", act="none",
                        out_layout="permuted", topk_w=None, out=None, workspace=None,
-                       debug=False, stream=None, wscale="channel", afmt="e4m3", plan_ready=False):
+                       debug=False, stream=None, wscale="channel", afmt="e4m3", plan_ready=False,
+                       wlayout="rows"):
     """Expert grouped W8A8 linear.
 
     ``x``: FP16 [T, K*] (tokens) or [T*top_k, K*] (permuted), K* = 2K for ``silu_mul``;
@@ -213,6 +237,7 @@ def moe_grouped_linear(x, topk_ids, w_q, w_scale, in_layout="tokens", act="none"
     ``topk_w``: FP16 [T, top_k] for ``out_layout='combined'``.
     ``plan_ready``: the ``workspace`` given already holds the routing plan of these ``topk_ids``
     from an earlier call (permuted input only; see ``RQ_MOE_PLAN_READY``).
+    ``wlayout``: byte layout of ``w_q`` ("rows", or "slabs" from ``pack_weights``).
     Returns FP16 [T*top_k, N] (permuted) or [T, N] (combined), plus the debug dict when
     ``debug=True``: ``a_q`` / ``a_scale`` hold the GEMM operand, one row per routed slot in
     the permuted order; ``h`` (``silu_mul``) one row per input row.
@@ -221,6 +246,7 @@ def moe_grouped_linear(x, topk_ids, w_q, w_scale, in_layout="tokens", act="none"
     a = _code(ACTS, act, "act")
     ol = _code(OUT_LAYOUTS, out_layout, "out_layout")
     g = _code(WSCALES, wscale, "wscale")
+    wl = _code(WLAYOUTS, wlayout, "wlayout")
     f = _code(AFMTS, afmt, "afmt")
     _dev(x, torch.float16, "x")
     _dev(topk_ids, torch.int32, "topk_ids")
@@ -248,7 +274,7 @@ def moe_grouped_linear(x, topk_ids, w_q, w_scale, in_layout="tokens", act="none"
         raise ValueError("plan_ready needs the workspace that holds the plan")
     st = lib.rq_fp8_moe_grouped_linear_ex(
         _ptr(x), il | (RQ_MOE_PLAN_READY if plan_ready else 0), a, f, _ptr(topk_ids), _ptr(topk_w), t, top_k,
-        _ptr(w_q), _ptr(w_scale), g, e, n, k,
+        _ptr(w_q), _ptr(w_scale), g | wl, e, n, k,
         _ptr(out), ol, _ptr(ws), ws.numel(), ctypes.byref(dbg_s) if dbg_s is not None else None,
         _stream(x, stream))
     _lib.check("rq_fp8_moe_grouped_linear_ex", st)

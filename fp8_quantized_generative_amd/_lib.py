@@ -17,6 +17,7 @@ RQ_MOE_OUT_PERMUTED, RQ_MOE_OUT_COMBINED = 0, 1
 RQ_KERNEL_QUANT, RQ_KERNEL_GEMM, RQ_KERNEL_COMBINE, RQ_KERNEL_ROUTER, RQ_KERNEL_ATTENTION, RQ_KERNEL_TOPK = \
     0, 1, 2, 3, 4, 5
 RQ_WSCALE_CHANNEL, RQ_WSCALE_TENSOR, RQ_WSCALE_BLOCK128 = 0, 1, 2
+RQ_WLAYOUT_SLABS = 0x100
 RQ_FP8_E4M3, RQ_FP8_E5M2 = 0, 1
 RQ_FLAG_EXPERT_ID = 1
 RQ_ERR_SCRATCH = 8
@@ -56,6 +57,7 @@ SIGNATURES = {
     "rq_topk_workspace_size": (_SZ, [_I64, _I64, _I]),
     "rq_topk": (_I, [_P, _I64, _I64, _I, _P, _P, _P, _SZ, _P]),
     "rq_fp8_linear_noalloc": (_I, [_P, _I64, _I64, _I, _P, _P, _I64, _P, _P]),
+    "rq_fp8_pack_weights": (_I, [_P, _I64, _I64, _I64, _P, _P]),
 }
 
 _lib = None

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "librq_fp8.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["quant.hip", "gemm.hip", "moe.hip", "router.hip", "attention.hip", "topk.hip", "api.hip"]
+SOURCES = ["quant.hip", "gemm.hip", "moe.hip", "router.hip", "attention.hip", "topk.hip", "layout.hip", "api.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [

@@ -204,6 +204,19 @@ int rq_fp8_quant_weights(const uint16_t* w, int64_t B, int64_t N, int64_t K, uin
   return rq_fp8_quant_weights_ex(w, B, N, K, RQ_WSCALE_CHANNEL, w_q, w_scale, stream);
 }
 
+int rq_fp8_pack_weights(const uint8_t* w_q, int64_t B, int64_t N, int64_t K, uint8_t* w_packed, void* stream) {
+  if (B < 0 || N < 0 || K <= 0) return RQ_ERR_SHAPE;
+  if (K % 64 != 0) return RQ_ERR_ALIGN;
+  if (N > 0 && B > INT64_MAX / N / K) return RQ_ERR_SHAPE;
+  if (B * N == 0) return RQ_OK;
+  if (!w_q || !w_packed) return RQ_ERR_NULL;
+  if (w_q == w_packed) return RQ_ERR_ARG;
+  if (!aligned(w_q, 16) || !aligned(w_packed, 16)) return RQ_ERR_ALIGN;
+  const int dev = check_device();
+  if (dev != RQ_OK) return dev;
+  return rq::launch_pack_slabs(w_q, B, N, K, w_packed, (hipStream_t)stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
+}
+
 size_t rq_fp8_linear_workspace_size(int64_t M, int64_t K, int act) {
   (void)act;
   if (M < 0 || K <= 0) return 0;
@@ -220,9 +233,12 @@ int rq_fp8_linear_ex(const uint16_t* x, int64_t M, int64_t K, int act, int a_fmt
                      size_t workspace_bytes, const rq_debug_out* dbg, void* stream) {
   if (act != RQ_ACT_NONE && act != RQ_ACT_SILU_MUL && act != RQ_ACT_GATE_SILU) return RQ_ERR_ARG;
   if (a_fmt != RQ_FP8_E4M3 && a_fmt != RQ_FP8_E5M2) return RQ_ERR_ARG;
+  const bool slabs = (w_gran & RQ_WLAYOUT_SLABS) != 0;
+  w_gran &= ~RQ_WLAYOUT_SLABS;
   if (w_gran != RQ_WSCALE_CHANNEL && w_gran != RQ_WSCALE_TENSOR && w_gran != RQ_WSCALE_BLOCK128) return RQ_ERR_ARG;
   if (M < 0 || K <= 0 || N <= 0) return RQ_ERR_SHAPE;
   if (K % 16 != 0 || N % 16 != 0 || (act == RQ_ACT_GATE_SILU && N % 64 != 0)) return RQ_ERR_ALIGN;
+  if (slabs && K % 64 != 0) return RQ_ERR_ALIGN;
   if (w_gran == RQ_WSCALE_BLOCK128 && (N % rq::kScaleBlock != 0 || K % rq::kScaleBlock != 0)) return RQ_ERR_ALIGN;
   if (K > kMaxK || N > (int64_t)1 << 30 || M > (int64_t)1 << 31) return RQ_ERR_SHAPE;
   if (M * K > kMaxOperandBytes || N * K > kMaxOperandBytes) return RQ_ERR_SHAPE;
@@ -274,6 +290,7 @@ int rq_fp8_linear_ex(const uint16_t* x, int64_t M, int64_t K, int act, int a_fmt
   g.a_fmt = a_fmt;
   g.splits = partial != nullptr ? rq::dense_splits(M, N, K, act, w_gran) : 1;
   g.partial = partial;
+  g.b_slabs = slabs ? 1 : 0;
   Hook hook(RQ_KERNEL_GEMM, s);
   return rq::launch_gemm_dense(g, s) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
@@ -314,6 +331,8 @@ int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act, int 
                                  int out_layout, void* workspace, size_t workspace_bytes,
                                  const rq_debug_out* dbg, void* stream) {
   if (act != RQ_ACT_NONE && act != RQ_ACT_SILU_MUL && act != RQ_ACT_GATE_SILU) return RQ_ERR_ARG;
+  const bool slabs = (w_gran & RQ_WLAYOUT_SLABS) != 0;
+  w_gran &= ~RQ_WLAYOUT_SLABS;
   if (w_gran != RQ_WSCALE_CHANNEL && w_gran != RQ_WSCALE_TENSOR && w_gran != RQ_WSCALE_BLOCK128) return RQ_ERR_ARG;
   if (a_fmt != RQ_FP8_E4M3 && a_fmt != RQ_FP8_E5M2) return RQ_ERR_ARG;
   // RQ_MOE_PLAN_READY: reuse the plan in the workspace (permuted input only: a token input
@@ -327,6 +346,7 @@ int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act, int 
     return RQ_ERR_SHAPE;
   if (K % 16 != 0 || N % 16 != 0 || (act == RQ_ACT_GATE_SILU && N % 64 != 0)) return RQ_ERR_ALIGN;
   if (w_gran == RQ_WSCALE_BLOCK128 && (N % rq::kScaleBlock != 0 || K % rq::kScaleBlock != 0)) return RQ_ERR_ALIGN;
+  if (slabs && K % 64 != 0) return RQ_ERR_ALIGN;
   if (K > kMaxK || N > (int64_t)1 << 30 || T * top_k > ((int64_t)1 << 31) - 1)
     return RQ_ERR_SHAPE;
   if (T * top_k * K > kMaxOperandBytes || N * K > kMaxOperandBytes) return RQ_ERR_SHAPE;
@@ -399,6 +419,7 @@ int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act, int 
   g.gate = act == RQ_ACT_GATE_SILU ? 1 : 0;
   g.b_gran = w_gran;
   g.a_fmt = a_fmt;
+  g.b_slabs = slabs ? 1 : 0;
   {
     Hook hook(RQ_KERNEL_GEMM, s);
     if (rq::launch_gemm_grouped(g, kind, s) != hipSuccess) return RQ_ERR_HIP;

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace rq {
 
 // Packed vector types.
@@ -82,6 +84,9 @@ hipError_t launch_quant_tensor(const uint16_t* w, int64_t B, int64_t N, int64_t 
                                hipStream_t stream);
 hipError_t launch_quant_blocks(const uint16_t* w, int64_t B, int64_t N, int64_t K, uint8_t* q, float* scale,
                                hipStream_t stream);
+// w_q [B][N][K] bytes -> the slab layout [B][K/64][N][64] (K a multiple of 64).
+hipError_t launch_pack_slabs(const uint8_t* w_q, int64_t B, int64_t N, int64_t K, uint8_t* w_packed,
+                             hipStream_t stream);
 
 struct GemmArgs {
   const uint8_t* a;       // [a_rows][K] E4M3 (token rows, or permuted rows in grouped mode)
@@ -105,6 +110,10 @@ struct GemmArgs {
   // and applies the epilogue
   int32_t splits;             // 1: no split
   float* partial;
+  // weight byte layout: 0 rows ([E][N][K]); 1 slabs ([E][K/64][N][64], see
+  // rq_fp8_pack_weights; K a multiple of 64): the 64-byte K slab of every weight row stored
+  // together, so that a GEMM tile's slab is one contiguous run of BN * 64 bytes
+  int32_t b_slabs;
 };
 
 // GEMM tile shapes (rows x columns of output per workgroup).

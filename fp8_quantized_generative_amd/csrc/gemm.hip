@@ -302,12 +302,21 @@ __device__ __forceinline__ v4i pick(bool c, v4i x, v4i y) { return c ? x : y; }
 
 // Split-K: the descriptors start at the part's first K byte (kl bytes per part), so the K
 // loop runs over the part as over a whole row; the row stride stays K.
+// Slab-layout weights ([E][K/64][N][64]): the tile's rows start at byte (k0 / 64) * 64 N +
+// 64 n0 of the expert's matrix and the range runs to the matrix's end.  Rows past N then read
+// the first rows of the next slab (or zero past the matrix): they only feed output columns
+// past N, which are never stored.
 template <int BN>
 __device__ __forceinline__ TileDesc2 tile_descs(const GemmArgs& p, const TileInfo& t, int kl = 0) {
   TileDesc2 d;
   const int k0 = t.part * kl;
   d.a = make_desc(p.a + (int64_t)t.row_begin * p.K + k0, (uint32_t)((t.row_end - t.row_begin) * p.K - k0));
-  d.b = make_desc(p.b + ((int64_t)t.expert * p.N + t.n0) * p.K + k0, (uint32_t)(min(BN, p.N - t.n0) * p.K - k0));
+  if (p.b_slabs) {
+    const int rel = k0 * p.N + 64 * t.n0;  // k0 is a multiple of 64
+    d.b = make_desc(p.b + (int64_t)t.expert * p.N * p.K + rel, (uint32_t)(p.N * p.K - rel));
+  } else {
+    d.b = make_desc(p.b + ((int64_t)t.expert * p.N + t.n0) * p.K + k0, (uint32_t)(min(BN, p.N - t.n0) * p.K - k0));
+  }
   return d;
 }
 
@@ -375,12 +384,16 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
   // The swizzle depends only on row bits 1..3, which (lane >> 2) fixes for every load, so
   // each lane fetches the same granule in all of its loads.  Offsets are relative to the
   // tile's descriptors, so they are the same for every tile.
+  // Slab-layout weights: B row r of the tile sits at 64 r and K slab s at 64 N s past the
+  // tile's start (bstep: the B byte offset of one K byte, N instead of 1).
   const int gran = swz(lane >> 2, lane & 3);  // XOR swizzle is its own inverse
+  const uint32_t bstep = p.b_slabs ? (uint32_t)N : 1u;
   uint32_t voff[C::LOADS];
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i) {
     const int row = 16 * (i * C::LOADERS + wave) + (lane >> 2);
-    voff[i] = (uint32_t)((i < C::A_LOADS ? row : row - C::BM) * K + 16 * gran);
+    const int brow = p.b_slabs ? (row - C::BM) * BK : (row - C::BM) * K;
+    voff[i] = (uint32_t)((i < C::A_LOADS ? row * K : brow) + 16 * gran);
   }
   // Wave-uniform LDS byte address of this wave's first 16-row group in ring buffer `buf`.
   auto wave_lds = [&](int buf) -> uint32_t {
@@ -389,13 +402,15 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
   // Full slab (all 64 K bytes in range): the K offset (soff = slab * 64) travels in the
   // scalar soffset.
   auto issue_full = [&](const TileDesc2& d, uint32_t soff, uint32_t lds, int i) {
-    load_lds_16(i < C::A_LOADS ? d.a : d.b, voff[i], soff, lds, 16 * BK * C::LOADERS * i);
+    load_lds_16(i < C::A_LOADS ? d.a : d.b, voff[i], i < C::A_LOADS ? soff : soff * bstep, lds,
+                16 * BK * C::LOADERS * i);
   };
   // Any slab, including the ragged last one: granules past K read zero.
   auto issue_one = [&](const TileDesc2& d, int slab, uint32_t lds, int i) {
     const uint32_t k0 = (uint32_t)slab * BK;
     const bool kin = (int)k0 + 16 * gran < KL;
-    load_lds_16(i < C::A_LOADS ? d.a : d.b, kin ? voff[i] + k0 : kOutOfRange, 0u, lds, 16 * BK * C::LOADERS * i);
+    load_lds_16(i < C::A_LOADS ? d.a : d.b, kin ? voff[i] + (i < C::A_LOADS ? k0 : k0 * bstep) : kOutOfRange, 0u,
+                lds, 16 * BK * C::LOADERS * i);
   };
   // The tile's BM row scales and BN column scales into scale area `region` (0 or 1);
   // entries past the tile's rows or columns read zero and are never used.

@@ -237,6 +237,26 @@ enum { RQ_WSCALE_CHANNEL = 0, RQ_WSCALE_TENSOR = 1, RQ_WSCALE_BLOCK128 = 2 };
  * multiplies them with the E4M3 weights.  Weights are always E4M3. */
 enum { RQ_FP8_E4M3 = 0, RQ_FP8_E5M2 = 1 };
 
+/* Weight byte layout, OR'ed into the w_gran argument of rq_fp8_linear_ex and
+ * rq_fp8_moe_grouped_linear_ex.  Without it w_q is [B][N][K] (row layout).  With
+ * RQ_WLAYOUT_SLABS w_q holds the same bytes in the slab layout rq_fp8_pack_weights writes;
+ * K must be a multiple of 64 (RQ_ERR_ALIGN otherwise).  Results are identical bit for bit to
+ * those of the row layout: only the addresses at which the GEMM finds the bytes change.  The
+ * scales keep their layout. */
+enum { RQ_WLAYOUT_SLABS = 0x100 };
+
+/* Offline repacking of quantized weights for the GEMM (a layout of this library; the pages fix
+ * none beyond one E4M3 byte per weight).  The GEMM streams each tile's weights as slabs of
+ * 128 or 256 rows x 64 K bytes; in the row layout such a slab is 64-byte pieces K bytes apart,
+ * which HBM streams markedly slower than a contiguous run.  The slab layout of each of the B
+ * matrices [N][K] is [K / 64][N][64]: the 64-byte K slab s of every row, rows in order, then
+ * slab s + 1; byte (b, n, k) lands at b * N * K + (k / 64) * 64 * N + 64 * n + k % 64.
+ * w_q [B][N][K] -> w_packed, B * N * K bytes, a separate buffer (RQ_ERR_ARG if the two are
+ * the same); any B, N >= 0; K > 0 with K % 64 == 0 (RQ_ERR_ALIGN); both pointers 16-byte
+ * aligned.  One kernel on `stream`; no workspace. */
+int rq_fp8_pack_weights(const uint8_t* w_q, int64_t B, int64_t N, int64_t K, uint8_t* w_packed,
+                        void* stream);
+
 /* rq_fp8_quant_weights with the weight-scale granularity w_gran (layouts above).
  * RQ_ERR_ARG for an unknown w_gran.  Per-tensor scales take four short kernels (amax words
  * are kept in w_scale until the last one writes the scales). */
@@ -245,6 +265,7 @@ int rq_fp8_quant_weights_ex(const uint16_t* w, int64_t B, int64_t N, int64_t K, 
 
 /* rq_fp8_linear with activations quantized to a_fmt (RQ_FP8_*; dbg->a_q then holds bytes of
  * that format) and weights quantized at granularity w_gran; w_scale has that layout (B = 1).
+ * w_gran may carry RQ_WLAYOUT_SLABS (w_q in the slab layout).
  * rq_fp8_linear is this call with RQ_FP8_E4M3 and RQ_WSCALE_CHANNEL.  RQ_ERR_ARG for an
  * unknown a_fmt or w_gran. */
 int rq_fp8_linear_ex(const uint16_t* x, int64_t M, int64_t K, int act, int a_fmt,
@@ -253,7 +274,8 @@ int rq_fp8_linear_ex(const uint16_t* x, int64_t M, int64_t K, int act, int a_fmt
                      const rq_debug_out* dbg, void* stream);
 
 /* rq_fp8_moe_grouped_linear with activations quantized to a_fmt and expert weights quantized
- * at granularity w_gran; w_scale has that layout with B = E.  rq_fp8_moe_grouped_linear is
+ * at granularity w_gran; w_scale has that layout with B = E.  w_gran may carry
+ * RQ_WLAYOUT_SLABS (w_q in the slab layout, B = E).  rq_fp8_moe_grouped_linear is
  * this call with RQ_FP8_E4M3 and RQ_WSCALE_CHANNEL.  The workspace size depends on neither. */
 int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act, int a_fmt,
                                  const int32_t* topk_ids, const uint16_t* topk_w,

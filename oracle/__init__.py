@@ -33,6 +33,8 @@ Arithmetic is float64 and integers.  Every rounding is explicit.  Modules:
                系统OneRec-V2中的优化实践", §2.1 / §2.2) and the linear that uses them.
 * ``topk``   - batched top-k of FP16 candidate rows for beam search (the RadixSelect TopK of
                page "FP8量化在生成式推荐系统OneRec-V2中的优化实践", §3.2).
+* ``layout`` - the slab byte layout of quantized weights (this library's own layout; the
+               pages fix none): a permutation of bytes, no arithmetic.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py`` against
 values fixed independently of this code (the OCP format definition, closed forms,
@@ -40,6 +42,6 @@ brute force over exact rationals, PyTorch's own float8_e4m3fn conversion and SiL
 No function is "parity unpinned".
 """
 
-from . import attention, e4m3, e5m2, quant, linear, ffn, moe, router, topk, wscale  # noqa: F401
+from . import attention, e4m3, e5m2, quant, linear, ffn, moe, router, topk, wscale, layout  # noqa: F401
 
 __all__ = ["attention", "e4m3", "e5m2", "quant", "linear", "ffn", "moe", "router", "topk", "wscale"]

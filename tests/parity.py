@@ -63,12 +63,17 @@ def check_quant(aq, a_s, rows16):
     return q, s
 
 
-def linear_all_rows(rq, x16, w16, label):
+def _packed(rq, wq, wlayout):
+    """The weights as the call takes them: packed offline for the slab layout."""
+    return rq.pack_weights(wq) if wlayout == "slabs" else wq
+
+
+def linear_all_rows(rq, x16, w16, label, wlayout="rows"):
     """One plain linear: weight and activation bytes bit-exact, every output row within
     the tolerance.  Returns the GPU output (host) and the worst ratio."""
     case(label)
     wq, ws = rq.quant_weights(dev(w16))
-    y, dbg = rq.linear(dev(x16), wq, ws, debug=True)
+    y, dbg = rq.linear(dev(x16), _packed(rq, wq, wlayout), ws, debug=True, wlayout=wlayout)
     wq_h, ws_h = host(wq), host(ws)
     check_quant(wq_h, ws_h, w16)
     xq, xs = check_quant(host(dbg["a_q"]), host(dbg["a_scale"]), x16)
@@ -76,8 +81,9 @@ def linear_all_rows(rq, x16, w16, label):
     return y, check_rows(y, xq, xs, wq_h, ws_h)
 
 
-def dense_ffn_gated(rq, x16, w_gu16, w_dn16, label):
-    """The dense FFN chain as the benchmark runs it, checked stage by stage."""
+def dense_ffn_gated(rq, x16, w_gu16, w_dn16, label, wlayout="rows"):
+    """The dense FFN chain as the benchmark runs it (gated gate/up and down on weights in
+    ``wlayout``), checked stage by stage."""
     f = w_gu16.shape[0] // 2
     case(label + ": gate/up, unfused and gated")
     wgu_q, wgu_s = rq.quant_weights(dev(w_gu16))
@@ -93,7 +99,7 @@ def dense_ffn_gated(rq, x16, w_gu16, w_dn16, label):
     # gated gate/up on interleaved weights (quantized from interleaved FP16 rows, as offline)
     wgi_q, wgi_s = rq.quant_weights(dev(rq.interleave_gate_up(w_gu16)))
     assert torch.equal(wgi_q, wgu_q[order]) and torch.equal(wgi_s, wgu_s[order])
-    h = rq.linear(x, wgi_q, wgi_s, act="gate_silu")
+    h = rq.linear(x, _packed(rq, wgi_q, wlayout), wgi_s, act="gate_silu", wlayout=wlayout)
     case(label + ": down")
     wdn_q, wdn_s = rq.quant_weights(dev(w_dn16))
     _, dbg_u = rq.linear(gu, wdn_q, wdn_s, act="silu_mul", debug=True)
@@ -101,7 +107,7 @@ def dense_ffn_gated(rq, x16, w_gu16, w_dn16, label):
     assert np.array_equal(h_h.view(np.uint16), host(dbg_u["h"]).view(np.uint16)), "gated h != unfused h"
     assert ulp_diff16(h_h, ffn.silu_mul(gu_h, f)).max() <= 1
     # down on the gated h, every row
-    y, dbg_d = rq.linear(h, wdn_q, wdn_s, debug=True)
+    y, dbg_d = rq.linear(h, _packed(rq, wdn_q, wlayout), wdn_s, debug=True, wlayout=wlayout)
     wdn_qh, wdn_sh = host(wdn_q), host(wdn_s)
     check_quant(wdn_qh, wdn_sh, w_dn16)
     hq, hs = check_quant(host(dbg_d["a_q"]), host(dbg_d["a_scale"]), h_h)
@@ -123,8 +129,9 @@ def _check_experts(y_perm, aq, a_s, src_of_row, offsets, wq, ws, chunk=CHUNK):
     return worst
 
 
-def moe_ffn_gated(rq, x16, ids, topk_w, w_gu16, w_dn16, label):
-    """The expert FFN as the benchmark runs it, checked stage by stage on every row."""
+def moe_ffn_gated(rq, x16, ids, topk_w, w_gu16, w_dn16, label, wlayout="rows"):
+    """The expert FFN as the benchmark runs it (gated gate/up, then down with the combine
+    reusing the plan, on expert weights in ``wlayout``), checked stage by stage on every row."""
     e, f2, k = w_gu16.shape
     f = f2 // 2
     t, top_k = ids.shape
@@ -149,7 +156,8 @@ def moe_ffn_gated(rq, x16, ids, topk_w, w_gu16, w_dn16, label):
     shared = torch.empty(max(rq.moe_workspace_size(t, top_k, e, f2, k, "tokens", "gate_silu", "permuted"),
                              rq.moe_workspace_size(t, top_k, e, k, f, "permuted", "none", "combined")),
                          dtype=torch.uint8, device="cuda")
-    h = rq.moe_grouped_linear(x, ids_d, wgi_q, wgi_s, "tokens", "gate_silu", "permuted", workspace=shared)
+    h = rq.moe_grouped_linear(x, ids_d, _packed(rq, wgi_q, wlayout), wgi_s, "tokens", "gate_silu", "permuted",
+                              workspace=shared, wlayout=wlayout)
     case(label + ": expert down, unfused and gated")
     wdn_q, wdn_s = rq.quant_weights(dev(w_dn16))
     out_u, dbg_u = rq.moe_grouped_linear(gu, ids_d, wdn_q, wdn_s, "permuted", "silu_mul", "combined",
@@ -157,14 +165,15 @@ def moe_ffn_gated(rq, x16, ids, topk_w, w_gu16, w_dn16, label):
     h_h = host(h)
     assert np.array_equal(h_h.view(np.uint16), host(dbg_u["h"]).view(np.uint16)), "gated h != unfused h"
     assert ulp_diff16(h_h, ffn.silu_mul(gu_h, f)).max() <= 1
-    out, dbg2 = rq.moe_grouped_linear(h, ids_d, wdn_q, wdn_s, "permuted", "none", "combined",
-                                      topk_w=tw, debug=True, workspace=shared, plan_ready=True)
+    wdn_t = _packed(rq, wdn_q, wlayout)
+    out, dbg2 = rq.moe_grouped_linear(h, ids_d, wdn_t, wdn_s, "permuted", "none", "combined",
+                                      topk_w=tw, debug=True, workspace=shared, plan_ready=True, wlayout=wlayout)
     out_h = host(out)
     assert np.array_equal(out_h.view(np.uint16), host(out_u).view(np.uint16)), "gated FFN != unfused FFN"
     wdn_qh, wdn_sh = host(wdn_q), host(wdn_s)
     check_quant(wdn_qh, wdn_sh, w_dn16)
     hq, hs = check_quant(host(dbg2["a_q"]), host(dbg2["a_scale"]), h_h)
-    y_perm = host(rq.moe_grouped_linear(h, ids_d, wdn_q, wdn_s, "permuted", "none", "permuted"))
+    y_perm = host(rq.moe_grouped_linear(h, ids_d, wdn_t, wdn_s, "permuted", "none", "permuted", wlayout=wlayout))
     r_dn = _check_experts(y_perm, hq, hs, lambda r: r, offsets, wdn_qh, wdn_sh)
     assert ulp_diff16(out_h, moe.combine(y_perm, pos, topk_w)).max() <= 1
     return counts, r_gu, r_dn

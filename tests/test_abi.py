@@ -209,3 +209,33 @@ def test_plan_ready_only_with_permuted_input():
     a = lib.rq_fp8_moe_workspace_size(16384, 2, 32, 8192, 2048, 0, 2, 0)
     b = lib.rq_fp8_moe_workspace_size(16384, 2, 32, 2048, 4096, 1, 0, 1)
     assert a > 0 and b > 0
+
+
+def test_pack_weights_validates_on_the_host():
+    lib = lib_mod.load()
+    call = lambda b, n, k, src=FAKE, dst=FAKE + 0x1000: lib.rq_fp8_pack_weights(src, b, n, k, dst, None)  # noqa: E731
+    assert call(1, 128, 48) == RQ_ERR_ALIGN          # K not a multiple of 64
+    assert call(-1, 128, 64) == RQ_ERR_SHAPE
+    assert call(1, -1, 64) == RQ_ERR_SHAPE
+    assert call(1, 128, 0) == RQ_ERR_SHAPE
+    assert call(0, 128, 64) == 0                     # nothing to pack: a validated no-op
+    assert call(3, 0, 64) == 0
+    assert call(1, 128, 64, src=None) == RQ_ERR_NULL
+    assert call(1, 128, 64, dst=FAKE) == RQ_ERR_ARG  # in place is not supported
+    assert call(1, 128, 64, dst=FAKE + 8) == RQ_ERR_ALIGN
+
+
+def test_slab_layout_flag_validates_on_the_host():
+    lib = lib_mod.load()
+    slabs = lib_mod.RQ_WLAYOUT_SLABS
+    lin = lambda m, n, k, g: lib.rq_fp8_linear_ex(FAKE, m, k, 0, 0, FAKE, FAKE, g, n, FAKE, FAKE, 1 << 30,  # noqa: E731
+                                                   None, None)
+    assert lin(0, 144, 64, slabs) == 0                        # a validated no-op; any N % 16 == 0
+    assert lin(0, 128, 80, slabs) == RQ_ERR_ALIGN             # K % 64
+    assert lin(0, 144, 80, 0) == 0                            # the row layout takes K % 16 == 0
+    assert lin(0, 128, 64, slabs | 3) == RQ_ERR_ARG           # unknown granularity still rejected
+    assert lin(0, 128, 64, 0x200) == RQ_ERR_ARG               # unknown layout bits too
+    moe = lambda n, k, g: lib.rq_fp8_moe_grouped_linear_ex(FAKE, 0, 0, 0, FAKE, FAKE, 0, 2, FAKE, FAKE, g,  # noqa: E731
+                                                            8, n, k, FAKE, 0, FAKE, 1 << 30, None, None)
+    assert moe(144, 128, slabs) == 0
+    assert moe(256, 96, slabs) == RQ_ERR_ALIGN

@@ -30,15 +30,15 @@ def layer():
 
 def test_layer_qkv_and_o(layer):
     rq = require_gpu()
-    _, r1 = parity.linear_all_rows(rq, layer["x_qkv"], layer["w_qkv"], "workload 5: QKV 512 x 6144 x 2048")
-    _, r2 = parity.linear_all_rows(rq, layer["x_o"], layer["w_o"], "workload 5: O 512 x 2048 x 2048")
+    _, r1 = parity.linear_all_rows(rq, layer["x_qkv"], layer["w_qkv"], "workload 5: QKV 512 x 6144 x 2048", "slabs")
+    _, r2 = parity.linear_all_rows(rq, layer["x_o"], layer["w_o"], "workload 5: O 512 x 2048 x 2048", "slabs")
     assert r1 <= 1 and r2 <= 1
 
 
 def test_layer_dense_ffn(layer):
     rq = require_gpu()
     r_gu, r_dn = parity.dense_ffn_gated(rq, layer["x_ffn"], layer["w_gu"], layer["w_dn"],
-                                        "workload 5: FFN 512 rows, F = 8192")
+                                        "workload 5: FFN 512 rows, F = 8192", "slabs")
     assert r_gu <= 1 and r_dn <= 1
 
 
@@ -46,6 +46,6 @@ def test_layer_expert_ffn(layer):
     rq = require_gpu()
     counts, r_gu, r_dn = parity.moe_ffn_gated(rq, layer["x_moe"], layer["ids"], layer["topk_w"],
                                               layer["w_gu_moe"], layer["w_dn_moe"],
-                                              "workload 5: MoE 512 tokens, top-2 of 32, F = 4096")
+                                              "workload 5: MoE 512 tokens, top-2 of 32, F = 4096", "slabs")
     assert (counts == 0).any() and counts.max() < 512
     assert r_gu <= 1 and r_dn <= 1

@@ -105,17 +105,18 @@ def test_merged_qkv_equals_split():
 def test_attention_full_size():
     rq = require_gpu()
     d = workloads.make(2)
-    parity.linear_all_rows(rq, d["x"], d["w_qkv"], "workload 2: QKV 4096 x 6144 x 2048, every row")
-    parity.linear_all_rows(rq, d["attn_out"], d["w_o"], "workload 2: O 4096 x 2048 x 2048, every row")
+    # as the benchmark runs them: weights packed offline into the slab layout
+    parity.linear_all_rows(rq, d["x"], d["w_qkv"], "workload 2: QKV 4096 x 6144 x 2048, every row", "slabs")
+    parity.linear_all_rows(rq, d["attn_out"], d["w_o"], "workload 2: O 4096 x 2048 x 2048, every row", "slabs")
 
 
 @pytest.mark.slow
 def test_ffn_full_size_chain():
     """The dense FFN at 4096 tokens as the benchmark runs it (gated gate/up, down over
-    K = 8192), every row, plus the unfused formulation bit for bit."""
+    K = 8192, slab-layout weights), every row, plus the unfused formulation bit for bit."""
     rq = require_gpu()
     d = workloads.make(3)
-    parity.dense_ffn_gated(rq, d["x"], d["w_gu"], d["w_dn"], "workload 3: FFN 4096 tokens, F = 8192")
+    parity.dense_ffn_gated(rq, d["x"], d["w_gu"], d["w_dn"], "workload 3: FFN 4096 tokens, F = 8192", "slabs")
 
 
 def test_determinism():

@@ -125,11 +125,12 @@ def test_moe_determinism():
 @pytest.mark.slow
 def test_moe_full_size_every_row():
     """16384 tokens, top-2 of 32 Zipf-loaded experts, F = 4096, as the benchmark runs it
-    (gated gate/up, down with the combine), every permuted row checked expert by expert."""
+    (gated gate/up, down with the combine, slab-layout expert weights), every permuted row
+    checked expert by expert."""
     rq = require_gpu()
     d = workloads.make(4)
     counts, r_gu, r_dn = parity.moe_ffn_gated(rq, d["x"], d["ids"], d["topk_w"], d["w_gu"], d["w_dn"],
-                                              "workload 4: MoE 16384 tokens, top-2 of 32, F = 4096")
+                                              "workload 4: MoE 16384 tokens, top-2 of 32, F = 4096", "slabs")
     assert (counts == 0).any()
 
 
