@@ -78,23 +78,27 @@ def parse():
     return ap.parse_args()
 
 
-# Calls of one step, in launch order: (workload, call, kind).  "linear" launches the row
-# quantizer and the GEMM; "moe" the routing-plan kernel (one workgroup at these sizes), the
-# quantizer and the grouped GEMM; "moe_combined" (the down call, which reuses the gate/up call's
-# plan) the quantizer, the grouped GEMM and the weighted combine.
+# Calls of one step, in launch order: (workload, call, kind), and the kernels each kind
+# launches (the library's choices at these shapes).  "linear": the row quantizer and the GEMM;
+# "linear_split" (512 x 2048 x 8192: K cut in 4 parts): also the reduce kernel that adds the
+# parts; "moe": the single-workgroup routing plan (up to 8192 slots), the quantizer and the
+# grouped GEMM; "moe_large" (32768 slots): the three plan kernels instead; "moe_combined" (the
+# down call, which reuses the gate/up call's plan): the quantizer, the grouped GEMM and the
+# weighted combine.
 STEP = [
     ("attention", "qkv", "linear"), ("attention", "o", "linear"),
     ("ffn", "gate_up", "linear"), ("ffn", "down", "linear"),
-    ("moe", "gate_up", "moe"), ("moe", "down", "moe_combined"),
+    ("moe", "gate_up", "moe_large"), ("moe", "down", "moe_combined"),
     ("layer_small_m", "qkv", "linear"), ("layer_small_m", "o", "linear"),
-    ("layer_small_m", "gate_up", "linear"), ("layer_small_m", "down", "linear"),
+    ("layer_small_m", "gate_up", "linear"), ("layer_small_m", "down", "linear_split"),
     ("layer_small_m", "moe_gate_up", "moe"), ("layer_small_m", "moe_down", "moe_combined"),
 ]
 DOMINANT = ("moe", "gate_up")
-KERNELS = {"linear": ["quant", "gemm"], "moe": ["plan", "quant", "gemm"],
-           "moe_combined": ["quant", "gemm", "combine"]}  # the down call reuses the gate/up call's plan
-OUR_KERNELS = ("quant_rows", "gemm_fp8_kernel", "plan_single", "plan_hist", "plan_scan", "plan_scatter",
-               "combine_kernel")
+KERNELS = {"linear": ["quant", "gemm"], "linear_split": ["quant", "gemm", "reduce"],
+           "moe": ["plan", "quant", "gemm"], "moe_large": ["plan_hist", "plan_scan", "plan_scatter", "quant", "gemm"],
+           "moe_combined": ["quant", "gemm", "combine"]}
+OUR_KERNELS = ("quant_rows", "gemm_fp8_kernel", "splitk_reduce", "plan_single", "plan_hist", "plan_scan",
+               "plan_scatter", "combine_kernel")
 
 
 def step_dispatches(only):
@@ -328,7 +332,7 @@ class Path:
                                                             out=y_b, workspace=ws_dn, wscale="block128",
                                                             wlayout=wlayout)))
             self.config["moe"] = ("16384 tokens x 2048; top-2 of 32 experts (Zipf 1.1; max %d, min nonzero %d, "
-                                  "%d empty rows of 32768); gate/up 2x4096, down K=4096"
+                                  "%d empty experts; 32768 routed rows); gate/up 2x4096, down K=4096"
                                   % (counts.max(), counts[counts > 0].min(), int((counts == 0).sum())))
             del d
         if "layer_small_m" in want:
@@ -565,7 +569,9 @@ def _rocprof_rows(path):
     return path, [r[1:] for r in rows]
 
 
-_KIND_TOKEN = {"quant": "quant_rows", "gemm": "gemm_fp8_kernel", "plan": "plan_single", "combine": "combine_kernel"}
+_KIND_TOKEN = {"quant": "quant_rows", "gemm": "gemm_fp8_kernel", "reduce": "splitk_reduce", "plan": "plan_single",
+               "plan_hist": "plan_hist", "plan_scan": "plan_scan", "plan_scatter": "plan_scatter",
+               "combine": "combine_kernel"}
 
 
 def _align_steps(names, only, steps):
@@ -690,9 +696,14 @@ def pmc_summary(path, only=None, steps=None):
           "instructions per FP8 MFMA" % (XCDS, SIMDS, XCDS))
 
 
+CUS = 256  # MI355X compute units: TA, TD and TCP counters are summed over them
+
+
 def pmc_dump(paths, only=None, steps=None):
     """Every counter of one or more rocprofv3 --pmc databases, averaged per GEMM call of the
-    step (the same dispatch matching as --pmc-summary), with the GEMM's average duration."""
+    step (the same dispatch matching as --pmc-summary), with the GEMM's average duration, then
+    the derived memory-pipeline figures of each call."""
+    derived = {}
     for path in paths:
         src, per = _pmc_db(path)
         ids = sorted(per)
@@ -704,8 +715,28 @@ def pmc_dump(paths, only=None, steps=None):
         print("# rocprofv3 --pmc: %s (%d steps matched)" % (path, nsteps))
         for label, recs in groups.items():
             print("  %-26s avg_us %.1f" % (label, np.mean([r[1] for r in recs]) / 1e3))
-            for k in sorted(recs[0][2]):
-                print("    %-34s %16.0f" % (k, np.mean([r[2][k] for r in recs])))
+            c = {k: float(np.mean([r[2][k] for r in recs])) for k in sorted(recs[0][2])}
+            for k, v in c.items():
+                print("    %-34s %16.0f" % (k, v))
+            d = derived.setdefault(label, {})
+            cyc = c.get("GRBM_GUI_ACTIVE", np.nan) / XCDS  # engine cycles of the dispatch
+            for name, key in (("ta_busy", "TA_TA_BUSY"), ("td_busy", "TD_TD_BUSY"), ("td_tc_stall", "TD_TC_STALL"),
+                              ("tcp_pending_stall", "TCP_PENDING_STALL_CYCLES")):
+                if key in c:
+                    d[name] = c[key] / (CUS * cyc)
+            if "TCP_TCC_READ_REQ" in c and "TCP_TCC_READ_REQ_LATENCY" in c:
+                d["l2_read_latency_cycles"] = c["TCP_TCC_READ_REQ_LATENCY"] / c["TCP_TCC_READ_REQ"]
+                d["l2_read_req_per_cu_cycle"] = c["TCP_TCC_READ_REQ"] / (CUS * cyc)
+            if "TCC_HIT_sum" in c and "TCC_MISS_sum" in c:
+                d["l2_hit_rate"] = c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"])
+    cols = ("ta_busy", "td_busy", "td_tc_stall", "tcp_pending_stall", "l2_read_latency_cycles",
+            "l2_read_req_per_cu_cycle", "l2_hit_rate")
+    print("# derived per GEMM call: busy/stall fractions = counter / (%d CUs x GRBM_GUI_ACTIVE / %d XCDs); "
+          "L2 read latency = TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ (cycles); L2 hit rate = TCC_HIT / "
+          "(TCC_HIT + TCC_MISS)" % (CUS, XCDS))
+    print("# %-26s %s" % ("call", " ".join("%12s" % c[:12] for c in cols)))
+    for label, d in derived.items():
+        print("  %-26s %s" % (label, " ".join("%12.3f" % d.get(c, np.nan) for c in cols)))
 
 
 def source_hash(files):
@@ -754,7 +785,9 @@ def traffic_summary(fetch_dir, write_dir, out, only=None, steps=None):
         names = [r[0] for r in rows]
         aligned, nsteps = _align_steps(names, only, steps)
         last = max(i for i, _, _ in aligned)
-        copies = [r for r in rows[last + 1:] if not any(k in r[0] for k in OUR_KERNELS)]
+        # the calibration copy (x * 1, an elementwise multiply); the fills that allocate the
+        # flush and calibration buffers around it are not copies
+        copies = [r for r in rows[last + 1:] if "MulFunctor" in r[0]]
         for res, label, kind in ((gemm, "%s %s" % DOMINANT, "gemm"), (qnt, "%s %s" % QUANT_CALL, "quant")):
             vals = [rows[i][1] for i, lb, kd in aligned if lb == label and kd == kind]
             if not vals or not copies:
@@ -808,7 +841,7 @@ def kernel_stats(path):
     with open(src) as f:
         for r in csv.DictReader(f):
             name = r["Name"]
-            if not any(k in name for k in OUR_KERNELS + ("router_topk", "attention_core", "topk_segment", "splitk_reduce",
+            if not any(k in name for k in OUR_KERNELS + ("router_topk", "attention_core", "topk_segment", "pack_slabs",
                                                        "quant_blocks", "tensor_")):
                 continue
             short = name.replace("rq::(anonymous namespace)::", "").replace("void ", "")

@@ -7,7 +7,7 @@
 //
 // Plan: slot j = t * top_k + k goes to expert ids[j].  The canonical permuted order sorts
 // slots by (expert, j) - a stable counting sort - computed without any host round trip.  Up to
-// 32768 slots (and 256 experts) one workgroup does it all in a single launch (plan_single);
+// 8192 slots (and 256 experts) one workgroup does it all in a single launch (plan_single);
 // beyond, three kernels:
 //   1. plan_hist:    per block of 1024 slots, a histogram over experts (LDS atomics on
 //                    integer counts, so the result is deterministic);
@@ -219,8 +219,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_scatter(const int32_t* __re
 // ids (slots tid, tid + 1024, ...) into registers at once, so the kernel waits for global
 // memory a single time; then the expert histogram (LDS integer atomics), the scans and the
 // M-tile table as in plan_scan, and the stable scatter over chunks of 1024 slots taken in slot
-// order, each ranked like plan_scatter and placed after the rows of earlier chunks.
-constexpr int64_t kSinglePlanMaxRows = 32768;
+// order, each ranked like plan_scatter and placed after the rows of earlier chunks.  The chunks
+// are serial and one compute unit issues every scattered store, so the single launch only
+// pays for small plans: on MI355X 32768 slots over 32 Zipf-loaded experts take 55 us in one
+// workgroup against 17 us in the three kernels, while 1024 slots save two launches.
+constexpr int64_t kSinglePlanMaxRows = 8192;
 constexpr int64_t kSinglePlanMaxExperts = 256;  // keeps its LDS (19 E + 1 words) under 20 KB
 
 template <int IPT>
@@ -349,8 +352,7 @@ hipError_t launch_moe_plan(const int32_t* ids, int64_t T, int top_k, int64_t E, 
     const int r = (int)R, per = (int)((R + kPlanThreads - 1) / kPlanThreads);  // ids per thread
     if (per <= 1) plan_single<1><<<g1, blk, lds, stream>>>(ids, r, e, nbits, offsets, tt, perm, pos);
     else if (per <= 4) plan_single<4><<<g1, blk, lds, stream>>>(ids, r, e, nbits, offsets, tt, perm, pos);
-    else if (per <= 8) plan_single<8><<<g1, blk, lds, stream>>>(ids, r, e, nbits, offsets, tt, perm, pos);
-    else plan_single<32><<<g1, blk, lds, stream>>>(ids, r, e, nbits, offsets, tt, perm, pos);
+    else plan_single<8><<<g1, blk, lds, stream>>>(ids, r, e, nbits, offsets, tt, perm, pos);
     return hipGetLastError();
   }
   if (nb > 0) {

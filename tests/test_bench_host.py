@@ -12,18 +12,22 @@ import bench
 
 def _names(only=None, steps=2, prefix=("quant_rows_regs<4, false>", "at::native::fill")):
     tok = {"quant": "void rq::quant_rows_regs<8, false>(...)", "gemm": "void rq::gemm_fp8_kernel<Cfg>(...)",
-           "plan": "rq::plan_single(...)", "combine": "rq::combine_kernel(...)"}
+           "reduce": "void rq::splitk_reduce<false>(...)", "plan": "void rq::plan_single<1>(...)",
+           "plan_hist": "rq::plan_hist(...)", "plan_scan": "rq::plan_scan(...)", "plan_scatter": "rq::plan_scatter(...)",
+           "combine": "rq::combine_kernel(...)"}
     seq = [tok[k] for _, k in bench.step_dispatches(only)]
     return list(prefix) + seq * steps + ["at::native::vectorized_elementwise_kernel (copy)"]
 
 
 def test_step_table_matches_workloads():
     seq = bench.step_dispatches(None)
-    # 8 linears x 2 kernels, 2 gate/up MoE calls x 3 (plan, quantizer, GEMM), 2 down calls x 3
-    # (they reuse the plan: quantizer, GEMM, combine)
-    assert len(seq) == 8 * 2 + 2 * 3 + 2 * 3
+    # 8 linears x 2 kernels plus the split-K reduce of the small-M down projection; the 32768-slot
+    # gate/up MoE call x 5 (three plan kernels, quantizer, GEMM), the 1024-slot one x 3 (one plan
+    # kernel); 2 down calls x 3 (they reuse the plan: quantizer, GEMM, combine)
+    assert len(seq) == 8 * 2 + 1 + 5 + 3 + 2 * 3
     assert ("moe gate_up", "gemm") in seq and ("moe down", "plan") not in seq
-    assert len(bench.step_dispatches("moe")) == 6
+    assert ("layer_small_m down", "reduce") in seq and ("moe gate_up", "plan_scan") in seq
+    assert len(bench.step_dispatches("moe")) == 8
 
 
 def test_align_finds_every_step_and_labels():
