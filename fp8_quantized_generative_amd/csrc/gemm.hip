@@ -623,18 +623,40 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
     using LastK = std::integral_constant<int, 1>;  // last slab of a K block (kt odd)
     using NewK = std::integral_constant<int, 2>;   // first slab of a K block (kt even, kt >= 2)
     using RtK = std::integral_constant<int, 3>;    // decided at run time
-    if (C::S < full_slabs) step(True{}, True{}, Any{}, NoK{}, 0, fb0, fb1);
-    else step(False{}, True{}, Any{}, NoK{}, 0, fb0, fb1);
-    int kt = 1;
-    for (; kt + 1 + C::S < full_slabs; kt += 2) {  // kt and kt+1 steady: kt+1+S < full_slabs
-      step(True{}, False{}, Any{}, LastK{}, kt, fb1, fb0);
-      step(True{}, False{}, Any{}, NewK{}, kt + 1, fb0, fb1);
+    // A slab for a wave none of whose rows lies in the tile (whole waves past the valid rows
+    // of an expert's or the matrix's last M-tile): the waits, the barrier and its share of
+    // the loads, without the MFMAs and fragment reads that would only feed rows never stored.
+    auto idle = [&](int kt) {
+      if (loader) wait_slabs<C::LOADS, C::S - 2, true>(lim - kt - 2);
+      else wait_lgkm0();
+      const int fetch = !loader ? 0 : kt + C::S < ktiles ? 1 : (pre ? 2 : 0);
+      __syncthreads();
+      const uint32_t lds_dst = wave_lds((unsigned)(rb + kt) % C::S);
+      if (fetch == 2 && kt + C::S == ktiles) issue_scales(nxt, (j + 1) & 1);
+      if (fetch != 0) {
+        const bool nx = fetch == 2;
+        for (int l = 0; l < C::LOADS; ++l)
+          issue_one(TileDesc2{pick(nx, dn.a, dc.a), pick(nx, dn.b, dc.b)}, nx ? kt + C::S - ktiles : kt + C::S,
+                    lds_dst, l);
+      }
+    };
+    const bool busy = cur.row_end - cur.row_begin > wm * C::WM;  // wave-uniform
+    if (!busy) {
+      for (int kt = 0; kt < ktiles; ++kt) idle(kt);
+    } else {
+      if (C::S < full_slabs) step(True{}, True{}, Any{}, NoK{}, 0, fb0, fb1);
+      else step(False{}, True{}, Any{}, NoK{}, 0, fb0, fb1);
+      int kt = 1;
+      for (; kt + 1 + C::S < full_slabs; kt += 2) {  // kt and kt+1 steady: kt+1+S < full_slabs
+        step(True{}, False{}, Any{}, LastK{}, kt, fb1, fb0);
+        step(True{}, False{}, Any{}, NewK{}, kt + 1, fb0, fb1);
+      }
+      for (; kt + 1 < ktiles; kt += 2) {
+        step(False{}, False{}, Any{}, RtK{}, kt, fb1, fb0);
+        step(False{}, False{}, Any{}, RtK{}, kt + 1, fb0, fb1);
+      }
+      if (kt < ktiles) step(False{}, False{}, Any{}, RtK{}, kt, fb1, fb0);
     }
-    for (; kt + 1 < ktiles; kt += 2) {
-      step(False{}, False{}, Any{}, RtK{}, kt, fb1, fb0);
-      step(False{}, False{}, Any{}, RtK{}, kt + 1, fb0, fb1);
-    }
-    if (kt < ktiles) step(False{}, False{}, Any{}, RtK{}, kt, fb1, fb0);
     // Every wave is past this tile's last barrier and no fragment read is pending, so the
     // ring is free unless `pre` already refilled it.
     if (has_next && !pre) prologue(nxt, dn, (j + 1) & 1);
