@@ -66,3 +66,49 @@ def test_calls_on_a_side_stream():
         ref = ref_lin if i % 2 == 0 else ref_moe
         assert np.array_equal(host(o).view(np.uint16), ref.view(np.uint16))
     assert torch.equal(q2, wl_q) and torch.equal(s2, wl_s)
+
+
+def test_concurrent_host_threads():
+    """Calls from several host threads at once, each on its own stream with its own buffers
+    and workspaces (the header's thread-safety contract): every result equals the
+    single-threaded one, bit for bit."""
+    import threading
+
+    rq = require_gpu()
+    case("linear and moe from 4 host threads on 4 streams")
+    d = workloads.make(4, t=400, k=256, f=128, e=8)
+    w_q, w_s = rq.quant_weights(dev(d["w_gu"]))
+    w_p = rq.pack_weights(w_q)
+    x, ids = dev(d["x"]), dev(d["ids"].astype(np.int32))
+    wl_q, wl_s = rq.quant_weights(dev(d["w_gu"][5]))
+    ref_lin = host(rq.linear(x, wl_q, wl_s))
+    ref_moe = host(rq.moe_grouped_linear(x, ids, w_p, w_s, wlayout="slabs"))
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    results = [[] for _ in streams]
+    errors = []
+
+    def work(n):
+        try:
+            s = streams[n]
+            with torch.cuda.stream(s):
+                for _ in range(6):
+                    results[n].append(("lin", rq.linear(x, wl_q, wl_s, stream=s)))
+                    results[n].append(("moe", rq.moe_grouped_linear(x, ids, w_p, w_s, wlayout="slabs", stream=s)))
+        except Exception as e:  # reported on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(n,)) for n in range(len(streams))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for s in streams:
+        s.synchronize()
+    for rs in results:
+        assert len(rs) == 12
+        for kind, o in rs:
+            ref = ref_lin if kind == "lin" else ref_moe
+            assert np.array_equal(host(o).view(np.uint16), ref.view(np.uint16))
