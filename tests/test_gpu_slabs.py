@@ -143,3 +143,28 @@ def test_moe_slabs_equal_rows(monkeypatch, tile, t, k, f, e):
         outs[wl] = (_bits(h), _bits(y))
     assert np.array_equal(outs["rows"][0], outs["slabs"][0])
     assert np.array_equal(outs["rows"][1], outs["slabs"][1])
+
+
+@pytest.mark.parametrize("wscale,afmt", [("block128", "e4m3"), ("tensor", "e4m3"), ("channel", "e5m2")])
+@pytest.mark.parametrize("tile", [None, "256x256", "64x256"])
+def test_moe_scale_formats_slabs_equal_rows(monkeypatch, tile, wscale, afmt):
+    """The grouped GEMM's scale and activation-format variants (the benchmark times the
+    block-scaled expert FFN on slab-layout weights) give the row layout's bytes."""
+    rq = require_gpu()
+    case("moe slabs wscale=%s afmt=%s tile=%s" % (wscale, afmt, tile))
+    if tile is not None:
+        monkeypatch.setenv("RQ_GEMM_TILE", tile)
+    t, k, f, e = 700, 256, 256, 6
+    d = workloads.make(4, t=t, k=k, f=f, e=e)
+    ids, tw, x = dev(d["ids"].astype(np.int32)), dev(d["topk_w"]), dev(d["x"])
+    wgu_q, wgu_s = rq.quant_weights(dev(rq.interleave_gate_up(d["w_gu"])), wscale=wscale)
+    wdn_q, wdn_s = rq.quant_weights(dev(d["w_dn"]), wscale=wscale)
+    outs = {}
+    for wl, (gq, dq) in {"rows": (wgu_q, wdn_q), "slabs": (rq.pack_weights(wgu_q), rq.pack_weights(wdn_q))}.items():
+        h = rq.moe_grouped_linear(x, ids, gq, wgu_s, "tokens", "gate_silu", "permuted", wscale=wscale, afmt=afmt,
+                                  wlayout=wl)
+        y = rq.moe_grouped_linear(h, ids, dq, wdn_s, "permuted", "none", "combined", topk_w=tw, wscale=wscale,
+                                  afmt=afmt, wlayout=wl)
+        outs[wl] = (_bits(h), _bits(y))
+    assert np.array_equal(outs["rows"][0], outs["slabs"][0])
+    assert np.array_equal(outs["rows"][1], outs["slabs"][1])
