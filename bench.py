@@ -970,7 +970,7 @@ def main():
         print("[bench] per-kernel breakdown (flushed, %d reps each)" % reps, file=sys.stderr, flush=True)
         result["kernels"] = kernel_breakdown(path, timer, reps)
         by_call = {(r["workload"], r["call"]): r for r in result["kernels"]}
-        # the three row-quantizer instances the >= 70% HBM target is judged on, flushed
+        # the three row-quantizer instances held to the >= 70% HBM target, flushed
         targets = []
         for key, what in ((("ffn", "down"), "FFN h re-quantization, 4096 x 8192 (SiLU*up written by the gate/up GEMM)"),
                           (("moe", "gate_up"), "MoE token quantization, 16384 x 2048, one row per routed slot"),
