@@ -76,7 +76,7 @@ def _expert_ffn(d, t, k, f, e, top_k, sample=None):
 
 @pytest.mark.parametrize("t,k,f,e,top_k", [
     (37, 64, 48, 5, 2), (300, 128, 144, 8, 2), (129, 256, 272, 16, 1), (64, 48, 32, 6, 4),
-    # the routing plan in three kernels: more than 65536 routed slots, or more than 256 experts
+    # the routing plan in three kernels: more than 8192 routed slots, or more than 256 experts
     (40000, 64, 32, 8, 2), (700, 64, 32, 300, 2),
 ])
 def test_expert_ffn_small(t, k, f, e, top_k):
