@@ -619,6 +619,8 @@ def rocprof_summary(path, only=None, steps=None):
             100.0 * sum(durs) / (step_ns * nsteps)))
     dom = groups.get(("%s %s" % DOMINANT, "gemm"))
     if dom:
+        print("# dominant launch (%s %s grouped GEMM) sources sha256_16: %s" % (DOMINANT[0], DOMINANT[1],
+                                                                           source_hash(GEMM_SOURCES)))
         print("# dominant launch (%s %s grouped GEMM): avg %.2f us over %d calls" % (
             DOMINANT[0], DOMINANT[1], np.mean(dom) / 1e3, len(dom)))
 
@@ -833,6 +835,26 @@ def stored_traffic(path=GEMM_TRAFFIC, sources=GEMM_SOURCES):
     return t.get("traffic_bytes_per_launch")
 
 
+STEP_TRACE = os.path.join(ROOT, "profiles", "bench_step_kernels.txt")
+
+
+def stored_trace_us(path=STEP_TRACE, sources=GEMM_SOURCES):
+    """The dominant launch's average duration in the committed kernel trace of the step, or None
+    when it is missing or was taken on different GEMM sources."""
+    try:
+        lines = open(path).read().splitlines()
+    except OSError:
+        return None
+    sha = [l.rsplit(":", 1)[1].strip() for l in lines if l.startswith("# dominant launch") and "sha256_16" in l]
+    avg = [l for l in lines if l.startswith("# dominant launch") and " avg " in l]
+    if not sha or not avg or sha[0] != source_hash(sources):
+        return None
+    try:
+        return float(avg[0].split(" avg ")[1].split(" us")[0])
+    except (IndexError, ValueError):
+        return None
+
+
 def kernel_stats(path):
     """Per-instantiation statistics of this library's kernels from rocprofv3 --stats."""
     import csv
@@ -921,9 +943,14 @@ def main():
                 "flops_per_launch": dom[3], "avg_launch_us": dom_st["mean"],
                 "launch_us_in_step": dom_st,
                 "frac_at_median": round(dom[3] / (dom_st["median"] * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                "trace_avg_us": stored_trace_us(),
                 "timing": "HIP events around each launch inside the %d timed steps (cache-warm: the "
                           "step's previous kernels leave the quantized A rows in cache); achieved = "
-                          "flops / mean launch time" % args.steps}
+                          "flops / mean launch time; trace_avg_us / frac_trace: the same kernel's average in "
+                          "the committed rocprofv3 trace of the step (profiles/bench_step_kernels.txt), "
+                          "given while it was taken on these GEMM sources" % args.steps}
+    if roofline["trace_avg_us"]:
+        roofline["frac_trace"] = round(dom[3] / (roofline["trace_avg_us"] * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4)
 
     qcall = path.calls[path.quant_dominant]
     q_st = stats_us([hip.elapsed_ms(a, b) for a, b in qevs])

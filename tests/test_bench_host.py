@@ -76,3 +76,15 @@ def test_stats_us_percentiles():
     st = bench.stats_us([i / 1000.0 for i in range(1, 101)])  # 1..100 us given in ms
     assert st["n"] == 100 and st["median"] == 50.5 and st["mean"] == 50.5
     assert st["p10"] == pytest.approx(10.9) and st["p90"] == pytest.approx(90.1)
+
+
+def test_stored_trace_needs_matching_sources(tmp_path):
+    good = tmp_path / "t.txt"
+    sha = bench.source_hash(bench.GEMM_SOURCES)
+    good.write_text("# x\n# dominant launch (moe gate_up grouped GEMM) sources sha256_16: %s\n"
+                    "# dominant launch (moe gate_up grouped GEMM): avg 512.25 us over 25 calls\n" % sha)
+    assert bench.stored_trace_us(str(good)) == 512.25
+    stale = tmp_path / "s.txt"
+    stale.write_text(good.read_text().replace(sha, "0" * 16))
+    assert bench.stored_trace_us(str(stale)) is None
+    assert bench.stored_trace_us(str(tmp_path / "missing.txt")) is None
