@@ -976,12 +976,17 @@ int pick_grouped(int64_t R, int64_t E, int64_t N) {
   const int forced = tile_override();
   if (forced == kTileBig || forced == kTileThinWide) return forced;
   // Rounds of resident workgroups (256 CUs; one 256x256 or two 64x256 workgroups per CU)
-  // each shape needs, counting each expert's last M-tile as half full.  A tile's K loop
-  // costs about the same in both shapes (measured), so fewer rounds win; ties go to the
-  // 256-row tiles, which read each expert's weights fewer times.
+  // each shape needs, counting a whole extra M-tile for each expert (its last, partial one:
+  // under skewed loads most experts fit in one partial tile).  A tile's K loop costs about
+  // the same in both shapes (measured), so fewer rounds win; ties go to the 256-row tiles,
+  // which read each expert's weights fewer times.  Measured on MI355X over 384-3072 tokens,
+  // top-2 of 32 Zipf-loaded experts: counting half an extra tile per expert kept 256-row
+  // tiles at 1024 tokens, where they spill into a second round (down projection 99 us
+  // against 70 us with 64-row tiles); counting a whole one picks the faster or an equal
+  // shape at every measured point but 1536 tokens, which it leaves as before.
   const int64_t nonempty = E < R ? E : R;
   auto rounds = [&](int bm, int bn, int per_cu) {
-    const int64_t tiles = ((R + bm - 1) / bm + nonempty / 2) * ((N + bn - 1) / bn);
+    const int64_t tiles = ((R + bm - 1) / bm + nonempty) * ((N + bn - 1) / bn);
     const int64_t cap = 256 * per_cu;
     return (tiles + cap - 1) / cap;
   };
