@@ -935,17 +935,25 @@ int tile_override() {
   return -1;
 }
 
-// Pick the tile for a dense M x N problem: the largest tile (most operand reuse per byte
-// loaded) that still yields enough workgroups to occupy the 256 CUs, else the thinnest.
-// On MI355X this rule picks the fastest shape for every linear of the workloads (measured
-// over all five shapes at M = 512 and M = 4096).
-int pick_dense(int64_t M, int64_t N, bool gate) {
+// Pick the tile for a dense M x N problem cut into `splits` K parts: the largest tile (most
+// operand reuse per byte loaded) whose work items (tiles x parts) still occupy the 256 CUs,
+// else the thinnest.  Split-K runs only on the tiles whose every wave stores (128x128 and
+// smaller), and there a taller tile is skipped when it pads the rows by more than an eighth
+// beyond 64-row tiles.  On MI355X this rule picks the fastest shape for every linear of the
+// workloads (measured over all five shapes at M = 512 and M = 4096).  Split cases, measured
+// (slab weights, caches flushed): 512 x 2048 x 8192 in 4 parts 29.4 -> 26.3 us and
+// 256 x 4096 x 8192 31.0 -> 27.2 us on 128x128 tiles; 300 x 6144 x 4096 stays on 64x128
+// (31.7 us; 34.7 us on 128x128, whose third M-tile is a third full).
+int pick_dense(int64_t M, int64_t N, bool gate, int splits) {
   const int forced = tile_override();
   if (forced >= 0 && !(gate && forced == kTileThin)) return forced;
   const int order[] = {kTileBig, kTileWide, kTileSmall, kTileThin};
+  auto padded = [&](int o) { return (M + kTiles[o].bm - 1) / kTiles[o].bm * kTiles[o].bm; };
   for (int o : order) {
+    if (splits > 1 && (o == kTileBig || o == kTileWide)) continue;
+    if (splits > 1 && o != kTileThin && padded(o) * 8 > padded(kTileThin) * 9) continue;
     const TileDesc& d = kTiles[o];
-    const int64_t tiles = ((M + d.bm - 1) / d.bm) * ((N + d.bn - 1) / d.bn);
+    const int64_t tiles = ((M + d.bm - 1) / d.bm) * ((N + d.bn - 1) / d.bn) * splits;
     if (tiles >= 192) return gate && o == kTileThin ? kTileThinWide : o;
   }
   // a gated output needs both 32-column blocks of a feature group in one wavefront
@@ -1022,7 +1030,10 @@ int64_t grouped_max_mtiles(int64_t R, int64_t E, int tile_m) { return (R + tile_
 
 hipError_t launch_gemm_dense(const GemmArgs& g, hipStream_t stream) {
   if (g.M <= 0) return hipSuccess;
-  switch (pick_dense(g.M, g.N, g.gate != 0)) {
+  // the K parts the launch will run (launch_dense splits only with a partial-sum buffer and
+  // per-channel or per-tensor scales)
+  const int splits = g.splits > 1 && g.partial != nullptr && g.b_gran != kScaleBlock128 ? g.splits : 1;
+  switch (pick_dense(g.M, g.N, g.gate != 0, splits)) {
     case kTileBig: return launch_dense<Big>(g, stream);
     case kTileWide: return launch_dense<Wide>(g, stream);
     case kTileSmall: return launch_dense<Small>(g, stream);
