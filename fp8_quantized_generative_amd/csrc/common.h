@@ -23,25 +23,60 @@ __device__ __forceinline__ uint32_t float_to_half_bits(float f) {
   return (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)f);  // round to nearest even
 }
 
-// h = fl16(fl32(silu(g) * u)) for two packed FP16 pairs, computed in FP32 with
-// silu(g) = g * rcp(1 + exp(-g)) (hardware exp2 and reciprocal).  The quantizer's SiLU*up input transform and the GEMM's gated
-// output both use this one definition, so the two FFN formulations give identical h.
-__device__ __forceinline__ uint32_t silu_mul_pair(uint32_t g2, uint32_t u2) {
-  uint32_t out = 0;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    float g = half_bits_to_float((g2 >> (16 * i)) & 0xFFFFu);
-    float u = half_bits_to_float((u2 >> (16 * i)) & 0xFFFFu);
-    // exp through the hardware exp2 and the quotient through the hardware reciprocal (about
-    // one FP32 ulp each): the correctly rounded division would cost ten instructions per value
-    float silu = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-    float p = silu * u;
-    // FP32 product, then FP16: the empty asm keeps the compiler from fusing the multiply
-    // into the conversion (a single rounding) in some contexts and not in others
-    asm("" : "+v"(p));
-    out |= float_to_half_bits(p) << (16 * i);
+// Two FP32 values rounded to FP16 (nearest even), packed low then high: one
+// v_cvt_pk_f16_f32.  The empty asm makes the inputs plain FP32 values, so the compiler cannot
+// fuse the multiply that produced them into a single-rounding multiply-to-FP16.
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
+  f2v v = {lo, hi};
+  asm("" : "+v"(v));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2v));
+}
+
+// p = fl32(fl32(silu(g)) * u) for the FP16 halves (low: HI = 0, high: HI = 1) of g2 and u2,
+// with silu(g) = fl32(g * rcp(1 + exp2(fl32(g * -log2 e)))) through the hardware exp2 and
+// reciprocal (about one FP32 ulp each; the correctly rounded division would cost ten
+// instructions per value).  Each multiply that takes an FP16 operand is a v_fma_mix_f32 with
+// an addend of -0: the FP16 value widens exactly, a * b + (-0) is a * b under every rounding
+// (also for a zero product of either sign), so the result equals the FP32 multiply of the
+// widened value, without the separate widening instruction.  One asm block, so the wait
+// state that each transcendental result needs before its next use is explicit.
+template <int HI>
+__device__ __forceinline__ float silu_mul_half(uint32_t g2, uint32_t u2) {
+  constexpr float kNegLog2e = -1.44269502162933349609375f;  // fl32(-log2 e)
+  float p, t;
+  if constexpr (HI) {
+    asm("v_fma_mix_f32 %1, %2, %4, neg(0) op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+        "v_exp_f32 %1, %1\n\t"
+        "s_nop 0\n\t"
+        "v_add_f32 %1, 1.0, %1\n\t"
+        "v_rcp_f32 %1, %1\n\t"
+        "s_nop 0\n\t"
+        "v_fma_mix_f32 %1, %2, %1, neg(0) op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mix_f32 %0, %3, %1, neg(0) op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=v"(p), "=&v"(t)
+        : "v"(g2), "v"(u2), "s"(kNegLog2e));
+  } else {
+    asm("v_fma_mix_f32 %1, %2, %4, neg(0) op_sel_hi:[1,0,0]\n\t"
+        "v_exp_f32 %1, %1\n\t"
+        "s_nop 0\n\t"
+        "v_add_f32 %1, 1.0, %1\n\t"
+        "v_rcp_f32 %1, %1\n\t"
+        "s_nop 0\n\t"
+        "v_fma_mix_f32 %1, %2, %1, neg(0) op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mix_f32 %0, %3, %1, neg(0) op_sel_hi:[1,0,0]"
+        : "=v"(p), "=&v"(t)
+        : "v"(g2), "v"(u2), "s"(kNegLog2e));
   }
-  return out;
+  return p;
+}
+
+// h = fl16(fl32(silu(g) * u)) for two packed FP16 pairs (the product above, rounded once to
+// FP16).  The quantizer's SiLU*up input transform and the GEMM's gated output both use this
+// one definition, so the two FFN formulations give identical h.
+__device__ __forceinline__ uint32_t silu_mul_pair(uint32_t g2, uint32_t u2) {
+  return pack_half2(silu_mul_half<0>(g2, u2), silu_mul_half<1>(g2, u2));
 }
 
 __device__ __forceinline__ uint4 ld_global_16(const void* p) {

@@ -223,16 +223,6 @@ __device__ __forceinline__ void load_lds_4(const v4i& desc, uint32_t voffset, ui
 #pragma clang diagnostic pop
 
 typedef float v16f __attribute__((ext_vector_type(16)));
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-
-// Two FP32 values rounded to FP16 (nearest even), packed low then high.  The empty asm
-// makes the inputs plain FP32 values: without it the compiler may fuse the multiply that
-// produced them into a single-rounding multiply-to-FP16 in some contexts and not others.
-__device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
-  asm("" : "+v"(lo), "+v"(hi));
-  const h2 v = {(_Float16)lo, (_Float16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
 
 struct TileInfo {
   int row_begin;  // first output row (permuted row in grouped mode)
