@@ -96,7 +96,9 @@ struct Cfg {
   static constexpr int SCALE_BYTES = 4 * ROWS;       // BM row scales, then BN column scales
   static constexpr int SCALE_LOADS = ROWS / 64;      // 4-byte-per-lane loads per tile
   static constexpr int EPI_STRIDE = 2 * WN + 16;     // padded FP16 row of an output strip
-  static constexpr int STRIP = 32 * EPI_STRIDE;     // a loader's 32-row output block
+  static constexpr int GATE_STRIDE = WN + 16;        // padded FP16 row of a gated (half-width) strip
+  // a loader's strip: one 32-row output block, or two of the gated output
+  static constexpr int STRIP = 32 * EPI_STRIDE > 64 * GATE_STRIDE ? 32 * EPI_STRIDE : 64 * GATE_STRIDE;
   static constexpr int SCALE_OFF = S * STAGE;
   static constexpr int EPI_OFF = SCALE_OFF + 2 * SCALE_BYTES;
   static constexpr int LDS = EPI_OFF + (SPLIT ? LOADERS * STRIP : 0);
@@ -703,8 +705,16 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
       const bool pcol_ok = lc < cols - pwn * kOutWN;
       uint16_t* ytile = p.y + (int64_t)cur.row_begin * NO + n0o;
       // FP16 of register group g of tile (i, jj): 4 columns
+      // the column scales of the wave's register groups, the same for every row block i: read
+      // from LDS once per tile, ahead of the first multiply
+      v4f sbv[C::TJ][4];
+#pragma unroll
+      for (int jj = 0; jj < C::TJ; ++jj)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          sbv[jj][g] = *reinterpret_cast<const v4f*>(sc + C::BM + wn * C::WN + 32 * jj + 8 * g + 4 * ehalf);
       auto group = [&](int i, int jj, int g, float sa) -> uint2 {
-        const v4f sb = *reinterpret_cast<const v4f*>(sc + C::BM + wn * C::WN + 32 * jj + 8 * g + 4 * ehalf);
+        const v4f& sb = sbv[jj][g];
         const v16f& a = acc[i][jj];
         uint2 v;
         v.x = pack_half2((a[4 * g] * sa) * sb[0], (a[4 * g + 1] * sa) * sb[1]);
@@ -720,29 +730,37 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
           return group(i, o, g, sa);
         }
       };
+      // SPLIT: the gated output (half the columns) passes through the strips two row blocks at a
+      // time, so one pair of barriers serves two blocks
+      constexpr int kBlk = (GATE && C::SPLIT && C::TI % 2 == 0) ? 2 : 1;
+      constexpr int kStride = kBlk == 2 ? C::GATE_STRIDE : C::EPI_STRIDE;
+      static_assert(kBlk * 32 * kStride <= C::STRIP, "strip holds the blocks of one round");
 #pragma unroll
-      for (int i = 0; i < C::TI; ++i) {
-        const float sa = sc[wm * C::WM + 32 * i + erow];
-        if (!storer) {
+      for (int i0 = 0; i0 < C::TI; i0 += kBlk) {
 #pragma unroll
-          for (int o = 0; o < kOutTJ; ++o)
+        for (int i = i0; i < i0 + kBlk; ++i) {
+          const float sa = sc[wm * C::WM + 32 * i + erow];
+          if (!storer) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-              *reinterpret_cast<uint2*>(strip + erow * C::EPI_STRIDE + 2 * (32 * o + 8 * g + 4 * ehalf)) =
-                  out_group(i, o, g, sa);
-        } else {
-          const int lrow = wm * C::WM + 32 * i + erow;
-          uint16_t* yrow = ytile + (int64_t)lrow * NO + wn * kOutWN + 8 * ehalf;
+            for (int o = 0; o < kOutTJ; ++o)
 #pragma unroll
-          for (int o = 0; o < kOutTJ; ++o) {
+              for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<uint2*>(strip + (32 * (i - i0) + erow) * kStride + 2 * (32 * o + 8 * g + 4 * ehalf)) =
+                    out_group(i, o, g, sa);
+          } else {
+            const int lrow = wm * C::WM + 32 * i + erow;
+            uint16_t* yrow = ytile + (int64_t)lrow * NO + wn * kOutWN + 8 * ehalf;
 #pragma unroll
-            for (int gp = 0; gp < 2; ++gp) {
-              const uint2 x = out_group(i, o, 2 * gp, sa), y = out_group(i, o, 2 * gp + 1, sa);
-              const auto s0 = __builtin_amdgcn_permlane32_swap(x.x, y.x, false, false);
-              const auto s1 = __builtin_amdgcn_permlane32_swap(x.y, y.y, false, false);
-              const int col = wn * kOutWN + 32 * o + 16 * gp + 8 * ehalf;
-              if (lrow < rows && col < cols)
-                st_global_16(yrow + 32 * o + 16 * gp, make_uint4(s0[0], s1[0], s0[1], s1[1]));
+            for (int o = 0; o < kOutTJ; ++o) {
+#pragma unroll
+              for (int gp = 0; gp < 2; ++gp) {
+                const uint2 x = out_group(i, o, 2 * gp, sa), y = out_group(i, o, 2 * gp + 1, sa);
+                const auto s0 = __builtin_amdgcn_permlane32_swap(x.x, y.x, false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(x.y, y.y, false, false);
+                const int col = wn * kOutWN + 32 * o + 16 * gp + 8 * ehalf;
+                if (lrow < rows && col < cols)
+                  st_global_16(yrow + 32 * o + 16 * gp, make_uint4(s0[0], s1[0], s0[1], s1[1]));
+              }
             }
           }
         }
@@ -750,10 +768,10 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
           __syncthreads();
           if (!loader) {
 #pragma unroll
-            for (int t = 0; t < 32 / kRpt; ++t) {
-              const int r = lr + kRpt * t;
-              const uint4 v = *reinterpret_cast<const uint4*>(strip + r * C::EPI_STRIDE + 2 * lc);
-              const int orow = pwm * C::WM + 32 * i + r;
+            for (int t = 0; t < 32 * kBlk / kRpt; ++t) {
+              const int r = lr + kRpt * t;  // strip row: block r / 32 of the round, its row r % 32
+              const uint4 v = *reinterpret_cast<const uint4*>(strip + r * kStride + 2 * lc);
+              const int orow = pwm * C::WM + 32 * i0 + r;
               if (orow < rows && pcol_ok) st_global_16(ytile + (int64_t)orow * NO + pwn * kOutWN + lc, v);
             }
           }
