@@ -731,10 +731,14 @@ def pmc_dump(paths, only=None, steps=None):
                 d["l2_read_req_per_cu_cycle"] = c["TCP_TCC_READ_REQ"] / (CUS * cyc)
             if "TCC_HIT_sum" in c and "TCC_MISS_sum" in c:
                 d["l2_hit_rate"] = c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"])
+            for name, key in (("lds_idx_active", "SQ_LDS_IDX_ACTIVE"), ("lds_bank_conflict", "SQ_LDS_BANK_CONFLICT"),
+                              ("lds_wait_inst", "SQ_WAIT_INST_LDS")):
+                if key in c:
+                    d[name] = c[key] / (CUS * cyc)
     cols = ("ta_busy", "td_busy", "td_tc_stall", "tcp_pending_stall", "l2_read_latency_cycles",
-            "l2_read_req_per_cu_cycle", "l2_hit_rate")
-    print("# derived per GEMM call: busy/stall fractions = counter / (%d CUs x GRBM_GUI_ACTIVE / %d XCDs); "
-          "L2 read latency = TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ (cycles); L2 hit rate = TCC_HIT / "
+            "l2_read_req_per_cu_cycle", "l2_hit_rate", "lds_idx_active", "lds_bank_conflict", "lds_wait_inst")
+    print("# derived per GEMM call: busy/stall fractions = counter / (%d CUs x GRBM_GUI_ACTIVE / %d XCDs) (the LDS "
+          "ones too); L2 read latency = TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ (cycles); L2 hit rate = TCC_HIT / "
           "(TCC_HIT + TCC_MISS)" % (CUS, XCDS))
     print("# %-26s %s" % ("call", " ".join("%12s" % c[:12] for c in cols)))
     for label, d in derived.items():
