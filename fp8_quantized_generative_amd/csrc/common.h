@@ -152,7 +152,7 @@ struct GemmArgs {
 };
 
 // GEMM tile shapes (rows x columns of output per workgroup).
-enum { kTileBig = 0, kTileWide, kTileSmall, kTileThin, kTileThinWide, kTileKinds };
+enum { kTileBig = 0, kTileWide, kTileSmall, kTileThin, kTileThinWide, kTileMid, kTileKinds };
 constexpr int kMinTileRows = 64;  // fewest rows of any tile shape (sizes the MoE tile table)
 
 hipError_t launch_gemm_dense(const GemmArgs& g, hipStream_t stream);

@@ -693,16 +693,12 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
       const int partner = loader ? wave : wave - C::LOADERS;
       uint8_t* strip = smem + C::EPI_OFF + partner * C::STRIP;
       constexpr int kCpr = kOutWN / 8;  // 16-byte chunks per strip row
-      constexpr int kRpt = 64 / kCpr;   // strip rows covered by one 64-lane read
       int el = lane;                    // opaque copy: addressing is redone per tile, not hoisted
       asm volatile("" : "+v"(el));
-      const int lr = el / kCpr;         // this lane's strip row (plus kRpt t) and column
-      const int lc = 8 * (el % kCpr);
       const int erow = el & 31, ehalf = el >> 5;  // MFMA output row and column half
       const int rows = cur.row_end - cur.row_begin;
       const int cols = NO - n0o;
       const int pwm = partner / C::WGN, pwn = partner % C::WGN;
-      const bool pcol_ok = lc < cols - pwn * kOutWN;
       uint16_t* ytile = p.y + (int64_t)cur.row_begin * NO + n0o;
       // FP16 of register group g of tile (i, jj): 4 columns
       // the column scales of the wave's register groups, the same for every row block i: read
@@ -768,11 +764,15 @@ __global__ __launch_bounds__(C::NT) void gemm_fp8_kernel(GemmArgs p, int m_tiles
           __syncthreads();
           if (!loader) {
 #pragma unroll
-            for (int t = 0; t < 32 * kBlk / kRpt; ++t) {
-              const int r = lr + kRpt * t;  // strip row: block r / 32 of the round, its row r % 32
+            // chunk c of the round's strip rows: row c / kCpr (block r / 32 of the round, its
+            // row r % 32), columns 8 (c % kCpr) ..
+            for (int t = 0; t < 32 * kBlk * kCpr / 64; ++t) {
+              const int c = el + 64 * t;
+              const int r = c / kCpr, lc = 8 * (c % kCpr);
               const uint4 v = *reinterpret_cast<const uint4*>(strip + r * kStride + 2 * lc);
               const int orow = pwm * C::WM + 32 * i0 + r;
-              if (orow < rows && pcol_ok) st_global_16(ytile + (int64_t)orow * NO + pwn * kOutWN + lc, v);
+              if (orow < rows && lc < cols - pwn * kOutWN)
+                st_global_16(ytile + (int64_t)orow * NO + pwn * kOutWN + lc, v);
             }
           }
           __syncthreads();
@@ -906,7 +906,10 @@ hipError_t launch_gate(const GemmArgs& g, int m_tiles, hipStream_t stream) {
 
 template <class C, bool GROUPED, bool A5>
 hipError_t launch_fmt(const GemmArgs& g, int m_tiles, hipStream_t stream) {
-  if (g.b_gran == kScaleBlock128) return launch_gate<C, GROUPED, true, A5>(g, m_tiles, stream);
+  if (g.b_gran == kScaleBlock128) {
+    if constexpr (kScaleBlock % C::WN == 0) return launch_gate<C, GROUPED, true, A5>(g, m_tiles, stream);
+    else return hipErrorInvalidValue;  // a wave's columns would straddle two scale blocks
+  }
   return launch_gate<C, GROUPED, false, A5>(g, m_tiles, stream);
 }
 
@@ -930,6 +933,10 @@ using Thin = Cfg<64, 128, 4, 1, 4, false>;      // 48 KB ring, three workgroups 
 // resident workgroups is as fast on the 512-token MoE (gate/up 103.0 us, down 72 us) and, at
 // 1024 tokens, 4% faster on the gate/up and 4% slower on the down projection.
 using ThinWide = Cfg<64, 256, 3, 1, 4, false>;
+// 112 KB ring, 64x96 per wavefront: three quarters of a 256x256 tile, for linears whose
+// 256x256 tile count ends in a partly filled round (per-channel or per-tensor scales, plain
+// output: a wavefront's 96 columns hold no gate/up pair and straddle 128-column scale blocks).
+using Mid = Cfg<256, 192, 4, 4, 2, true>;
 // 160 KB of LDS per CU: the resident workgroup counts above (and the grouped tile rule)
 // depend on these sizes.
 constexpr int kLdsPerCu = 160 * 1024;
@@ -942,6 +949,7 @@ struct TileDesc {
 };
 const TileDesc kTiles[kTileKinds] = {
     {"256x256", 256, 256}, {"256x128", 256, 128}, {"128x128", 128, 128}, {"64x128", 64, 128}, {"64x256", 64, 256},
+    {"256x192", 256, 192},
 };
 
 int tile_override() {
@@ -961,9 +969,10 @@ int tile_override() {
 // (slab weights, caches flushed): 512 x 2048 x 8192 in 4 parts 29.4 -> 26.3 us and
 // 256 x 4096 x 8192 31.0 -> 27.2 us on 128x128 tiles; 300 x 6144 x 4096 stays on 64x128
 // (31.7 us; 34.7 us on 128x128, whose third M-tile is a third full).
-int pick_dense(int64_t M, int64_t N, bool gate, int splits) {
+int pick_dense(int64_t M, int64_t N, bool gate, bool blocks, int splits) {
   const int forced = tile_override();
-  if (forced >= 0 && !(gate && forced == kTileThin)) return forced;
+  const bool mid_ok = !gate && !blocks && splits == 1;  // what the 256x192 tile serves
+  if (forced >= 0 && !(gate && forced == kTileThin) && !(forced == kTileMid && !mid_ok)) return forced;
   const int order[] = {kTileBig, kTileWide, kTileSmall, kTileThin};
   auto padded = [&](int o) { return (M + kTiles[o].bm - 1) / kTiles[o].bm * kTiles[o].bm; };
   for (int o : order) {
@@ -971,7 +980,15 @@ int pick_dense(int64_t M, int64_t N, bool gate, int splits) {
     if (splits > 1 && o != kTileThin && padded(o) * 8 > padded(kTileThin) * 9) continue;
     const TileDesc& d = kTiles[o];
     const int64_t tiles = ((M + d.bm - 1) / d.bm) * ((N + d.bn - 1) / d.bn) * splits;
-    if (tiles >= 192) return gate && o == kTileThin ? kTileThinWide : o;
+    if (tiles < 192) continue;
+    // 256x256 tiles that end in a partly filled round of the 256 CUs: 256x192 tiles whose
+    // rounds, at 7/8 of the time each (three quarters of the MFMA work, 7/8 of the operand
+    // bytes), take less time.  4096 x 6144: 384 tiles (2 rounds) -> 512 tiles (2 rounds).
+    if (o == kTileBig && mid_ok && N % 192 == 0) {
+      const int64_t mid = ((M + 255) / 256) * (N / 192);
+      if ((mid + 255) / 256 * 7 < (tiles + 255) / 256 * 8) return kTileMid;
+    }
+    return gate && o == kTileThin ? kTileThinWide : o;
   }
   // a gated output needs both 32-column blocks of a feature group in one wavefront
   return gate ? kTileThinWide : kTileThin;
@@ -1050,9 +1067,10 @@ hipError_t launch_gemm_dense(const GemmArgs& g, hipStream_t stream) {
   // the K parts the launch will run (launch_dense splits only with a partial-sum buffer and
   // per-channel or per-tensor scales)
   const int splits = g.splits > 1 && g.partial != nullptr && g.b_gran != kScaleBlock128 ? g.splits : 1;
-  switch (pick_dense(g.M, g.N, g.gate != 0, splits)) {
+  switch (pick_dense(g.M, g.N, g.gate != 0, g.b_gran == kScaleBlock128, splits)) {
     case kTileBig: return launch_dense<Big>(g, stream);
     case kTileWide: return launch_dense<Wide>(g, stream);
+    case kTileMid: return launch_dense<Mid>(g, stream);
     case kTileSmall: return launch_dense<Small>(g, stream);
     case kTileThin: return launch_dense<Thin>(g, stream);
     default: return launch_dense<ThinWide>(g, stream);

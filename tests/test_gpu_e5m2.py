@@ -71,7 +71,7 @@ def _check(rq, x16, w16, tile=None, wscale_name="channel"):
     assert ok, "max |d|/tol = %.3f" % ratio
 
 
-@pytest.mark.parametrize("tile", [None, "256x256", "256x128", "128x128", "64x128", "64x256"])
+@pytest.mark.parametrize("tile", [None, "256x256", "256x192", "256x128", "128x128", "64x128", "64x256"])
 @pytest.mark.parametrize("m,n,k", [(130, 272, 528), (300, 384, 2048), (64, 128, 8192)])
 def test_linear(monkeypatch, tile, m, n, k):
     rq = require_gpu()

@@ -130,7 +130,7 @@ def test_determinism():
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
 
 
-@pytest.mark.parametrize("tile", ["256x256", "256x128", "128x128", "64x128", "64x256"])
+@pytest.mark.parametrize("tile", ["256x256", "256x192", "256x128", "128x128", "64x128", "64x256"])
 @pytest.mark.parametrize("m,n,k", [(130, 272, 528), (257, 144, 192), (64, 512, 512), (300, 384, 2048)])
 def test_every_tile_shape(monkeypatch, tile, m, n, k):
     case("linear tile=%s m=%d n=%d k=%d" % (tile, m, n, k))
@@ -142,7 +142,7 @@ def test_every_tile_shape(monkeypatch, tile, m, n, k):
 
 
 @pytest.mark.parametrize("grid", ["3", "8"])
-@pytest.mark.parametrize("tile", ["256x256", "256x128", "128x128", "64x128", "64x256"])
+@pytest.mark.parametrize("tile", ["256x256", "256x192", "256x128", "128x128", "64x128", "64x256"])
 @pytest.mark.parametrize("m,n,k", [(300, 400, 1040), (130, 272, 208), (257, 144, 128), (70, 528, 64)])
 def test_persistent_walk(monkeypatch, grid, tile, m, n, k):
     """Few workgroups, many tiles each: the LDS ring and the scale areas carried from one
@@ -157,7 +157,7 @@ def test_persistent_walk(monkeypatch, grid, tile, m, n, k):
     _check(x, w)
 
 
-@pytest.mark.parametrize("tile", [None, "256x256", "256x128", "128x128", "64x256"])
+@pytest.mark.parametrize("tile", [None, "256x256", "256x192", "256x128", "128x128", "64x256"])
 @pytest.mark.parametrize("m,f,k", [(130, 64, 272), (300, 320, 528), (64, 2048, 512)])
 def test_gated_silu_output(monkeypatch, tile, m, f, k):
     """act='gate_silu' on interleaved gate/up weights writes exactly the h that the unfused

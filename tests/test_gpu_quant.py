@@ -1,7 +1,8 @@
 """GPU row quantizer vs the oracle: bytes and scales bit-exact.
 
 Covers the exhaustive FP16 sweep at unit scale, every FP16 amax, config-shaped rows at
-every register-tiling width (and the wide-row loop path), zero and signed-zero rows,
+every register-tiling width (and the wide-row loop path), launches whose workgroups walk
+several row groups, zero and signed-zero rows,
 saturation extremes, the SiLU*up prologue, the weight entry point over [B, N, K], and
 determinism.
 """
@@ -77,6 +78,17 @@ def test_config_shaped_rows(k, rows):
     rng = np.random.default_rng(k * 1000 + rows)
     recipe = [workloads.acts_outliers, workloads.acts_channel_lognormal, workloads.acts_student_t][k % 3]
     x = recipe(rng, rows, k)
+    _assert_exact(x)
+
+
+@pytest.mark.parametrize("rows,k", [(10241, 2048), (20483, 512), (5121, 8192)])
+def test_rows_walked_by_resident_workgroups(rows, k):
+    # 2.5x as many row groups (4, 2 or 1 rows each) as a device of 256 CUs keeps resident:
+    # the prefetching launch walks several groups per workgroup, and the first two shapes end
+    # on a partly filled group
+    case("quant: prefetching walk rows=%d k=%d" % (rows, k))
+    rng = np.random.default_rng(rows + k)
+    x = workloads.acts_student_t(rng, rows, k)
     _assert_exact(x)
 
 

@@ -22,7 +22,7 @@ from tests.gpu_util import case, dev, host, require_gpu
 
 pytestmark = pytest.mark.gpu
 
-TILES = [None, "256x256", "256x128", "128x128", "64x128", "64x256"]
+TILES = [None, "256x256", "256x192", "256x128", "128x128", "64x128", "64x256"]
 
 
 def _bits(t):

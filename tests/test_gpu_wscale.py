@@ -73,7 +73,7 @@ def _check_linear(rq, x16, w16, gran, act="none"):
 
 
 @pytest.mark.parametrize("gran", ["tensor", "block128"])
-@pytest.mark.parametrize("tile", [None, "256x256", "256x128", "128x128", "64x128", "64x256"])
+@pytest.mark.parametrize("tile", [None, "256x256", "256x192", "256x128", "128x128", "64x128", "64x256"])
 @pytest.mark.parametrize("m,n,k", [(130, 384, 512), (300, 256, 2048), (64, 128, 256)])
 def test_linear(monkeypatch, gran, tile, m, n, k):
     """Short K (only the generic slab steps: each K block's rescale decided at run time) and

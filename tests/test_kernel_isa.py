@@ -57,7 +57,8 @@ def test_gemm_m0_only_in_lds_dma_asm(gemm_asm):
 
 # Waves per SIMD each tile shape must reach (its workgroups per CU times its wavefronts per
 # workgroup, over 4 SIMDs): the persistent grid and the grouped tile rule assume these.
-_OCCUPANCY = {"Li256ELi256E": 2, "Li256ELi128E": 2, "Li128ELi128E": 2, "Li64ELi128E": 3, "Li64ELi256E": 2}
+_OCCUPANCY = {"Li256ELi256E": 2, "Li256ELi128E": 2, "Li128ELi128E": 2, "Li64ELi128E": 3, "Li64ELi256E": 2,
+              "Li256ELi192E": 2}
 
 
 def test_gemm_occupancy(gemm_asm):
