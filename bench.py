@@ -746,12 +746,17 @@ def pmc_dump(paths, only=None, steps=None):
 
 
 def source_hash(files):
-    """Hash of a kernel's sources: stored traffic counters are valid only for this code."""
+    """Hash of a kernel's code: stored traffic counters and traces are valid only for this code.
+    Line comments and blank lines are left out (the sources use no block comments and no "//"
+    inside string literals), so editing a comment keeps the stored evidence valid."""
     import hashlib
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "fp8_quantized_generative_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "fp8_quantized_generative_amd", "csrc", f), encoding="utf-8") as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode("utf-8") + b"\n")
     return h.hexdigest()[:16]
 
 

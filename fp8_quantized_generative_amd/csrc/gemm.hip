@@ -17,7 +17,7 @@
 //   the 32 x 32 result comes out transposed: lane l holds token row (l & 31) and, in
 //   register r, output column 8 (r / 4) + 4 (l / 32) + r % 4 - four consecutive columns
 //   per group of four registers, which the epilogue writes straight to memory.
-// * Tiles: BM x BN outputs per workgroup (256x256, 256x128, 128x128, 64x128 or 64x256)
+// * Tiles: BM x BN outputs per workgroup (256x256, 256x192, 256x128, 128x128, 64x128 or 64x256)
 //   split over a grid of wavefronts, each owning a block of 32x32 MFMA tiles.
 // * Persistent workgroups: the grid holds as many workgroups as the CUs keep resident and
 //   each walks a list of tiles, so one tile's epilogue overlaps the loads of the next.
@@ -964,8 +964,9 @@ int tile_override() {
 // operand reuse per byte loaded) whose work items (tiles x parts) still occupy the 256 CUs,
 // else the thinnest.  Split-K runs only on the tiles whose every wave stores (128x128 and
 // smaller), and there a taller tile is skipped when it pads the rows by more than an eighth
-// beyond 64-row tiles.  On MI355X this rule picks the fastest shape for every linear of the
-// workloads (measured over all five shapes at M = 512 and M = 4096).  Split cases, measured
+// beyond 64-row tiles; a 256x256 pick may then become 256x192 (below).  On MI355X the rule
+// picked the fastest of the other five shapes for every linear of the workloads (measured at
+// M = 512 and M = 4096).  Split cases, measured
 // (slab weights, caches flushed): 512 x 2048 x 8192 in 4 parts 29.4 -> 26.3 us and
 // 256 x 4096 x 8192 31.0 -> 27.2 us on 128x128 tiles; 300 x 6144 x 4096 stays on 64x128
 // (31.7 us; 34.7 us on 128x128, whose third M-tile is a third full).
