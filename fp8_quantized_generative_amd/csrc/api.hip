@@ -387,7 +387,7 @@ int rq_fp8_moe_grouped_linear_ex(const uint16_t* x, int in_layout, int act, int 
   if (ds) as = ds;
 
   hipStream_t s = (hipStream_t)stream;
-  const int kind = rq::pick_grouped(R, E, N);
+  const int kind = rq::pick_grouped(R, E, N, act == RQ_ACT_GATE_SILU);
   const int which = rq::tile_rows(kind) == kPlanTileRows[0] ? 0 : 1;
   if (!plan_ready && rq::launch_moe_plan(topk_ids, T, top_k, E, offsets, tt, perm, pos, block_hist, s) != hipSuccess)
     return RQ_ERR_HIP;

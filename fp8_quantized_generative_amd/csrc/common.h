@@ -160,7 +160,7 @@ hipError_t launch_gemm_dense(const GemmArgs& g, hipStream_t stream);
 int dense_splits(int64_t M, int64_t N, int64_t K, int act, int w_gran);
 size_t dense_partial_bytes(int64_t M, int64_t N, int64_t K, int act, int w_gran);
 hipError_t launch_gemm_grouped(const GemmArgs& g, int kind, hipStream_t stream);
-int pick_grouped(int64_t R, int64_t E, int64_t N);  // tile shape for R routed rows over E experts
+int pick_grouped(int64_t R, int64_t E, int64_t N, bool gate);  // tile shape for R routed rows over E experts
 int tile_rows(int kind);                       // M rows of a tile shape
 int64_t grouped_max_mtiles(int64_t R, int64_t E, int tile_m);
 

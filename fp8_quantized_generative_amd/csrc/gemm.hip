@@ -1015,9 +1015,9 @@ hipError_t launch_dense(const GemmArgs& g, hipStream_t stream) {
 
 }  // namespace
 
-int pick_grouped(int64_t R, int64_t E, int64_t N) {
+int pick_grouped(int64_t R, int64_t E, int64_t N, bool gate) {
   const int forced = tile_override();
-  if (forced == kTileBig || forced == kTileThinWide) return forced;
+  if (forced == kTileBig || forced == kTileThinWide || (forced == kTileThin && !gate)) return forced;
   // Rounds of resident workgroups (256 CUs; one 256x256 or two 64x256 workgroups per CU)
   // each shape needs, counting a whole extra M-tile for each expert (its last, partial one:
   // under skewed loads most experts fit in one partial tile).  A tile's K loop costs about
@@ -1033,7 +1033,15 @@ int pick_grouped(int64_t R, int64_t E, int64_t N) {
     const int64_t cap = 256 * per_cu;
     return (tiles + cap - 1) / cap;
   };
-  return rounds(256, 256, 1) <= rounds(64, 256, 2) ? kTileBig : kTileThinWide;
+  if (rounds(256, 256, 1) <= rounds(64, 256, 2)) return kTileBig;
+  // Few routed rows (the weight-streaming regime): while the 64x256 tiles leave resident slots
+  // idle and the 64x128 tiles, three per CU, still fit one round, the plain (ungated) output
+  // takes 64x128 tiles - twice the workgroups streaming weights.  Measured on MI355X, 512
+  // tokens, top-2 of 32 Zipf-loaded experts, down projection: 71.4 -> 64.7 us; at 1024 tokens
+  // the 64x256 tiles fill a round and stay.
+  auto tiles = [&](int bm, int bn) { return ((R + bm - 1) / bm + nonempty) * ((N + bn - 1) / bn); };
+  if (!gate && tiles(64, 256) < 256 * 2 && tiles(64, 128) <= 256 * 3) return kTileThin;
+  return kTileThinWide;
 }
 
 int tile_rows(int kind) { return kTiles[kind].bm; }
@@ -1082,6 +1090,7 @@ hipError_t launch_gemm_grouped(const GemmArgs& g, int kind, hipStream_t stream) 
   if (g.M <= 0) return hipSuccess;
   if (kind == kTileThinWide)
     return launch<ThinWide, true>(g, (int)grouped_max_mtiles(g.M, g.E, ThinWide::BM), stream);
+  if (kind == kTileThin) return launch<Thin, true>(g, (int)grouped_max_mtiles(g.M, g.E, Thin::BM), stream);
   return launch<Big, true>(g, (int)grouped_max_mtiles(g.M, g.E, Big::BM), stream);
 }
 

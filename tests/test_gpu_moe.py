@@ -135,7 +135,7 @@ def test_moe_full_size_every_row():
 
 
 @pytest.mark.parametrize("grid", [None, "5", "16"])
-@pytest.mark.parametrize("tile", ["256x256", "64x256", None])
+@pytest.mark.parametrize("tile", ["256x256", "64x256", "64x128", None])
 def test_grouped_tile_shapes(monkeypatch, tile, grid):
     # 600 tokens, top-2 of 6 experts: about 200 rows per expert (256-row tiles by default);
     # a capped grid makes each workgroup walk many expert tiles
